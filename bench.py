@@ -1,0 +1,235 @@
+"""Benchmark of the MI355X fused MoE expert layer (one GPU).
+
+Default workload: the large-batch layer, M=16384 tokens, hidden K=2048,
+intermediate N=768, 128 local experts, topk=8, uniform softmax-topk routing,
+fp8 e4m3 weights with 128x128 fp32 block scales, bf16 in/out.  One step is
+one moe_forward_chunked call over the whole batch (input quant, count,
+permute, GEMM w13, SiLU-mul requant, GEMM w2, unpermute-reduce), inputs
+already resident in HBM.
+
+Prints one JSON line: tokens/s for the layer, plus per-op times, GEMM TFLOP/s,
+per-op algorithmic GB/s, the roofline of the dominant kernel (GEMM w13) and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import unpermute_count_expert_amd as moe  # noqa: E402
+from unpermute_count_expert_amd import generators as gen  # noqa: E402
+
+METRIC = "MoE layer tokens/s; grouped-GEMM fp8 TFLOP/s; scatter/gather HBM GB/s"
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w13_traffic.json")
+GEMM_SRC = os.path.join(ROOT, "unpermute_count_expert_amd", "csrc", "gemm_fp8.hip")
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a.copy()).to("cuda:0")
+
+
+def gemm_source_hash() -> str:
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per GEMM-w13 launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemm_source_sha256_16") != gemm_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def timed(fn, iters, stream):
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(iters):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / iters  # ms
+
+
+def per_op_times(inp, d, layer, on_input, iters, stream):
+    """Times each op of the pipeline through its own C-ABI entry point, on the
+    same buffers the layer uses, with HIP events on the launching stream."""
+    cfg = inp.cfg
+    M, K, N, T, El = cfg.M, cfg.K, cfg.N, cfg.topk, cfg.El
+    cap = moe.moe_max_rows(M, T, El, cfg.align)
+    u8, f32, i32, bf = torch.uint8, torch.float32, torch.int32, torch.int16
+    e = lambda shape, dt: torch.empty(shape, dtype=dt, device="cuda:0")
+    a_q, a_s = e((M, K), u8), e((M, K // 128), f32)
+    a_perm, a_perm_s = e((cap, K), u8), e((cap, K // 128), f32)
+    counts, offs = e((El,), i32), e((El + 1,), i32)
+    inv, rsrc = e((M, T), i32), e((cap,), i32)
+    pws = e((moe.moe_permute_workspace_size(M, T, El),), u8)
+    h = e((cap, 2 * N), bf)
+    act_q, act_s = e((cap, N), u8), e((cap, N // 128), f32)
+    y = e((cap, K), bf)
+    out = e((M, K), bf)
+    cnt2 = e((El,), i32)
+    emap = d["emap"]
+    ops = {
+        "input_quant": lambda: moe.moe_act_quant(d["x"], K, moe.MOE_ACT_IDENTITY, a_q, a_s),
+        "count": lambda: moe.moe_count(d["ids"], emap, cfg.Eg, El, cnt2),
+        "permute": lambda: moe.moe_permute(a_q, a_s, d["ids"], d["w"], on_input, emap, cfg.Eg, El, cfg.align,
+                                           cap, a_perm, a_perm_s, counts, offs, inv, rsrc, pws),
+        "gemm_w13": lambda: moe.moe_grouped_gemm_fp8(a_perm, a_perm_s, layer.w13, layer.w13_s, offs, counts, h),
+        "silu_mul_quant": lambda: moe.moe_act_quant(h, N, moe.MOE_ACT_SILU_MUL, act_q, act_s, offs, counts, El),
+        "gemm_w2": lambda: moe.moe_grouped_gemm_fp8(act_q, act_s, layer.w2, layer.w2_s, offs, counts, y),
+        "unpermute": lambda: moe.moe_unpermute_weight_reduce(y, inv, d["w"], on_input, out),
+    }
+    # one pass in order to fill every buffer, then each op timed on its own
+    for fn in ops.values():
+        fn()
+    torch.cuda.synchronize()
+    res = {name: timed(fn, iters, stream) for name, fn in ops.items()}
+    c = counts.cpu().numpy()
+    return res, c, int(offs[-1].item())
+
+
+def algorithmic(cfg, counts: np.ndarray, R: int):
+    M, K, N, T = cfg.M, cfg.K, cfg.N, cfg.topk
+    P = int(counts.sum())
+    Ene = int((counts > 0).sum())
+    g1_flops = 2.0 * P * (2 * N) * K
+    g2_flops = 2.0 * P * K * N
+    by = {
+        "count": 4 * M * T + 4 * cfg.El,
+        "input_quant": 2 * M * K + M * K + 4 * M * K / 128,
+        "permute": M * K + 4 * M * K / 128 + P * K + 4 * P * K / 128 + 8 * M * T + 4 * R,
+        "gemm_w13": P * K + Ene * 2 * N * K + 4 * P * N + 4 * P * K / 128 + 4 * Ene * (2 * N // 128) * (K // 128),
+        "silu_mul_quant": 4 * P * N + P * N + 4 * P * N / 128,
+        "gemm_w2": P * N + Ene * K * N + 2 * P * K + 4 * P * N / 128 + 4 * Ene * (K // 128) * (N // 128),
+        "unpermute": 2 * P * K + 8 * M * T + 2 * M * K,
+    }
+    return P, Ene, g1_flops, g2_flops, by
+
+
+def cpu_baseline(inp, on_input, target_s=15.0):
+    """The oracle (plain C, OpenMP over rows) on the first S tokens of the
+    same workload; S is grown from a 16-token probe to about target_s of work."""
+    import oracle
+    cfg = inp.cfg
+
+    def run(S):
+        t0 = time.perf_counter()
+        oracle.forward_chunked(inp.x[:S], inp.topk_ids[:S], inp.topk_weights[:S], inp.expert_map, inp.w13,
+                               inp.w13_s, inp.w2, inp.w2_s, cfg.Eg, apply_on_input=on_input, align=cfg.align)
+        return time.perf_counter() - t0
+
+    probe = 16
+    tp = run(probe)
+    S = int(min(cfg.M, max(probe, probe * target_s / max(tp, 1e-3))))
+    ts = run(S)
+    return {"value": S / ts, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {S} of {cfg.M} tokens of the same layer (all expert weights), {ts:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="C5u", choices=sorted(gen.CONFIGS))
+    ap.add_argument("--op-iters", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU expert-parallel path is not part of it)", file=sys.stderr)
+        sys.exit(2)
+
+    cfg = gen.CONFIGS[args.config]
+    on_input = cfg.apply_router_weight_on_input
+    t_gen = time.perf_counter()
+    inp = gen.make_inputs(cfg)
+    t_gen = time.perf_counter() - t_gen
+    d = dict(x=dev(inp.x), ids=dev(inp.topk_ids), w=dev(inp.topk_weights),
+             emap=dev(inp.expert_map) if inp.expert_map is not None else None)
+    layer = moe.MoeLayer(dev(inp.w13), dev(inp.w13_s), dev(inp.w2), dev(inp.w2_s), cfg.Eg, d["emap"], cfg.align)
+    stream = torch.cuda.current_stream()
+    out = torch.empty((cfg.M, cfg.K), dtype=torch.int16, device="cuda:0")
+
+    def step():
+        layer.forward(d["x"], d["ids"], d["w"], chunk_size=cfg.chunk_size, apply_on_input=on_input, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = timed(step, args.steps, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ops, counts, R = per_op_times(inp, d, layer, on_input, args.op_iters, stream)
+    P, Ene, g1f, g2f, by = algorithmic(cfg, counts, R)
+    ops_out = {}
+    for name, t in ops.items():
+        rec = {"ms": round(t, 5), "GB/s": round(by[name] / (t * 1e-3) / 1e9, 1)}
+        rec["hbm_frac"] = round(rec["GB/s"] / PEAK_HBM_GBS, 4)
+        if name == "gemm_w13":
+            rec["TFLOP/s"] = round(g1f / (t * 1e-3) / 1e12, 1)
+        if name == "gemm_w2":
+            rec["TFLOP/s"] = round(g2f / (t * 1e-3) / 1e12, 1)
+        ops_out[name] = rec
+    t_g1 = ops["gemm_w13"]
+    achieved = g1f / (t_g1 * 1e-3) / 1e12
+    gemm_both = (g1f + g2f) / ((ops["gemm_w13"] + ops["gemm_w2"]) * 1e-3) / 1e12
+    traffic = measured_traffic()
+    line = {
+        "metric": METRIC,
+        "value": round(cfg.M / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: M={cfg.M} K={cfg.K} N={cfg.N} E={cfg.El}/{cfg.Eg} "
+                               f"topk={cfg.topk} routing={cfg.routing} on_input={on_input}",
+                   "M": cfg.M, "K": cfg.K, "N": cfg.N, "experts": cfg.El, "topk": cfg.topk,
+                   "chunk_size": cfg.chunk_size, "align": cfg.align, "pairs": P, "padded_rows": R},
+        "roofline": {"bound": "mfma", "kernel": "grouped GEMM w13 (k_grouped_gemm)",
+                     "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic},
+        "gemm_tflops_both": round(gemm_both, 1),
+        "gemm_frac_both": round(gemm_both / PEAK_FP8_TFLOPS, 4),
+        "ops": ops_out,
+        "wall_s_timed": round(wall, 3),
+        "input_gen_s": round(t_gen, 1),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp, on_input, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

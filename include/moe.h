@@ -1,0 +1,178 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) fused MoE expert pipeline.
+ *
+ * One layer call on one GPU's local experts:
+ *   input fp8 quant -> count -> permute -> fp8 grouped GEMM (w13)
+ *   -> SiLU-and-mul + fp8 requant -> fp8 grouped GEMM (w2)
+ *   -> unpermute with topk weight and reduce to (M, K),
+ * chunked over M with per-chunk expert counts and workspace shapes.
+ *
+ * The operations follow three vLLM pull-request pages:
+ *  [P20903] "[Kernel] DeepGemm MoE : Integrate triton permute / unpermute
+ *           kernels" -- Purpose (workspaces sized from local experts and
+ *           expert counts; ep_scatter / ep_gather permute and unpermute),
+ *           Optimizations (float8_e4m3fn, 128x128 block shape, topk 4
+ *           profile), bot Highlights (weights applied and reduced inside the
+ *           experts; finalize becomes a no-op).
+ *  [P20725] "[Misc] ModularKernel : Perform WeightAndReduce inside
+ *           TritonExperts & DeepGemmExperts" -- Purpose/Changes
+ *           (topk_weights and apply_router_weight_on_input reach the
+ *           experts; workspace reuse rules).
+ *  [P20392] "[Bugfix] Fused MoE Modular Kernel chunking loop" -- Purpose
+ *           Bug 1 (workspace shapes per chunk), Bug 2 (expert_num_tokens
+ *           recounted per chunk by count_expert_num_tokens), review thread
+ *           (count over topk ids, local expert count and expert map).
+ *
+ * Conventions for every entry point:
+ *  - Tensors are DEVICE pointers, contiguous row-major, caller-owned, 16-byte
+ *    aligned.  bf16 travels as uint16_t bits, e4m3 (OCP E4M3FN) as uint8_t.
+ *    Nothing is retained after return.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *    asynchronously; the library never synchronises and never allocates or
+ *    frees device memory.
+ *  - Arguments are validated on the host before anything is enqueued; on an
+ *    error nothing is launched and a status != MOE_OK is returned, with
+ *    detail in moe_last_error() (thread-local).  Device faults surface at the
+ *    caller's next synchronisation.
+ *  - The library runs on gfx950 only (MOE_ERR_UNSUPPORTED_DEVICE otherwise).
+ *  - A local expert id of a global id is: -1 if the id is -1 or outside
+ *    [0, Eg); expert_map[id] if a map is given; else the id if < El, else -1.
+ *    Pairs with local id -1 are dropped.  Limits: 1 <= El <= 1024,
+ *    1 <= topk <= 256, K and N multiples of 128, Mc*topk < 2^31.
+ */
+#ifndef MOE_H
+#define MOE_H
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,        /* null / misaligned pointer, bad flag, overlap */
+    MOE_ERR_SHAPE = 2,              /* size not supported (K%128, align, limits) */
+    MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+    MOE_ERR_UNSUPPORTED_DEVICE = 4, /* current device is not gfx950 */
+    MOE_ERR_HIP = 5                 /* a HIP call or kernel launch failed */
+} moe_status;
+
+#define MOE_ACT_IDENTITY 0
+#define MOE_ACT_SILU_MUL 1
+
+typedef struct {
+    int64_t M;                         /* tokens in the layer call */
+    int32_t K;                         /* hidden size, multiple of 128 */
+    int32_t N;                         /* expert intermediate size, multiple of 128 */
+    int32_t topk;
+    int32_t num_global_experts;        /* Eg */
+    int32_t num_local_experts;         /* El */
+    int32_t align;                     /* row padding per expert: 16, 32, 64 or 128 */
+    int32_t apply_router_weight_on_input; /* 0 or 1 [P20725 Purpose/Changes] */
+    int64_t chunk_size;                /* <= 0 or >= M: one chunk [P20392 Bug 1] */
+} moe_problem;
+
+const char* moe_status_string(int status);
+const char* moe_last_error(void);
+
+/* Rows a padded, expert-contiguous permuted buffer needs for Mc tokens, for
+ * any routing: P + min(El, P) * (align - 1) with P = Mc * topk.  Returns -1 on
+ * bad arguments.  Sync-free stand-in for sizing from host-side expert counts
+ * [P20903 Purpose item 1]. */
+int64_t moe_max_rows(int64_t Mc, int32_t topk, int32_t El, int32_t align);
+
+/* Workspace bytes moe_forward_chunked needs for problem p (sized for the
+ * largest chunk and reused by every chunk). */
+int moe_forward_workspace_size(const moe_problem* p, size_t* bytes);
+
+/* Workspace bytes moe_permute needs for Mc tokens. */
+int moe_permute_workspace_size(int64_t Mc, int32_t topk, int32_t El, size_t* bytes);
+
+/* count_expert_num_tokens [P20392 Bug 2; review thread]:
+ *   counts[e] = #{ f < num_pairs : local(topk_ids[f]) == e },  e < El.
+ * topk_ids: [num_pairs] int32 global ids.  expert_map: [Eg] int32 or NULL
+ * (identity, requires El <= Eg).  counts: [El] int32, overwritten.
+ * invalid_ids: NULL or [1] int32, overwritten with the number of ids outside
+ * [-1, Eg).  Exact integer counts. */
+int moe_count(const int32_t* topk_ids, int64_t num_pairs, const int32_t* expert_map, int32_t Eg,
+              int32_t El, int32_t* counts, int32_t* invalid_ids, void* stream);
+
+/* ep_scatter permute [P20903 Purpose item 2]:
+ *   counts as moe_count; expert_offsets[0] = 0,
+ *   expert_offsets[e+1] = expert_offsets[e] + align * ceil(counts[e] / align);
+ *   pair f = t*topk + k with local expert e takes row
+ *   expert_offsets[e] + #{ f' < f : local(f') == e }   (stable order);
+ *   a_perm[row] = a_q[t];  a_perm_s[row] = a_s[t] (times topk_weights[f]
+ *   when apply_on_input [P20725 Purpose/Changes]);
+ *   inv_perm[f] = row or -1;  row_src[row] = t, -1 on padding rows and on
+ *   rows in [expert_offsets[El], cap_rows).
+ * a_q [Mc,K] e4m3, a_s [Mc,K/128] f32, topk_ids [Mc,topk], topk_weights
+ * [Mc,topk] f32 (read only if apply_on_input), cap_rows >= moe_max_rows(),
+ * a_perm [cap_rows,K], a_perm_s [cap_rows,K/128], counts [El],
+ * expert_offsets [El+1], inv_perm [Mc,topk], row_src [cap_rows].
+ * Padding rows of a_perm / a_perm_s are left unwritten.
+ * workspace: >= moe_permute_workspace_size() bytes of device memory. */
+int moe_permute(const uint8_t* a_q, const float* a_s, const int32_t* topk_ids,
+                const float* topk_weights, int32_t apply_on_input, int64_t Mc, int32_t K,
+                int32_t topk, const int32_t* expert_map, int32_t Eg, int32_t El, int32_t align,
+                int64_t cap_rows, uint8_t* a_perm, float* a_perm_s, int32_t* counts,
+                int32_t* expert_offsets, int32_t* inv_perm, int32_t* row_src, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/* Block-scaled fp8 grouped GEMM (the DeepGEMM grouped GEMM of [P20903],
+ * Optimizations: e4m3, 128x128 blocks).  For every valid row r of expert e
+ * (expert_offsets[e] <= r < expert_offsets[e] + counts[e]) and n < n_out:
+ *   out[r,n] = bf16( sum_g a_s[r,g] * w_s[e, n/128, g] *
+ *                    sum_{k in group g} a[r,k] * w[e,n,k] ),
+ * fp32 accumulation.  a [cap_rows,k_in] e4m3, a_s [cap_rows,k_in/128] f32,
+ * w [El,n_out,k_in] e4m3, w_s [El,n_out/128,k_in/128] f32,
+ * out [cap_rows,n_out] bf16.  Rows that are not valid are not written. */
+int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const uint8_t* w, const float* w_s,
+                         const int32_t* expert_offsets, const int32_t* counts, int32_t El,
+                         int64_t cap_rows, int32_t n_out, int32_t k_in, uint16_t* out,
+                         void* stream);
+
+/* Per-token-group (1x128) fp8 quantisation.
+ *   MOE_ACT_IDENTITY: v = in[r, :n]                        (in is [rows, n])
+ *   MOE_ACT_SILU_MUL: v = bf16(silu(in[r, :n]) * in[r, n:2n]) (in is [rows, 2n])
+ * then per group of 128: d = max(amax|v|, 1e-10), q_s = d/448,
+ * q = e4m3(v * (448/d)) (saturating, nearest-even).
+ * expert_offsets / counts: NULL = every row valid; otherwise only valid rows
+ * (as in moe_grouped_gemm_fp8) are written.  q [rows,n], q_s [rows,n/128]. */
+int moe_act_quant(const uint16_t* in, int64_t rows, int32_t n, int32_t mode,
+                  const int32_t* expert_offsets, const int32_t* counts, int32_t El, uint8_t* q,
+                  float* q_s, void* stream);
+
+/* ep_gather unpermute with topk weight and reduce [P20903 Highlights;
+ * P20725 Purpose]: for each token t and column c,
+ *   acc = +0; for k = 0..topk-1 with 0 <= inv_perm[t,k] < y_rows:
+ *       acc = fmaf(w', y[inv_perm[t,k], c], acc)
+ *   out[t,c] = bf16(acc),  w' = topk_weights[t,k], or 1 when apply_on_input.
+ * y [y_rows,K] bf16, inv_perm [Mc,topk], topk_weights [Mc,topk] f32 (unread
+ * if apply_on_input), out [Mc,K] bf16 (must not overlap y).  Rows outside
+ * [0, y_rows) are never read. */
+int moe_unpermute_weight_reduce(const uint16_t* y, int64_t y_rows, const int32_t* inv_perm,
+                                const float* topk_weights, int64_t Mc, int32_t K, int32_t topk,
+                                int32_t apply_on_input, uint16_t* out, void* stream);
+
+/* The whole layer, chunked over M [P20392 Purpose]: for each chunk of
+ * chunk_size tokens (the last one may be short) it runs input quant, count,
+ * permute, GEMM(w13), SiLU-mul requant, GEMM(w2) and unpermute into the
+ * chunk's rows of out.  Counts and shapes are per chunk; the workspace is
+ * reused, laid out so that out never aliases it [P20725 author notes].
+ * x [M,K] bf16, topk_ids [M,topk], topk_weights [M,topk] f32, expert_map
+ * [Eg] or NULL, w13 [El,2N,K] e4m3, w13_s [El,2N/128,K/128] f32, w2 [El,K,N]
+ * e4m3, w2_s [El,K/128,N/128] f32, out [M,K] bf16, workspace >=
+ * moe_forward_workspace_size(p).  per_chunk_counts: NULL or device
+ * [num_chunks, El] int32 receiving each chunk's counts. */
+int moe_forward_chunked(const moe_problem* p, const uint16_t* x, const int32_t* topk_ids,
+                        const float* topk_weights, const int32_t* expert_map, const uint8_t* w13,
+                        const float* w13_s, const uint8_t* w2, const float* w2_s, uint16_t* out,
+                        void* workspace, size_t workspace_bytes, int32_t* per_chunk_counts,
+                        void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,59 @@
+"""Helpers shared by the GPU parity tests: device transfer and comparisons."""
+import sys
+
+import numpy as np
+import torch
+
+DEV = "cuda:0"
+RTOL, ATOL = 1e-2, 1e-3   # bf16 outputs: |gpu - ref| <= ATOL + RTOL*|ref|
+
+
+def announce(*what):
+    print("CASE", *what, flush=True)
+    sys.stdout.flush()
+
+
+# bf16 travels as raw 16-bit patterns: numpy uint16 on the host, torch int16
+# on the device (only data_ptr() is handed to the library).
+def dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a.copy()).to(DEV)
+
+
+def host(t: torch.Tensor, bf16=False) -> np.ndarray:
+    torch.cuda.synchronize()
+    a = t.cpu().numpy()
+    return a.view(np.uint16) if (bf16 or t.dtype == torch.int16) else a
+
+
+def empty(shape, dtype) -> torch.Tensor:
+    if dtype == "bf16":
+        dtype = torch.int16
+    return torch.empty(shape, dtype=dtype, device=DEV)
+
+
+def filled(shape, dtype, v) -> torch.Tensor:
+    if dtype == "bf16":
+        dtype = torch.int16
+    return torch.full(shape, v, dtype=dtype, device=DEV)
+
+
+def bf16_f64(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def assert_bf16_close(got: np.ndarray, ref: np.ndarray, what=""):
+    g, r = bf16_f64(got), bf16_f64(ref)
+    bad = ~(np.abs(g - r) <= ATOL + RTOL * np.abs(r))
+    bad &= ~(np.isnan(g) & np.isnan(r))
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; first {idx.tolist()} "
+                             f"got {g[tuple(idx[0])]} ref {r[tuple(idx[0])]}")
+
+
+def valid_rows(offsets: np.ndarray, counts: np.ndarray) -> np.ndarray:
+    return np.concatenate([np.arange(offsets[e], offsets[e] + counts[e]) for e in range(len(counts))]
+                          + [np.zeros(0, np.int64)]).astype(np.int64)

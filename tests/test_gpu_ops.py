@@ -1,0 +1,283 @@
+"""Per-op parity of the gfx950 kernels (through the C ABI) with the CPU oracle.
+
+Same seeded inputs on both sides.  Bit-exact: counts, offsets, inv_perm,
+row_src, permuted rows and scales, act-quant codes and scales, unpermute.
+GEMM: within |d| <= 1e-3 + 1e-2|ref| of the oracle, and bit-exact against an
+int64 matmul in the integer special case.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import unpermute_count_expert_amd as moe
+from unpermute_count_expert_amd import generators as gen
+from tests.gpu_helpers import (announce, assert_bf16_close, dev, empty, filled, host, valid_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+# ---------------------------------------------------------------- act quant
+def _gpu_quant_identity(x_bits):
+    rows, n = x_bits.shape
+    q = empty((rows, n), torch.uint8)
+    s = empty((rows, n // 128), torch.float32)
+    moe.moe_act_quant(dev(x_bits), n, moe.MOE_ACT_IDENTITY, q, s)
+    return host(q), host(s)
+
+
+def test_e4m3_every_bf16_value_through_identity_quant():
+    """Groups anchored by 448 have scale 448/448 = 1, so each code is e4m3(v)
+    of the bf16 input itself: every finite bf16 pattern with |v| <= 448, and
+    NaNs, are encoded exactly as the oracle encodes them."""
+    announce("e4m3 all-bf16 anchored")
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = (pats.astype(np.uint32) << 16).view(np.float32)
+    keep = np.isnan(v) | (np.abs(v) <= 448)
+    pats = pats[keep]
+    pad = (-len(pats)) % 127
+    pats = np.concatenate([pats, np.zeros(pad, np.uint16)]).reshape(-1, 127)
+    anchor = np.full((pats.shape[0], 1), 0x43E0, np.uint16)   # bf16 448.0
+    x = np.concatenate([anchor, pats], axis=1)                 # rows of one group
+    q, s = _gpu_quant_identity(x)
+    qr, sr = oracle.act_quant_identity(x)
+    np.testing.assert_array_equal(s, sr)
+    assert np.all(s == 1.0)
+    np.testing.assert_array_equal(q, qr)
+
+
+def test_identity_quant_all_bf16_patterns_shuffled():
+    announce("identity quant shuffled patterns")
+    rng = np.random.default_rng(0)
+    pats = rng.permutation(np.arange(65536, dtype=np.uint32)).astype(np.uint16)
+    x = pats.reshape(-1, 256)
+    q, s = _gpu_quant_identity(x)
+    qr, sr = oracle.act_quant_identity(x)
+    np.testing.assert_array_equal(s, sr)
+    np.testing.assert_array_equal(q, qr)
+
+
+@pytest.mark.parametrize("rows,n,scale", [(1, 128, 1.0), (37, 384, 1e-3), (4096, 2048, 1.0),
+                                          (16384, 2048, 3.0)])
+def test_identity_quant_parity(rows, n, scale):
+    announce("identity quant", rows, n, scale)
+    rng = np.random.default_rng(rows + n)
+    x = gen.bf16_bits((rng.standard_normal((rows, n)) * scale).astype(np.float32))
+    q, s = _gpu_quant_identity(x)
+    qr, sr = oracle.act_quant_identity(x)
+    np.testing.assert_array_equal(s, sr)
+    np.testing.assert_array_equal(q, qr)
+
+
+@pytest.mark.parametrize("masked", [False, True])
+def test_silu_mul_quant_parity(masked):
+    announce("silu quant masked" if masked else "silu quant")
+    rng = np.random.default_rng(5)
+    rows, n = 1000, 768
+    h = gen.bf16_bits((rng.standard_normal((rows, 2 * n)) * 4).astype(np.float32))
+    # a few extreme gates: large positive / negative, exp clamp region, zeros
+    h[0, :8] = gen.bf16_bits(np.array([100, -100, 88.5, -87, 0, -0.0, 1e-30, -3e4], np.float32))
+    offs = cnt = None
+    El = 0
+    if masked:
+        cnt = np.array([1, 0, 129, 300, 7], np.int32)
+        offs = np.concatenate([[0], np.cumsum(128 * ((cnt + 127) // 128))]).astype(np.int32)
+        El = len(cnt)
+        assert offs[-1] <= rows
+    q = filled((rows, n), torch.uint8, 0xAB)
+    s = filled((rows, n // 128), torch.float32, -7.0)
+    moe.moe_act_quant(dev(h), n, moe.MOE_ACT_SILU_MUL, q, s,
+                      dev(offs) if masked else None, dev(cnt) if masked else None, El)
+    qg, sg = host(q), host(s)
+    qr, sr = oracle.silu_mul_quant(h, offs, cnt, El)
+    rows_v = valid_rows(offs, cnt) if masked else np.arange(rows)
+    np.testing.assert_array_equal(sg[rows_v], sr[rows_v])
+    np.testing.assert_array_equal(qg[rows_v], qr[rows_v])
+    if masked:
+        other = np.setdiff1d(np.arange(rows), rows_v)
+        assert np.all(qg[other] == 0xAB) and np.all(sg[other] == -7.0)
+
+
+# ---------------------------------------------------------------- count
+@pytest.mark.parametrize("M,T,Eg,El,mapped,p_neg,p_bad", [
+    (64, 4, 128, 64, True, 0.0, 0.0),
+    (16384, 8, 128, 128, False, 0.0, 0.0),
+    (1000, 6, 256, 256, False, 0.05, 0.02),
+    (333, 2, 16, 1, True, 0.1, 0.05),
+    (1 << 21, 8, 128, 128, False, 0.0, 0.0),     # 2^24 pairs (64 MiB of ids)
+])
+def test_count_parity(M, T, Eg, El, mapped, p_neg, p_bad):
+    announce("count", M, T, Eg, El, mapped)
+    rng = np.random.default_rng(M + El)
+    ids = gen.random_ids(rng, M, T, Eg, p_neg, p_bad)
+    emap = None
+    if mapped:
+        emap = np.full(Eg, -1, np.int32)
+        emap[rng.permutation(Eg)[:El]] = np.arange(El, dtype=np.int32)
+    counts = filled((El,), torch.int32, 12345)
+    bad = filled((1,), torch.int32, 999)
+    moe.moe_count(dev(ids), dev(emap) if mapped else None, Eg, El, counts, bad)
+    cr, br = oracle.count(ids, emap, Eg, El)
+    np.testing.assert_array_equal(host(counts), cr)
+    assert int(host(bad)[0]) == br
+
+
+def test_count_all_dropped():
+    announce("count all dropped")
+    ids = np.full((50, 4), -1, np.int32)
+    counts = filled((8,), torch.int32, 7)
+    moe.moe_count(dev(ids), None, 8, 8, counts)
+    assert np.all(host(counts) == 0)
+
+
+# ---------------------------------------------------------------- permute
+def _gpu_permute(a_q, a_s, ids, w, on_input, emap, Eg, El, align):
+    Mc, K = a_q.shape
+    T = ids.shape[1]
+    cap = moe.moe_max_rows(Mc, T, El, align)
+    ws = empty((moe.moe_permute_workspace_size(Mc, T, El),), torch.uint8)
+    a_perm = filled((cap, K), torch.uint8, 0)
+    a_perm_s = filled((cap, K // 128), torch.float32, 0)
+    counts = empty((El,), torch.int32)
+    offs = empty((El + 1,), torch.int32)
+    inv = filled((Mc, T), torch.int32, -77)
+    rsrc = filled((cap,), torch.int32, -77)
+    moe.moe_permute(dev(a_q), dev(a_s), dev(ids), dev(w), on_input, dev(emap) if emap is not None else None,
+                    Eg, El, align, cap, a_perm, a_perm_s, counts, offs, inv, rsrc, ws)
+    return dict(a_perm=host(a_perm), a_perm_s=host(a_perm_s), counts=host(counts),
+                expert_offsets=host(offs), inv_perm=host(inv), row_src=host(rsrc), cap_rows=cap)
+
+
+def _check_permute(g, r):
+    for k in ("counts", "expert_offsets", "inv_perm", "row_src"):
+        np.testing.assert_array_equal(g[k], r[k], err_msg=k)
+    rows = valid_rows(r["expert_offsets"], r["counts"])
+    np.testing.assert_array_equal(g["a_perm"][rows], r["a_perm"][rows])
+    np.testing.assert_array_equal(g["a_perm_s"][rows], r["a_perm_s"][rows])
+
+
+@pytest.mark.parametrize("M,K,T,Eg,El,mapped,align,on_input,routing", [
+    (77, 256, 4, 32, 12, True, 128, 0, "random"),
+    (77, 256, 4, 32, 12, True, 16, 1, "random"),
+    (300, 384, 3, 20, 20, False, 32, 0, "random"),
+    (257, 128, 1, 8, 8, False, 64, 1, "random"),
+    (64, 2048, 4, 128, 64, True, 128, 0, "uniform"),       # profiling shape
+    (16384, 2048, 8, 128, 128, False, 128, 0, "uniform"),  # large batch
+    (16384, 2048, 8, 128, 128, False, 128, 1, "hot"),
+    (3, 256, 256, 300, 300, False, 16, 0, "random"),       # topk 256 (one token per block)
+])
+def test_permute_parity(M, K, T, Eg, El, mapped, align, on_input, routing):
+    announce("permute", M, K, T, Eg, El, mapped, align, on_input, routing)
+    rng = np.random.default_rng(M * 7 + T)
+    a_q = gen.random_codes(rng, (M, K))
+    a_s = rng.uniform(0.01, 2, (M, K // 128)).astype(np.float32)
+    if routing == "random":
+        ids = gen.random_ids(rng, M, T, Eg, 0.05, 0.02)
+    else:
+        cfg = gen.small_config(M=M, K=K, N=128, Eg=Eg, El=El, topk=T,
+                               routing="softmax" if routing == "uniform" else "hot", seed=M)
+        ids, _, _ = gen.routing(rng, cfg)
+    w = rng.uniform(0, 1, (M, T)).astype(np.float32)
+    emap = None
+    if mapped:
+        emap = np.full(Eg, -1, np.int32)
+        emap[Eg - El:] = np.arange(El, dtype=np.int32)
+    g = _gpu_permute(a_q, a_s, ids, w, on_input, emap, Eg, El, align)
+    r = oracle.permute(a_q, a_s, ids, w, on_input, emap, Eg, El, align)
+    _check_permute(g, r)
+
+
+def test_permute_single_expert_takes_everything():
+    announce("permute single expert")
+    rng = np.random.default_rng(1)
+    M, K, T = 500, 128, 4
+    a_q = gen.random_codes(rng, (M, K))
+    a_s = rng.uniform(0.5, 1, (M, 1)).astype(np.float32)
+    ids = np.full((M, T), 3, np.int32)
+    w = np.ones((M, T), np.float32)
+    g = _gpu_permute(a_q, a_s, ids, w, 0, None, 8, 8, 128)
+    r = oracle.permute(a_q, a_s, ids, w, 0, None, 8, 8, 128)
+    _check_permute(g, r)
+
+
+# ---------------------------------------------------------------- grouped GEMM
+def _gpu_gemm(a, a_s, w, w_s, offs, cnt):
+    cap, k_in = a.shape
+    El, n_out, _ = w.shape
+    out = filled((cap, n_out), "bf16", 0x7FC1)
+    moe.moe_grouped_gemm_fp8(dev(a), dev(a_s), dev(w), dev(w_s), dev(offs), dev(cnt), out)
+    return host(out, bf16=True)
+
+
+def _segments(counts, align):
+    counts = np.asarray(counts, np.int32)
+    offs = np.concatenate([[0], np.cumsum(align * ((counts + align - 1) // align))]).astype(np.int32)
+    return offs, counts
+
+
+def test_gemm_integer_case_bit_exact():
+    """Codes in {0, +1, -1} with unit scales: every partial and total is an
+    integer of magnitude <= 256, so the result is exact and must equal an
+    int64 matmul bit for bit."""
+    announce("gemm integer")
+    rng = np.random.default_rng(4)
+    El, n_out, k_in = 5, 384, 256
+    offs, cnt = _segments([1, 130, 0, 257, 64], 128)
+    cap = int(offs[-1]) + 40
+    pm1 = np.array([0x00, 0x38, 0xB8], np.uint8)
+    a_i = rng.integers(-1, 2, (cap, k_in))
+    w_i = rng.integers(-1, 2, (El, n_out, k_in))
+    a = pm1[np.where(a_i < 0, 2, a_i)]
+    w = pm1[np.where(w_i < 0, 2, w_i)]
+    a_s = np.ones((cap, k_in // 128), np.float32)
+    w_s = np.ones((El, n_out // 128, k_in // 128), np.float32)
+    out = _gpu_gemm(a, a_s, w, w_s, offs, cnt)
+    for e in range(El):
+        r = np.arange(offs[e], offs[e] + cnt[e])
+        want = a_i[r].astype(np.int64) @ w_i[e].T.astype(np.int64)
+        got = (out[r].astype(np.uint32) << 16).view(np.float32)
+        np.testing.assert_array_equal(got, want.astype(np.float32))
+    # rows outside the valid segments are not written
+    untouched = np.setdiff1d(np.arange(cap), valid_rows(offs, cnt))
+    assert np.all(out[untouched] == 0x7FC1)
+
+
+@pytest.mark.parametrize("El,n_out,k_in,counts,align", [
+    (4, 256, 512, [1, 127, 128, 300], 128),
+    (3, 384, 256, [17, 0, 250], 16),
+    (6, 128, 1024, [5, 33, 64, 1, 0, 129], 32),
+    (2, 1536, 2048, [200, 77], 128),
+])
+def test_gemm_random_parity(El, n_out, k_in, counts, align):
+    announce("gemm random", El, n_out, k_in, counts, align)
+    rng = np.random.default_rng(n_out + k_in)
+    offs, cnt = _segments(counts, align)
+    cap = int(offs[-1]) + 3
+    a = gen.random_codes(rng, (cap, k_in))
+    w = gen.random_codes(rng, (El, n_out, k_in))
+    a_s = rng.uniform(1e-3, 1, (cap, k_in // 128)).astype(np.float32)
+    w_s = rng.uniform(1e-3, 1, (El, n_out // 128, k_in // 128)).astype(np.float32)
+    out = _gpu_gemm(a, a_s, w, w_s, offs, cnt)
+    ref = oracle.grouped_gemm(a, a_s, w, w_s, offs, cnt)
+    rows = valid_rows(offs, cnt)
+    assert_bf16_close(out[rows], ref[rows], "gemm")
+    untouched = np.setdiff1d(np.arange(cap), rows)
+    assert np.all(out[untouched] == 0x7FC1)
+
+
+# ---------------------------------------------------------------- unpermute
+@pytest.mark.parametrize("M,K,T,on_input", [(1, 128, 1, 0), (513, 2048, 8, 0), (100, 384, 3, 1),
+                                            (16384, 2048, 8, 0)])
+def test_unpermute_parity(M, K, T, on_input):
+    announce("unpermute", M, K, T, on_input)
+    rng = np.random.default_rng(M + K)
+    R = M * T + 50
+    y = gen.bf16_bits(rng.standard_normal((R, K)).astype(np.float32))
+    inv = rng.permutation(R)[:M * T].reshape(M, T).astype(np.int32)
+    inv[rng.random((M, T)) < 0.1] = -1
+    w = rng.uniform(0, 1, (M, T)).astype(np.float32)
+    out = filled((M, K), "bf16", 0x7FC1)
+    moe.moe_unpermute_weight_reduce(dev(y), dev(inv), dev(w), on_input, out)
+    got = host(out, bf16=True)
+    ref = oracle.unpermute(y, inv, w, on_input)
+    np.testing.assert_array_equal(got, ref)   # same fmaf order on both sides

@@ -1,0 +1,122 @@
+// act_quant.hip -- per-token 1x128-group fp8 (OCP E4M3FN) quantisation on
+// gfx950: the input activations before the permute (fp8 block-128 tokens and
+// scales of vLLM PR #20903, Optimizations) and SiLU-and-mul + requant between
+// the two grouped GEMMs.
+//
+// Sixteen lanes own one group (8 bf16 = 16 bytes each, fully coalesced); the
+// group amax is a 4-step xor-shuffle inside the 16 lanes; codes leave as one
+// 8-byte store per lane.  Compiled without FMA contraction so each operation
+// below is the IEEE operation written.
+#include "moe_device.hpp"
+#include "moe_internal.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kLanesPerGroup = 16;
+constexpr int kGroupsPerBlock = kThreads / kLanesPerGroup;
+
+struct Vals8 {
+    float v[8];
+};
+
+__device__ __forceinline__ Vals8 unpack_bf16x8(uint4 u) {
+    Vals8 r;
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r.v[2 * i] = __uint_as_float(w[i] << 16);
+        r.v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+    return r;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restrict__ in, int64_t rows,
+                                                        int n, const int32_t* __restrict__ offsets,
+                                                        const int32_t* __restrict__ counts, int El,
+                                                        uint8_t* __restrict__ q,
+                                                        float* __restrict__ q_s) {
+    __shared__ int s_off[kMaxLocalExperts + 1];
+    __shared__ int s_end[kMaxLocalExperts];
+    const bool masked = offsets != nullptr;
+    if (masked) {
+        for (int e = threadIdx.x; e <= El; e += blockDim.x) s_off[e] = offsets[e];
+        for (int e = threadIdx.x; e < El; e += blockDim.x) s_end[e] = offsets[e] + counts[e];
+    }
+    __syncthreads();
+    const int ng = n / kGroup;
+    const int64_t total = rows * ng;
+    const int sub = threadIdx.x & (kLanesPerGroup - 1);
+    for (int64_t grp = (int64_t)blockIdx.x * kGroupsPerBlock + threadIdx.x / kLanesPerGroup; grp < total;
+         grp += (int64_t)gridDim.x * kGroupsPerBlock) {
+        const int64_t r = grp / ng;
+        const int gi = (int)(grp - r * ng);
+        bool valid = true;
+        if (masked) {
+            // the expert segment holding row r: largest e with s_off[e] <= r
+            int lo = 0, hi = El;  // answer in [0, El]
+            while (lo < hi) {
+                int mid = (lo + hi + 1) >> 1;
+                if (s_off[mid] <= r) lo = mid; else hi = mid - 1;
+            }
+            valid = lo < El && r < s_end[lo];
+        }
+        Vals8 x;
+        if (MODE == MOE_ACT_IDENTITY_K) {
+            const uint4 u = *reinterpret_cast<const uint4*>(in + r * n + gi * kGroup + sub * 8);
+            x = unpack_bf16x8(u);
+        } else {
+            const uint16_t* base = in + r * 2 * (int64_t)n + gi * kGroup + sub * 8;
+            const Vals8 g = unpack_bf16x8(*reinterpret_cast<const uint4*>(base));
+            const Vals8 u = unpack_bf16x8(*reinterpret_cast<const uint4*>(base + n));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float e = exp_pinned(-g.v[i]);
+                const float s = g.v[i] / (1.0f + e);
+                const float prod = s * u.v[i];
+                x.v[i] = bf16_to_f32(f32_to_bf16(prod));
+            }
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x.v[i]));
+#pragma unroll
+        for (int d = kLanesPerGroup / 2; d >= 1; d >>= 1)
+            amax = __builtin_fmaxf(amax, __shfl_xor(amax, d, kWave));
+        const float dd = __builtin_fmaxf(amax, 1e-10f);
+        const float scale = dd / 448.0f;
+        const float inv = 448.0f / dd;
+        float t[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t[i] = x.v[i] * inv;
+        uint2 codes;
+        codes.x = f32x4_to_e4m3(t[0], t[1], t[2], t[3]);
+        codes.y = f32x4_to_e4m3(t[4], t[5], t[6], t[7]);
+        if (valid) {
+            *reinterpret_cast<uint2*>(q + r * n + gi * kGroup + sub * 8) = codes;
+            if (sub == 0) q_s[r * ng + gi] = scale;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_act_quant(const uint16_t* in, int64_t rows, int n, int mode,
+                            const int32_t* offsets, const int32_t* counts, int El, uint8_t* q,
+                            float* q_s, hipStream_t s) {
+    const int64_t groups = rows * (n / kGroup);
+    if (groups <= 0) return hipSuccess;
+    int64_t blocks = (groups + kGroupsPerBlock - 1) / kGroupsPerBlock;
+    if (blocks > 8192) blocks = 8192;
+    if (mode == MOE_ACT_IDENTITY_K)
+        k_act_quant<MOE_ACT_IDENTITY_K><<<(unsigned)blocks, kThreads, 0, s>>>(in, rows, n, offsets, counts,
+                                                                             El, q, q_s);
+    else
+        k_act_quant<MOE_ACT_SILU_MUL_K><<<(unsigned)blocks, kThreads, 0, s>>>(in, rows, n, offsets, counts,
+                                                                             El, q, q_s);
+    return hipGetLastError();
+}
+
+}  // namespace moe

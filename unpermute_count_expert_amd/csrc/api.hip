@@ -1,0 +1,384 @@
+// api.hip -- the C ABI of include/moe.h: host-side validation, the workspace
+// plan and the chunk loop of the MoE expert pipeline on gfx950.
+//
+// Every entry point validates its arguments before enqueuing anything, so a
+// bad call leaves the stream untouched.  Nothing here allocates, frees or
+// synchronises device memory.
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "moe.h"
+#include "moe_device.hpp"
+#include "moe_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_dev_cus[kMaxDevices];
+
+// Confirms the current device is gfx950 (cached per device) and returns its
+// compute-unit count through *cus.
+int check_device(int* cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice failed");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED_DEVICE, "device %d", dev);
+    int st = g_dev_state[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return fail(MOE_ERR_HIP, "hipGetDeviceProperties failed");
+        const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        g_dev_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+        st = ok ? 1 : 2;
+        g_dev_state[dev].store(st, std::memory_order_release);
+    }
+    if (st != 1) return fail(MOE_ERR_UNSUPPORTED_DEVICE, "device %d is not gfx950", dev);
+    if (cus) *cus = g_dev_cus[dev].load(std::memory_order_relaxed);
+    return MOE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE(cond, status, ...) \
+    do {                           \
+        if (!(cond)) return fail(status, __VA_ARGS__); \
+    } while (0)
+
+#define REQUIRE_PTR(p) \
+    REQUIRE((p) != nullptr && aligned16(p), MOE_ERR_INVALID_ARG, "%s must be a non-null 16-byte aligned device pointer", #p)
+
+#define HIP_OK(expr)                                                                   \
+    do {                                                                               \
+        hipError_t e_ = (expr);                                                        \
+        if (e_ != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+    } while (0)
+
+bool valid_align(int a) { return a == 16 || a == 32 || a == 64 || a == 128; }
+
+int64_t max_rows(int64_t Mc, int32_t topk, int32_t El, int32_t align) {
+    if (Mc < 0 || topk <= 0 || El <= 0 || !valid_align(align)) return -1;
+    const int64_t p = Mc * topk;
+    const int64_t ne = p < El ? p : El;
+    return p + ne * (align - 1);
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return na && nb && x < y + nb && y < x + na;
+}
+
+size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// The forward workspace, carved once for the largest chunk and reused by all.
+//   bufA   a_perm [cap,K] then act_q [cap,N]          (e4m3)
+//   bufAs  a_perm_s then act_s                         (fp32 scales)
+//   bufB   a_q, a_s (before the permute), then h [cap,2N], then y [cap,K] (bf16)
+//   small  counts, offsets, inv_perm, row_src, per-block histogram
+// Each buffer is dead before it is reused: GEMM1 reads bufA and writes bufB,
+// act-quant reads bufB and writes bufA, GEMM2 reads bufA and writes bufB,
+// the unpermute reads bufB.  The output never aliases the workspace.
+struct Plan {
+    int64_t cs, cap, nblk;
+    size_t bufA, bufAs, bufB, a_s_in_B, counts, offsets, inv, rsrc, hist, total;
+};
+
+Plan make_plan(const moe_problem& p) {
+    Plan pl{};
+    pl.cs = (p.chunk_size <= 0 || p.chunk_size >= p.M) ? p.M : p.chunk_size;
+    if (pl.cs < 1) pl.cs = 1;
+    pl.cap = max_rows(pl.cs, p.topk, p.num_local_experts, p.align);
+    pl.nblk = moe::permute_num_blocks(pl.cs, p.topk);
+    const int64_t K = p.K, N = p.N, El = p.num_local_experts;
+    const int64_t wA = K > N ? K : N;
+    const int64_t wB = (2 * N > K ? 2 * N : K) * 2;
+    size_t off = 0;
+    pl.bufA = off;  off += up256((size_t)pl.cap * wA);
+    pl.bufAs = off; off += up256((size_t)pl.cap * (wA / moe::kGroup) * 4);
+    pl.bufB = off;
+    pl.a_s_in_B = up256((size_t)pl.cs * K);
+    size_t bsz = (size_t)pl.cap * wB;
+    const size_t need_in = pl.a_s_in_B + (size_t)pl.cs * (K / moe::kGroup) * 4;
+    if (need_in > bsz) bsz = need_in;
+    off += up256(bsz);
+    pl.counts = off;  off += up256((size_t)El * 4);
+    pl.offsets = off; off += up256((size_t)(El + 1) * 4);
+    pl.inv = off;     off += up256((size_t)pl.cs * p.topk * 4);
+    pl.rsrc = off;    off += up256((size_t)pl.cap * 4);
+    pl.hist = off;    off += up256((size_t)pl.nblk * El * 4);
+    pl.total = off;
+    return pl;
+}
+
+int check_problem(const moe_problem* p) {
+    REQUIRE(p != nullptr, MOE_ERR_INVALID_ARG, "problem is NULL");
+    REQUIRE(p->M >= 0, MOE_ERR_SHAPE, "M=%lld < 0", (long long)p->M);
+    REQUIRE(p->K > 0 && p->K % moe::kGroup == 0, MOE_ERR_SHAPE, "K=%d is not a positive multiple of 128", p->K);
+    REQUIRE(p->N > 0 && p->N % moe::kGroup == 0, MOE_ERR_SHAPE, "N=%d is not a positive multiple of 128", p->N);
+    REQUIRE(p->topk >= 1 && p->topk <= 256, MOE_ERR_SHAPE, "topk=%d outside [1,256]", p->topk);
+    REQUIRE(p->num_global_experts >= 1, MOE_ERR_SHAPE, "Eg=%d", p->num_global_experts);
+    REQUIRE(p->num_local_experts >= 1 && p->num_local_experts <= moe::kMaxLocalExperts, MOE_ERR_SHAPE,
+            "El=%d outside [1,1024]", p->num_local_experts);
+    REQUIRE(valid_align(p->align), MOE_ERR_SHAPE, "align=%d not in {16,32,64,128}", p->align);
+    REQUIRE(p->apply_router_weight_on_input == 0 || p->apply_router_weight_on_input == 1,
+            MOE_ERR_INVALID_ARG, "apply_router_weight_on_input=%d", p->apply_router_weight_on_input);
+    const int64_t cs = (p->chunk_size <= 0 || p->chunk_size >= p->M) ? p->M : p->chunk_size;
+    const int64_t cap = max_rows(cs > 0 ? cs : 1, p->topk, p->num_local_experts, p->align);
+    REQUIRE(cs * p->topk < (int64_t(1) << 31) && cap < (int64_t(1) << 31), MOE_ERR_SHAPE,
+            "chunk of %lld tokens x topk %d is too large", (long long)cs, p->topk);
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int s) {
+    switch (s) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+        case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE";
+        case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+        case MOE_ERR_UNSUPPORTED_DEVICE: return "MOE_ERR_UNSUPPORTED_DEVICE";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+        default: return "MOE_ERR_UNKNOWN";
+    }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+int64_t moe_max_rows(int64_t Mc, int32_t topk, int32_t El, int32_t align) {
+    return max_rows(Mc, topk, El, align);
+}
+
+int moe_forward_workspace_size(const moe_problem* p, size_t* bytes) {
+    int st = check_problem(p);
+    if (st) return st;
+    REQUIRE(bytes != nullptr, MOE_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = make_plan(*p).total;
+    return MOE_OK;
+}
+
+int moe_permute_workspace_size(int64_t Mc, int32_t topk, int32_t El, size_t* bytes) {
+    REQUIRE(bytes != nullptr, MOE_ERR_INVALID_ARG, "bytes is NULL");
+    REQUIRE(Mc >= 0 && topk >= 1 && topk <= 256 && El >= 1 && El <= moe::kMaxLocalExperts, MOE_ERR_SHAPE,
+            "Mc=%lld topk=%d El=%d", (long long)Mc, topk, El);
+    *bytes = up256((size_t)moe::permute_num_blocks(Mc, topk) * El * 4);
+    if (*bytes == 0) *bytes = 256;
+    return MOE_OK;
+}
+
+int moe_count(const int32_t* topk_ids, int64_t num_pairs, const int32_t* expert_map, int32_t Eg,
+              int32_t El, int32_t* counts, int32_t* invalid_ids, void* stream) {
+    REQUIRE(num_pairs >= 0, MOE_ERR_SHAPE, "num_pairs < 0");
+    REQUIRE(Eg >= 1 && El >= 1 && El <= moe::kMaxLocalExperts, MOE_ERR_SHAPE, "Eg=%d El=%d", Eg, El);
+    REQUIRE(expert_map != nullptr || El <= Eg, MOE_ERR_SHAPE, "El > Eg without an expert map");
+    if (num_pairs > 0) REQUIRE_PTR(topk_ids);
+    REQUIRE(counts != nullptr && ((uintptr_t)counts & 3u) == 0, MOE_ERR_INVALID_ARG, "counts");
+    REQUIRE(expert_map == nullptr || ((uintptr_t)expert_map & 3u) == 0, MOE_ERR_INVALID_ARG, "expert_map");
+    REQUIRE(invalid_ids == nullptr || ((uintptr_t)invalid_ids & 3u) == 0, MOE_ERR_INVALID_ARG, "invalid_ids");
+    int st = check_device(nullptr);
+    if (st) return st;
+    HIP_OK(moe::launch_count(topk_ids, num_pairs, expert_map, Eg, El, counts, invalid_ids,
+                             static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
+int moe_permute(const uint8_t* a_q, const float* a_s, const int32_t* topk_ids,
+                const float* topk_weights, int32_t apply_on_input, int64_t Mc, int32_t K,
+                int32_t topk, const int32_t* expert_map, int32_t Eg, int32_t El, int32_t align,
+                int64_t cap_rows, uint8_t* a_perm, float* a_perm_s, int32_t* counts,
+                int32_t* expert_offsets, int32_t* inv_perm, int32_t* row_src, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    REQUIRE(Mc >= 0, MOE_ERR_SHAPE, "Mc < 0");
+    REQUIRE(K > 0 && K % moe::kGroup == 0, MOE_ERR_SHAPE, "K=%d is not a positive multiple of 128", K);
+    REQUIRE(topk >= 1 && topk <= 256, MOE_ERR_SHAPE, "topk=%d outside [1,256]", topk);
+    REQUIRE(Eg >= 1 && El >= 1 && El <= moe::kMaxLocalExperts, MOE_ERR_SHAPE, "Eg=%d El=%d", Eg, El);
+    REQUIRE(expert_map != nullptr || El <= Eg, MOE_ERR_SHAPE, "El > Eg without an expert map");
+    REQUIRE(valid_align(align), MOE_ERR_SHAPE, "align=%d not in {16,32,64,128}", align);
+    REQUIRE(apply_on_input == 0 || apply_on_input == 1, MOE_ERR_INVALID_ARG, "apply_on_input=%d", apply_on_input);
+    REQUIRE(Mc * topk < (int64_t(1) << 31) && cap_rows < (int64_t(1) << 31), MOE_ERR_SHAPE, "too many rows");
+    const int64_t need_rows = max_rows(Mc, topk, El, align);
+    REQUIRE(cap_rows >= need_rows, MOE_ERR_WORKSPACE_TOO_SMALL, "cap_rows=%lld < %lld",
+            (long long)cap_rows, (long long)need_rows);
+    size_t need_ws = 0;
+    moe_permute_workspace_size(Mc, topk, El, &need_ws);
+    REQUIRE(workspace_bytes >= need_ws, MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes",
+            workspace_bytes, need_ws);
+    REQUIRE_PTR(workspace);
+    REQUIRE_PTR(counts);
+    REQUIRE_PTR(expert_offsets);
+    if (cap_rows > 0) REQUIRE_PTR(row_src);
+    if (Mc > 0) {
+        REQUIRE_PTR(a_q);
+        REQUIRE_PTR(a_s);
+        REQUIRE_PTR(topk_ids);
+        REQUIRE_PTR(a_perm);
+        REQUIRE_PTR(a_perm_s);
+        REQUIRE_PTR(inv_perm);
+        if (apply_on_input) REQUIRE_PTR(topk_weights);
+    }
+    REQUIRE(expert_map == nullptr || aligned16(expert_map), MOE_ERR_INVALID_ARG, "expert_map alignment");
+    int st = check_device(nullptr);
+    if (st) return st;
+    HIP_OK(moe::launch_permute(a_q, a_s, topk_ids, topk_weights, apply_on_input, Mc, K, topk, expert_map,
+                               Eg, El, align, cap_rows, a_perm, a_perm_s, counts, expert_offsets, inv_perm,
+                               row_src, static_cast<int32_t*>(workspace), nullptr,
+                               static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
+int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const uint8_t* w, const float* w_s,
+                         const int32_t* expert_offsets, const int32_t* counts, int32_t El,
+                         int64_t cap_rows, int32_t n_out, int32_t k_in, uint16_t* out,
+                         void* stream) {
+    REQUIRE(El >= 1 && El <= moe::kMaxLocalExperts, MOE_ERR_SHAPE, "El=%d outside [1,1024]", El);
+    REQUIRE(n_out > 0 && n_out % moe::kGroup == 0, MOE_ERR_SHAPE, "n_out=%d is not a positive multiple of 128", n_out);
+    REQUIRE(k_in > 0 && k_in % moe::kGroup == 0, MOE_ERR_SHAPE, "k_in=%d is not a positive multiple of 128", k_in);
+    REQUIRE(cap_rows >= 0 && cap_rows < (int64_t(1) << 31), MOE_ERR_SHAPE, "cap_rows=%lld", (long long)cap_rows);
+    if (cap_rows == 0) return MOE_OK;
+    REQUIRE_PTR(a);
+    REQUIRE_PTR(a_s);
+    REQUIRE_PTR(w);
+    REQUIRE_PTR(w_s);
+    REQUIRE_PTR(expert_offsets);
+    REQUIRE_PTR(counts);
+    REQUIRE_PTR(out);
+    int cus = 0;
+    int st = check_device(&cus);
+    if (st) return st;
+    HIP_OK(moe::launch_grouped_gemm(a, a_s, w, w_s, expert_offsets, counts, El, cap_rows, n_out, k_in, out,
+                                    cus, static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
+int moe_act_quant(const uint16_t* in, int64_t rows, int32_t n, int32_t mode,
+                  const int32_t* expert_offsets, const int32_t* counts, int32_t El, uint8_t* q,
+                  float* q_s, void* stream) {
+    REQUIRE(rows >= 0, MOE_ERR_SHAPE, "rows < 0");
+    REQUIRE(n > 0 && n % moe::kGroup == 0, MOE_ERR_SHAPE, "n=%d is not a positive multiple of 128", n);
+    REQUIRE(mode == MOE_ACT_IDENTITY || mode == MOE_ACT_SILU_MUL, MOE_ERR_INVALID_ARG, "mode=%d", mode);
+    REQUIRE((expert_offsets == nullptr) == (counts == nullptr), MOE_ERR_INVALID_ARG,
+            "expert_offsets and counts must both be given or both be NULL");
+    if (expert_offsets) {
+        REQUIRE(El >= 1 && El <= moe::kMaxLocalExperts, MOE_ERR_SHAPE, "El=%d outside [1,1024]", El);
+        REQUIRE_PTR(expert_offsets);
+        REQUIRE_PTR(counts);
+    }
+    if (rows == 0) return MOE_OK;
+    REQUIRE_PTR(in);
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(q_s);
+    int st = check_device(nullptr);
+    if (st) return st;
+    HIP_OK(moe::launch_act_quant(in, rows, n, mode, expert_offsets, counts, El, q, q_s,
+                                 static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
+int moe_unpermute_weight_reduce(const uint16_t* y, int64_t y_rows, const int32_t* inv_perm,
+                                const float* topk_weights, int64_t Mc, int32_t K, int32_t topk,
+                                int32_t apply_on_input, uint16_t* out, void* stream) {
+    REQUIRE(Mc >= 0 && y_rows >= 0, MOE_ERR_SHAPE, "Mc / y_rows < 0");
+    REQUIRE(K > 0 && K % moe::kGroup == 0, MOE_ERR_SHAPE, "K=%d is not a positive multiple of 128", K);
+    REQUIRE(topk >= 1 && topk <= 256, MOE_ERR_SHAPE, "topk=%d outside [1,256]", topk);
+    REQUIRE(apply_on_input == 0 || apply_on_input == 1, MOE_ERR_INVALID_ARG, "apply_on_input=%d", apply_on_input);
+    if (Mc == 0) return MOE_OK;
+    REQUIRE_PTR(inv_perm);
+    REQUIRE_PTR(out);
+    if (y_rows > 0) REQUIRE_PTR(y);
+    if (!apply_on_input) REQUIRE_PTR(topk_weights);
+    REQUIRE(!overlaps(out, (size_t)Mc * K * 2, y, (size_t)y_rows * K * 2), MOE_ERR_INVALID_ARG,
+            "out overlaps y");
+    int st = check_device(nullptr);
+    if (st) return st;
+    HIP_OK(moe::launch_unpermute(y, y_rows, inv_perm, topk_weights, Mc, K, topk, apply_on_input, out,
+                                 static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
+int moe_forward_chunked(const moe_problem* p, const uint16_t* x, const int32_t* topk_ids,
+                        const float* topk_weights, const int32_t* expert_map, const uint8_t* w13,
+                        const float* w13_s, const uint8_t* w2, const float* w2_s, uint16_t* out,
+                        void* workspace, size_t workspace_bytes, int32_t* per_chunk_counts,
+                        void* stream) {
+    int st = check_problem(p);
+    if (st) return st;
+    const moe_problem& P = *p;
+    REQUIRE(expert_map != nullptr || P.num_local_experts <= P.num_global_experts, MOE_ERR_SHAPE,
+            "El > Eg without an expert map");
+    if (P.M == 0) return MOE_OK;
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(topk_ids);
+    REQUIRE_PTR(topk_weights);
+    REQUIRE_PTR(w13);
+    REQUIRE_PTR(w13_s);
+    REQUIRE_PTR(w2);
+    REQUIRE_PTR(w2_s);
+    REQUIRE_PTR(out);
+    REQUIRE_PTR(workspace);
+    REQUIRE(expert_map == nullptr || aligned16(expert_map), MOE_ERR_INVALID_ARG, "expert_map alignment");
+    REQUIRE(per_chunk_counts == nullptr || aligned16(per_chunk_counts), MOE_ERR_INVALID_ARG,
+            "per_chunk_counts alignment");
+    const Plan pl = make_plan(P);
+    REQUIRE(workspace_bytes >= pl.total, MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes",
+            workspace_bytes, pl.total);
+    const size_t out_bytes = (size_t)P.M * P.K * 2;
+    REQUIRE(!overlaps(out, out_bytes, workspace, pl.total), MOE_ERR_INVALID_ARG, "out overlaps the workspace");
+    REQUIRE(!overlaps(out, out_bytes, x, out_bytes), MOE_ERR_INVALID_ARG, "out overlaps x");
+    int cus = 0;
+    st = check_device(&cus);
+    if (st) return st;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    uint8_t* bufA = ws + pl.bufA;
+    float* bufAs = reinterpret_cast<float*>(ws + pl.bufAs);
+    uint8_t* bufB = ws + pl.bufB;
+    uint8_t* a_q = bufB;
+    float* a_s = reinterpret_cast<float*>(bufB + pl.a_s_in_B);
+    uint16_t* hy = reinterpret_cast<uint16_t*>(bufB);
+    int32_t* counts = reinterpret_cast<int32_t*>(ws + pl.counts);
+    int32_t* offsets = reinterpret_cast<int32_t*>(ws + pl.offsets);
+    int32_t* inv = reinterpret_cast<int32_t*>(ws + pl.inv);
+    int32_t* rsrc = reinterpret_cast<int32_t*>(ws + pl.rsrc);
+    int32_t* hist = reinterpret_cast<int32_t*>(ws + pl.hist);
+
+    const int64_t K = P.K, N = P.N, T = P.topk, El = P.num_local_experts;
+    const int on_in = P.apply_router_weight_on_input;
+    const int64_t nchunks = (P.M + pl.cs - 1) / pl.cs;
+    for (int64_t c = 0; c < nchunks; ++c) {
+        const int64_t t0 = c * pl.cs;
+        const int64_t Mc = (t0 + pl.cs <= P.M) ? pl.cs : (P.M - t0);
+        const int32_t* ids_c = topk_ids + t0 * T;
+        const float* w_c = topk_weights + t0 * T;
+        HIP_OK(moe::launch_act_quant(x + t0 * K, Mc, (int)K, moe::MOE_ACT_IDENTITY_K, nullptr, nullptr, 0,
+                                     a_q, a_s, s));
+        HIP_OK(moe::launch_permute(a_q, a_s, ids_c, w_c, on_in, Mc, (int)K, (int)T, expert_map,
+                                   P.num_global_experts, (int)El, P.align, pl.cap, bufA, bufAs, counts,
+                                   offsets, inv, rsrc, hist,
+                                   per_chunk_counts ? per_chunk_counts + c * El : nullptr, s));
+        HIP_OK(moe::launch_grouped_gemm(bufA, bufAs, w13, w13_s, offsets, counts, (int)El, pl.cap,
+                                        (int)(2 * N), (int)K, hy, cus, s));
+        HIP_OK(moe::launch_act_quant(hy, pl.cap, (int)N, moe::MOE_ACT_SILU_MUL_K, offsets, counts, (int)El,
+                                     bufA, bufAs, s));
+        HIP_OK(moe::launch_grouped_gemm(bufA, bufAs, w2, w2_s, offsets, counts, (int)El, pl.cap, (int)K,
+                                        (int)N, hy, cus, s));
+        HIP_OK(moe::launch_unpermute(hy, pl.cap, inv, w_c, Mc, (int)K, (int)T, on_in, out + t0 * K, s));
+    }
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// moe_device.hpp -- device-side numerics and helpers shared by the gfx950
+// kernels of the MoE expert pipeline (bf16 rounding, OCP E4M3FN encoding,
+// the pinned exp used by SiLU, wave helpers).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kGroup = 128;      // quantisation group / weight block edge
+constexpr int kWave = 64;
+constexpr int kMaxLocalExperts = 1024;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float v) {
+    uint32_t u = __float_as_uint(v);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Four fp32 -> four OCP E4M3FN codes packed little-endian in one dword.
+// The hardware conversion rounds to nearest even; saturation to +-448 is
+// done by the clamp, and NaN maps to 0x7F with its sign.
+__device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, float d) {
+    float ca = __builtin_fminf(__builtin_fmaxf(a, -448.0f), 448.0f);
+    float cb = __builtin_fminf(__builtin_fmaxf(b, -448.0f), 448.0f);
+    float cc = __builtin_fminf(__builtin_fmaxf(c, -448.0f), 448.0f);
+    float cd = __builtin_fminf(__builtin_fmaxf(d, -448.0f), 448.0f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(cc, cd, w, true);
+    uint32_t r = static_cast<uint32_t>(w);
+    // NaN lanes: 0x7F | sign
+    if (a != a) r = (r & 0xffffff00u) | ((__float_as_uint(a) >> 24) & 0x80u) | 0x7fu;
+    if (b != b) r = (r & 0xffff00ffu) | ((((__float_as_uint(b) >> 24) & 0x80u) | 0x7fu) << 8);
+    if (c != c) r = (r & 0xff00ffffu) | ((((__float_as_uint(c) >> 24) & 0x80u) | 0x7fu) << 16);
+    if (d != d) r = (r & 0x00ffffffu) | ((((__float_as_uint(d) >> 24) & 0x80u) | 0x7fu) << 24);
+    return r;
+}
+
+// exp for SiLU, fixed operation by operation so that it is reproducible:
+// clamp to [-86, 88]; n = nearest-even(x / ln2); r = x - n*ln2 with ln2 in
+// two parts (Cody-Waite); Horner over the Taylor coefficients 1/k!, k<=7;
+// result p * 2^n.
+__device__ __forceinline__ float exp_pinned(float x) {
+    const float kLog2e = __uint_as_float(0x3fb8aa3bu);
+    const float kLn2Hi = __uint_as_float(0x3f317200u);
+    const float kLn2Lo = __uint_as_float(0x35bfbe8eu);
+    float xc = __builtin_fminf(__builtin_fmaxf(x, -86.0f), 88.0f);
+    float n = __builtin_rintf(xc * kLog2e);
+    float r = __builtin_fmaf(-n, kLn2Hi, xc);
+    r = __builtin_fmaf(-n, kLn2Lo, r);
+    float p = __uint_as_float(0x39500d01u);                 // 1/7!
+    p = __builtin_fmaf(p, r, __uint_as_float(0x3ab60b61u)); // 1/6!
+    p = __builtin_fmaf(p, r, __uint_as_float(0x3c088889u)); // 1/5!
+    p = __builtin_fmaf(p, r, __uint_as_float(0x3d2aaaabu)); // 1/4!
+    p = __builtin_fmaf(p, r, __uint_as_float(0x3e2aaaabu)); // 1/3!
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    return __builtin_amdgcn_ldexpf(p, static_cast<int>(n));
+}
+
+__device__ __forceinline__ int local_expert(int id, const int32_t* __restrict__ emap, int Eg, int El) {
+    if (id < 0 || id >= Eg) return -1;
+    int e = emap ? emap[id] : id;
+    return (e >= 0 && e < El) ? e : -1;
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const int lane = threadIdx.x & (kWave - 1);
+    return lane ? (~0ull >> (64 - lane)) : 0ull;
+}
+
+}  // namespace moe

@@ -1,0 +1,51 @@
+// moe_internal.hpp -- host-side launchers of the gfx950 kernels (internal to
+// libmoe_hip.so; the public surface is include/moe.h).  Launchers assume
+// arguments were validated by the C-ABI layer and return hipGetLastError().
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int MOE_ACT_IDENTITY_K = 0;  // same values as MOE_ACT_* in moe.h
+constexpr int MOE_ACT_SILU_MUL_K = 1;
+
+// ---- count / permute -------------------------------------------------------
+// Tokens handled by one permute block: a token's topk pairs never straddle
+// blocks and a block holds at most 256 pairs.
+inline int permute_tokens_per_block(int topk) { return topk >= 256 ? 1 : 256 / topk; }
+inline int64_t permute_num_blocks(int64_t Mc, int topk) {
+    int tb = permute_tokens_per_block(topk);
+    return (Mc + tb - 1) / tb;
+}
+
+hipError_t launch_count(const int32_t* ids, int64_t num_pairs, const int32_t* emap, int Eg, int El,
+                        int32_t* counts, int32_t* invalid, hipStream_t s);
+
+// hist: [nblk, El] int32 scratch.  Writes counts, offsets, row_src padding,
+// and per-block row bases into hist.
+hipError_t launch_permute(const uint8_t* a_q, const float* a_s, const int32_t* ids,
+                          const float* topk_w, int apply_on_input, int64_t Mc, int K, int topk,
+                          const int32_t* emap, int Eg, int El, int align, int64_t cap_rows,
+                          uint8_t* a_perm, float* a_perm_s, int32_t* counts, int32_t* offsets,
+                          int32_t* inv_perm, int32_t* row_src, int32_t* hist,
+                          int32_t* counts_copy, hipStream_t s);
+
+// ---- activation quantisation ------------------------------------------------
+hipError_t launch_act_quant(const uint16_t* in, int64_t rows, int n, int mode,
+                            const int32_t* offsets, const int32_t* counts, int El, uint8_t* q,
+                            float* q_s, hipStream_t s);
+
+// ---- grouped GEMM ------------------------------------------------------------
+hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_s, const uint8_t* w,
+                               const float* w_s, const int32_t* offsets, const int32_t* counts,
+                               int El, int64_t cap_rows, int n_out, int k_in, uint16_t* out,
+                               int num_cus, hipStream_t s);
+
+// ---- unpermute ----------------------------------------------------------------
+hipError_t launch_unpermute(const uint16_t* y, int64_t y_rows, const int32_t* inv_perm,
+                            const float* topk_w, int64_t Mc, int K, int topk, int apply_on_input, uint16_t* out,
+                            hipStream_t s);
+
+}  // namespace moe
