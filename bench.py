@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 import unpermute_count_expert_amd as moe  # noqa: E402
 from unpermute_count_expert_amd import generators as gen  # noqa: E402
+from unpermute_count_expert_amd.pipeline import StepBuffers, step_ops  # noqa: E402
 
 METRIC = "MoE layer tokens/s; grouped-GEMM fp8 TFLOP/s; scatter/gather HBM GB/s"
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
@@ -72,42 +73,22 @@ def timed(fn, iters, stream):
     return start.elapsed_time(end) / iters  # ms
 
 
-def per_op_times(inp, d, layer, on_input, iters, stream):
-    """Times each op of the pipeline through its own C-ABI entry point, on the
-    same buffers the layer uses, with HIP events on the launching stream."""
-    cfg = inp.cfg
-    M, K, N, T, El = cfg.M, cfg.K, cfg.N, cfg.topk, cfg.El
-    cap = moe.moe_max_rows(M, T, El, cfg.align)
-    u8, f32, i32, bf = torch.uint8, torch.float32, torch.int32, torch.int16
-    e = lambda shape, dt: torch.empty(shape, dtype=dt, device="cuda:0")
-    a_q, a_s = e((M, K), u8), e((M, K // 128), f32)
-    a_perm, a_perm_s = e((cap, K), u8), e((cap, K // 128), f32)
-    counts, offs = e((El,), i32), e((El + 1,), i32)
-    inv, rsrc = e((M, T), i32), e((cap,), i32)
-    pws = e((moe.moe_permute_workspace_size(M, T, El),), u8)
-    h = e((cap, 2 * N), bf)
-    act_q, act_s = e((cap, N), u8), e((cap, N // 128), f32)
-    y = e((cap, K), bf)
-    out = e((M, K), bf)
-    cnt2 = e((El,), i32)
-    emap = d["emap"]
-    ops = {
-        "input_quant": lambda: moe.moe_act_quant(d["x"], K, moe.MOE_ACT_IDENTITY, a_q, a_s),
-        "count": lambda: moe.moe_count(d["ids"], emap, cfg.Eg, El, cnt2),
-        "permute": lambda: moe.moe_permute(a_q, a_s, d["ids"], d["w"], on_input, emap, cfg.Eg, El, cfg.align,
-                                           cap, a_perm, a_perm_s, counts, offs, inv, rsrc, pws),
-        "gemm_w13": lambda: moe.moe_grouped_gemm_fp8(a_perm, a_perm_s, layer.w13, layer.w13_s, offs, counts, h),
-        "silu_mul_quant": lambda: moe.moe_act_quant(h, N, moe.MOE_ACT_SILU_MUL, act_q, act_s, offs, counts, El),
-        "gemm_w2": lambda: moe.moe_grouped_gemm_fp8(act_q, act_s, layer.w2, layer.w2_s, offs, counts, y),
-        "unpermute": lambda: moe.moe_unpermute_weight_reduce(y, inv, d["w"], on_input, out),
-    }
-    # one pass in order to fill every buffer, then each op timed on its own
-    for fn in ops.values():
-        fn()
+def per_op_times(layer, d, on_input, iters, stream, only=None):
+    """Times each op of the pipeline through its own C-ABI entry point (the
+    kernels the fused call runs), with HIP events on the launching stream.
+    With `only`, the ops before it run once to fill its inputs and only it is
+    timed (so a profiler sees no other launch of the same kernel)."""
+    b = StepBuffers(layer, d["x"].shape[0], d["ids"].shape[1])
+    ops = step_ops(layer, d["x"], d["ids"], d["w"], on_input, b)
+    names = list(ops)
+    if only is not None:
+        names = names[:names.index(only) + 1]
+    for name in names:          # fill every buffer once, in order
+        ops[name]()
     torch.cuda.synchronize()
-    res = {name: timed(fn, iters, stream) for name, fn in ops.items()}
-    c = counts.cpu().numpy()
-    return res, c, int(offs[-1].item())
+    timed_names = [only] if only is not None else names
+    res = {name: timed(ops[name], iters, stream) for name in timed_names}
+    return res, b.counts.cpu().numpy(), int(b.offsets[-1].item())
 
 
 def algorithmic(cfg, counts: np.ndarray, R: int):
@@ -130,7 +111,7 @@ def algorithmic(cfg, counts: np.ndarray, R: int):
 
 def cpu_baseline(inp, on_input, target_s=15.0):
     """The oracle (plain C, OpenMP over rows) on the first S tokens of the
-    same workload; S is grown from a 16-token probe to about target_s of work."""
+    same workload; S grows geometrically until one run takes about target_s."""
     import oracle
     cfg = inp.cfg
 
@@ -140,12 +121,27 @@ def cpu_baseline(inp, on_input, target_s=15.0):
                                inp.w13_s, inp.w2, inp.w2_s, cfg.Eg, apply_on_input=on_input, align=cfg.align)
         return time.perf_counter() - t0
 
-    probe = 16
-    tp = run(probe)
-    S = int(min(cfg.M, max(probe, probe * target_s / max(tp, 1e-3))))
-    ts = run(S)
-    return {"value": S / ts, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"first {S} of {cfg.M} tokens of the same layer (all expert weights), {ts:.1f} s"}
+    S = 32
+    while True:
+        ts = run(S)
+        if ts >= 0.5 * target_s or S >= cfg.M:
+            break
+        S = int(min(cfg.M, max(2 * S, S * target_s / max(ts, 1e-3))))
+    return {"value": round(S / ts, 2), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {S} of {cfg.M} tokens of the same layer (all {cfg.El} experts' weights), "
+                      f"{ts:.1f} s"}
+
+
+def copy_calibration(iters):
+    """A plain device copy of known size (256 MiB read + 256 MiB written),
+    for scaling HBM byte counters."""
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    stream = torch.cuda.current_stream()
+    ms = timed(lambda: b.copy_(a), iters, stream)
+    print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n, "ms": round(ms, 5),
+                      "GB/s": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def main():
@@ -157,12 +153,18 @@ def main():
     ap.add_argument("--op-iters", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--profile-op", default=None,
+                    help="time only this op (input_quant, count, permute, gemm_w13, silu_mul_quant, "
+                         "gemm_w2, unpermute) or 'copy'; for profiler runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the multi-GPU expert-parallel path is not part of it)", file=sys.stderr)
         sys.exit(2)
 
+    if args.profile_op == "copy":
+        copy_calibration(args.op_iters)
+        return
     cfg = gen.CONFIGS[args.config]
     on_input = cfg.apply_router_weight_on_input
     t_gen = time.perf_counter()
@@ -177,6 +179,12 @@ def main():
     def step():
         layer.forward(d["x"], d["ids"], d["w"], chunk_size=cfg.chunk_size, apply_on_input=on_input, out=out)
 
+    if args.profile_op is not None:
+        ops, counts, R = per_op_times(layer, d, on_input, args.op_iters, stream, only=args.profile_op)
+        print(json.dumps({"mode": "profile_op", "op": args.profile_op, "iters": args.op_iters,
+                          "ms": round(ops[args.profile_op], 5), "config": cfg.name}), flush=True)
+        return
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -185,7 +193,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    ops, counts, R = per_op_times(inp, d, layer, on_input, args.op_iters, stream)
+    ops, counts, R = per_op_times(layer, d, on_input, args.op_iters, stream)
     P, Ene, g1f, g2f, by = algorithmic(cfg, counts, R)
     ops_out = {}
     for name, t in ops.items():

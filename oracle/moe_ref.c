@@ -128,12 +128,16 @@ float moe_ref_exp_spec(float x) {
     return ldexpf(p, (int)n);
 }
 
-/* One 1x128 group: amax in fp32 (NaN ignored), d = max(amax, 1e-10),
+/* One 1x128 group: amax = the largest non-NaN |v| (quiet and signalling
+ * NaNs alike are skipped), d = max(amax, 1e-10),
  * scale s = d/448, codes e4m3(v * (448/d)).  Reading: fp8 per-128-group
  * activation scales as in PR #20903 (Optimizations, block 128). */
 void moe_ref_quant_group(const float* v, uint8_t* q, float* s) {
     float amax = 0.0f;
-    for (int i = 0; i < GROUP; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    for (int i = 0; i < GROUP; ++i) {
+        float a = fabsf(v[i]);
+        if (a > amax) amax = a;   /* false for NaN */
+    }
     float d = fmaxf(amax, 1e-10f);
     float scale = d / 448.0f;
     float inv = 448.0f / d;

@@ -57,3 +57,33 @@ def assert_bf16_close(got: np.ndarray, ref: np.ndarray, what=""):
 def valid_rows(offsets: np.ndarray, counts: np.ndarray) -> np.ndarray:
     return np.concatenate([np.arange(offsets[e], offsets[e] + counts[e]) for e in range(len(counts))]
                           + [np.zeros(0, np.int64)]).astype(np.int64)
+
+
+def bf16_ulp(v: np.ndarray) -> np.ndarray:
+    """bf16 spacing at |v| (as float64)."""
+    a = np.abs(np.asarray(v, np.float64)).astype(np.float32)
+    return np.spacing(a).astype(np.float64) * 65536.0
+
+
+def gemm_tolerance(ref_bits: np.ndarray, absterm_bits: np.ndarray) -> np.ndarray:
+    """Allowed |gpu - ref| for a block-scaled fp8 GEMM output.
+
+    The GPU sums each 128-group in the MFMA and folds 16-ish groups with fp32
+    FMAs: its error is at most ~(128 + groups + 2) * 2^-24 times the sum of
+    the absolute terms T = sum_g s_g sum_k |a_k w_k| (bounded here by 2^-16 T),
+    plus the two bf16 roundings.  Where the terms do not cancel this is far
+    inside the benchmark spec's tolerance 1e-3 + 1e-2|ref|, which is always allowed."""
+    ref = bf16_f64(ref_bits)
+    T = bf16_f64(absterm_bits) * 1.01
+    return np.maximum(ATOL + RTOL * np.abs(ref), 2.0 ** -16 * T + bf16_ulp(np.abs(ref) + 2.0 ** -16 * T))
+
+
+def assert_gemm_close(got_bits, ref_bits, absterm_bits, what=""):
+    g, r = bf16_f64(got_bits), bf16_f64(ref_bits)
+    tol = gemm_tolerance(ref_bits, absterm_bits)
+    bad = ~(np.abs(g - r) <= tol)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        i0 = tuple(idx[0])
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside the GEMM bound; first {idx.tolist()} "
+                             f"got {g[i0]} ref {r[i0]} tol {tol[i0]}")

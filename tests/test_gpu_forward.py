@@ -1,10 +1,24 @@
-"""Whole-layer parity: moe_forward_chunked on the GPU against the oracle.
+"""Whole-layer parity: the GPU layer against the oracle, op by op and end to end.
 
-Small layers are compared in full; the full-size layers (prefill 4096 and
-large batch 16384 tokens) on sampled tokens, which the oracle computes on
-their own (a token's output depends only on its own row, ids and weights).
-Per-chunk counts are compared bit for bit; chunked GPU runs are compared
-with the unchunked GPU run.
+The layer is run on the GPU as its chain of C-ABI ops (the kernels
+moe_forward_chunked runs, in the same order), so every intermediate can be
+checked against the oracle fed with the GPU's own input to that op:
+
+* count, offsets, inv_perm, row_src, permuted rows/scales: bit-exact;
+* h = GEMM(w13): within the GEMM bound of the oracle on the same a_perm;
+* act_q/act_s: bit-exact against the oracle's SiLU-mul requant of the GPU h
+  (the quantisation decision is taken on the identical bf16 h);
+* y = GEMM(w2): within the GEMM bound of the oracle on the GPU act_q;
+* out: bit-exact against the oracle's unpermute of the GPU y;
+* moe_forward_chunked: bit-exact against the chain, chunked == unchunked;
+* end to end against the all-oracle layer: within 1e-3 + 1e-2|ref| for every
+  token whose act codes the GPU and the oracle decide alike; a token whose
+  h differs from the exact sum by one bf16 rounding can land a group amax or
+  a code on the other side of a rounding boundary, and only such tokens may
+  exceed it (they must stay within 1e-2 + 5e-2|ref|).
+
+Full-size layers (4096 and 16384 tokens) are checked on sampled rows/tokens,
+which the oracle computes on their own (rows are independent).
 """
 import numpy as np
 import pytest
@@ -13,25 +27,25 @@ import torch
 import oracle
 import unpermute_count_expert_amd as moe
 from unpermute_count_expert_amd import generators as gen
-from tests.gpu_helpers import announce, assert_bf16_close, dev, filled, host
+from unpermute_count_expert_amd.pipeline import run_steps
+from tests.gpu_helpers import (ATOL, RTOL, announce, assert_gemm_close, bf16_f64, dev, filled, host,
+                               valid_rows)
 
 pytestmark = pytest.mark.gpu
-
 
 _INPUTS = {}
 
 
-def _inputs(key):
-    """make_inputs for a named config; the weight-sharing on/off variants of
-    one seed reuse the same arrays."""
-    cfg = gen.CONFIGS[key]
-    k = (cfg.seed, cfg.M, cfg.routing)
+def _inputs(cfg):
+    """make_inputs, reusing the arrays of the last config with the same seed
+    (the on-input variants share the off variants' inputs)."""
+    k = (cfg.seed, cfg.M, cfg.K, cfg.N, cfg.El, cfg.topk, cfg.routing)
     if k not in _INPUTS:
         _INPUTS.clear()
         _INPUTS[k] = gen.make_inputs(cfg)
-    inp = _INPUTS[k]
-    return gen.LayerInputs(cfg, inp.x, inp.topk_ids, inp.topk_weights, inp.expert_map, inp.w13,
-                           inp.w13_s, inp.w2, inp.w2_s, inp.extra)
+    i = _INPUTS[k]
+    return gen.LayerInputs(cfg, i.x, i.topk_ids, i.topk_weights, i.expert_map, i.w13, i.w13_s, i.w2,
+                           i.w2_s, i.extra)
 
 
 def _layer(inp):
@@ -40,95 +54,136 @@ def _layer(inp):
                         inp.cfg.align)
 
 
-def _gpu_forward(layer, inp, chunk_size, on_input, want_counts=False, x=None, ids=None, w=None):
-    x = dev(inp.x) if x is None else x
-    ids = dev(inp.topk_ids) if ids is None else ids
-    w = dev(inp.topk_weights) if w is None else w
-    M = x.shape[0]
+def _forward(layer, d, M, chunk_size, on_input, want_counts=False):
     cs = M if chunk_size <= 0 or chunk_size >= M else chunk_size
-    nch = -(-M // cs)
-    pcc = filled((nch, layer.El), torch.int32, -5) if want_counts else None
-    out = layer.forward(x, ids, w, chunk_size=chunk_size, apply_on_input=on_input, per_chunk_counts=pcc)
+    pcc = filled((-(-M // cs), layer.El), torch.int32, -5) if want_counts else None
+    out = layer.forward(d["x"], d["ids"], d["w"], chunk_size=chunk_size, apply_on_input=on_input,
+                        per_chunk_counts=pcc)
     return host(out, bf16=True), (host(pcc) if want_counts else None)
 
 
-def _oracle_forward(inp, chunk_size, on_input, rows=None):
-    x, ids, w = inp.x, inp.topk_ids, inp.topk_weights
-    if rows is not None:
-        x, ids, w = x[rows], ids[rows], w[rows]
-    return oracle.forward_chunked(x, ids, w, inp.expert_map, inp.w13, inp.w13_s, inp.w2, inp.w2_s,
-                                  inp.cfg.Eg, apply_on_input=on_input, chunk_size=chunk_size,
-                                  align=inp.cfg.align, want_counts=True)
+def _sample(M, rng, n):
+    if M <= n:
+        return np.arange(M)
+    return np.unique(np.concatenate([[0, 1, M // 2, M - 2, M - 1], rng.choice(M, n, replace=False)]))
 
 
-SMALL = [
+def check_layer(cfg, on_input, n_sample_rows=64, n_sample_tokens=48):
+    inp = _inputs(cfg)
+    M, K, N, T, El = cfg.M, cfg.K, cfg.N, cfg.topk, cfg.El
+    layer = _layer(inp)
+    d = dict(x=dev(inp.x), ids=dev(inp.topk_ids), w=dev(inp.topk_weights))
+    b = run_steps(layer, d["x"], d["ids"], d["w"], on_input)
+    g = {k: host(getattr(b, k)) for k in ("a_q", "a_s", "a_perm", "a_perm_s", "counts", "offsets", "inv_perm",
+                                          "row_src", "act_q", "act_s", "count_only")}
+    g["h"], g["y"], g["out"] = host(b.h, bf16=True), host(b.y, bf16=True), host(b.out, bf16=True)
+    rng = np.random.default_rng(cfg.seed + 1000 * on_input)
+
+    # -- input quant and routing bookkeeping: bit-exact on everything
+    a_q, a_s = oracle.act_quant_identity(inp.x)
+    np.testing.assert_array_equal(g["a_q"], a_q)
+    np.testing.assert_array_equal(g["a_s"], a_s)
+    counts, _ = oracle.count(inp.topk_ids, inp.expert_map, cfg.Eg, El)
+    np.testing.assert_array_equal(g["count_only"], counts)
+    r = oracle.permute(a_q, a_s, inp.topk_ids, inp.topk_weights, on_input, inp.expert_map, cfg.Eg, El,
+                       cfg.align)
+    for k in ("counts", "expert_offsets", "inv_perm", "row_src"):
+        np.testing.assert_array_equal(g["offsets" if k == "expert_offsets" else k], r[k], err_msg=k)
+    rows = valid_rows(r["expert_offsets"], r["counts"])
+    np.testing.assert_array_equal(g["a_perm"][rows], r["a_perm"][rows])
+    np.testing.assert_array_equal(g["a_perm_s"][rows], r["a_perm_s"][rows])
+    row_exp = np.repeat(np.arange(El), r["counts"]).astype(np.int32)   # expert of each valid row
+
+    # -- GEMM w13 on sampled valid rows
+    pick = _sample(len(rows), rng, n_sample_rows)
+    sr, se = rows[pick], row_exp[pick]
+    h_ref = oracle.gemm_rows(g["a_perm"][sr], g["a_perm_s"][sr], se, inp.w13, inp.w13_s)
+    h_abs = oracle.gemm_rows(g["a_perm"][sr] & 0x7F, g["a_perm_s"][sr], se, inp.w13 & 0x7F, inp.w13_s)
+    assert_gemm_close(g["h"][sr], h_ref, h_abs, f"{cfg.name} h")
+
+    # -- SiLU-mul requant of the GPU's own h: bit-exact on every valid row
+    q, s = oracle.silu_mul_quant(g["h"][rows])
+    np.testing.assert_array_equal(g["act_q"][rows], q)
+    np.testing.assert_array_equal(g["act_s"][rows], s)
+
+    # -- GEMM w2 on the GPU's act_q, sampled rows
+    y_ref = oracle.gemm_rows(g["act_q"][sr], g["act_s"][sr], se, inp.w2, inp.w2_s)
+    y_abs = oracle.gemm_rows(g["act_q"][sr] & 0x7F, g["act_s"][sr], se, inp.w2 & 0x7F, inp.w2_s)
+    assert_gemm_close(g["y"][sr], y_ref, y_abs, f"{cfg.name} y")
+
+    # -- unpermute of the GPU's y: bit-exact
+    np.testing.assert_array_equal(g["out"], oracle.unpermute(g["y"], g["inv_perm"], inp.topk_weights, on_input))
+
+    # -- the fused entry point computes the same bits; chunking changes nothing
+    full, pcc = _forward(layer, d, M, 0, on_input, want_counts=True)
+    np.testing.assert_array_equal(full, g["out"])
+    np.testing.assert_array_equal(pcc[0], counts)
+    if cfg.chunk_size and cfg.chunk_size < M:
+        chunked, pcc = _forward(layer, d, M, cfg.chunk_size, on_input, want_counts=True)
+        np.testing.assert_array_equal(chunked, full)
+        cs = cfg.chunk_size
+        for c in range(pcc.shape[0]):
+            np.testing.assert_array_equal(
+                pcc[c], oracle.count(inp.topk_ids[c * cs:(c + 1) * cs], inp.expert_map, cfg.Eg, El)[0])
+
+    # -- end to end against the all-oracle layer on sampled tokens
+    toks = _sample(M, rng, n_sample_tokens)
+    ref = bf16_f64(oracle.forward_chunked(inp.x[toks], inp.topk_ids[toks], inp.topk_weights[toks],
+                                          inp.expert_map, inp.w13, inp.w13_s, inp.w2, inp.w2_s, cfg.Eg,
+                                          apply_on_input=on_input, align=cfg.align))
+    got = bf16_f64(g["out"][toks])
+    # tokens where the oracle's own h leads to different act codes than the GPU's h
+    flipped = np.zeros(len(toks), bool)
+    for i, t in enumerate(toks):
+        trows = g["inv_perm"][t][g["inv_perm"][t] >= 0].astype(np.int64)
+        if len(trows) == 0:
+            continue
+        ex = np.searchsorted(r["expert_offsets"], trows, side="right").astype(np.int32) - 1
+        h_or = oracle.gemm_rows(g["a_perm"][trows], g["a_perm_s"][trows], ex, inp.w13, inp.w13_s)
+        q_or, s_or = oracle.silu_mul_quant(h_or)
+        flipped[i] = not (np.array_equal(q_or, g["act_q"][trows]) and np.array_equal(s_or, g["act_s"][trows]))
+    err = np.abs(got - ref)
+    tight = err <= ATOL + RTOL * np.abs(ref)
+    loose = err <= 1e-2 + 5e-2 * np.abs(ref)
+    bad_tight = ~tight.all(axis=1) & ~flipped
+    assert not bad_tight.any(), (f"{cfg.name}: tokens {toks[bad_tight][:5].tolist()} exceed 1e-3 + 1e-2|ref| "
+                                 f"without an act-code flip; max err {err[bad_tight].max()}")
+    assert loose.all(), f"{cfg.name}: max err {err.max()} beyond 1e-2 + 5e-2|ref|"
+    print(f"{cfg.name} on_input={on_input}: {flipped.sum()} of {len(toks)} sampled tokens have an act-code "
+          f"flip; max end-to-end err {err.max():.3g}", flush=True)
+    assert flipped.mean() <= 0.25
+
+
+CASES = [
     ("C1", gen.CONFIGS["C1"], 0),
     ("C1_on", gen.CONFIGS["C1"], 1),
-    ("small_chunked", gen.small_config(M=300, K=512, N=256, Eg=32, El=16, topk=4, chunk_size=64,
-                                       routing="zipf", seed=21, ep_rank_of_2=1), 0),
+    ("small_chunked_zipf", gen.small_config(M=300, K=512, N=256, Eg=32, El=16, topk=4, chunk_size=64,
+                                            routing="zipf", seed=21, ep_rank_of_2=1), 0),
     ("small_align16", gen.small_config(M=150, K=256, N=384, Eg=16, El=16, topk=3, chunk_size=0,
                                        routing="softmax", seed=22, align=16), 1),
     ("C2_profiling", gen.CONFIGS["C2"], 0),
     ("C4b_tail_130_by_128", gen.CONFIGS["C4b"], 0),
+    ("C3_prefill", gen.CONFIGS["C3"], 0),
+    ("C4_chunk_stress", gen.CONFIGS["C4"], 0),
+    ("C5u", gen.CONFIGS["C5u"], 0),
+    ("C5u_on", gen.CONFIGS["C5u_on"], 1),
+    ("C5h", gen.CONFIGS["C5h"], 0),
+    ("C5h_on", gen.CONFIGS["C5h_on"], 1),
 ]
 
 
-@pytest.mark.parametrize("name,cfg,on_input", SMALL, ids=[s[0] for s in SMALL])
-def test_forward_small_full_parity(name, cfg, on_input):
-    announce("forward", name, on_input)
-    inp = gen.make_inputs(cfg)
-    layer = _layer(inp)
-    got, pcc = _gpu_forward(layer, inp, cfg.chunk_size, on_input, want_counts=True)
-    ref, pcc_ref = _oracle_forward(inp, cfg.chunk_size, on_input)
-    np.testing.assert_array_equal(pcc, pcc_ref)
-    assert_bf16_close(got, ref, name)
-    if cfg.chunk_size and cfg.chunk_size < cfg.M:
-        whole, _ = _gpu_forward(layer, inp, 0, on_input)
-        np.testing.assert_array_equal(got, whole)   # rows are independent: no split-K
+@pytest.mark.parametrize("name,cfg,on_input", CASES, ids=[c[0] for c in CASES])
+def test_layer_parity(name, cfg, on_input):
+    announce("layer", name, on_input)
+    check_layer(cfg, on_input)
 
 
-def _sample_rows(M, rng, n=48):
-    picks = np.unique(np.concatenate([[0, 1, M // 2, M - 2, M - 1], rng.choice(M, n, replace=False)]))
-    return picks.astype(np.int64)
-
-
-LARGE = [("C3_prefill", "C3", 0), ("C5u", "C5u", 0), ("C5u_on", "C5u_on", 1), ("C5h", "C5h", 0),
-         ("C5h_on", "C5h_on", 1)]
-
-
-@pytest.mark.parametrize("name,key,on_input", LARGE, ids=[s[0] for s in LARGE])
-def test_forward_large_sampled_parity(name, key, on_input):
-    announce("forward sampled", name)
-    cfg = gen.CONFIGS[key]
-    inp = _inputs(key)
-    layer = _layer(inp)
-    got, pcc = _gpu_forward(layer, inp, 0, on_input, want_counts=True)
-    counts_ref, _ = oracle.count(inp.topk_ids, inp.expert_map, cfg.Eg, cfg.El)
-    np.testing.assert_array_equal(pcc[0], counts_ref)
-    rows = _sample_rows(cfg.M, np.random.default_rng(cfg.seed))
-    ref, _ = _oracle_forward(inp, 0, on_input, rows)
-    assert_bf16_close(got[rows], ref, name)
-
-
-def test_forward_chunk_stress_zipf():
-    """8192 tokens in chunks of 64 with Zipf routing over 64 local of 128
-    experts: per-chunk counts bit for bit (including zero-count experts),
-    sampled tokens against the oracle, and chunked == unchunked on the GPU."""
-    announce("forward chunk stress C4")
+def test_chunk_stress_has_empty_experts():
     cfg = gen.CONFIGS["C4"]
-    inp = gen.make_inputs(cfg)
-    layer = _layer(inp)
-    got, pcc = _gpu_forward(layer, inp, cfg.chunk_size, 0, want_counts=True)
-    nch = cfg.M // cfg.chunk_size
-    for c in range(nch):
-        ids_c = inp.topk_ids[c * 64:(c + 1) * 64]
-        np.testing.assert_array_equal(pcc[c], oracle.count(ids_c, inp.expert_map, cfg.Eg, cfg.El)[0])
-    assert (pcc == 0).sum() > 0, "some local expert must get no tokens in some chunk"
-    rows = _sample_rows(cfg.M, np.random.default_rng(4), 40)
-    ref, _ = _oracle_forward(inp, 0, 0, rows)
-    assert_bf16_close(got[rows], ref, "C4")
-    whole, _ = _gpu_forward(layer, inp, 0, 0)
-    np.testing.assert_array_equal(got, whole)
+    inp = _inputs(cfg)
+    per = np.stack([oracle.count(inp.topk_ids[c * 64:(c + 1) * 64], inp.expert_map, cfg.Eg, cfg.El)[0]
+                    for c in range(cfg.M // 64)])
+    assert (per == 0).sum() > 0
 
 
 def test_forward_all_pairs_nonlocal_gives_zero():
@@ -136,9 +191,10 @@ def test_forward_all_pairs_nonlocal_gives_zero():
     cfg = gen.small_config(M=70, K=256, N=128, Eg=16, El=8, topk=2, routing="softmax", seed=3,
                            ep_rank_of_2=1)
     inp = gen.make_inputs(cfg)
-    ids = np.where(inp.topk_ids >= 8, inp.topk_ids - 8, inp.topk_ids).astype(np.int32)  # all < 8: remote
-    got, _ = _gpu_forward(_layer(inp), inp, 0, 0, ids=dev(ids))
-    assert np.all(got == 0)
+    ids = np.where(inp.topk_ids >= 8, inp.topk_ids - 8, inp.topk_ids).astype(np.int32)  # all remote
+    layer = _layer(inp)
+    out = layer.forward(dev(inp.x), dev(ids), dev(inp.topk_weights))
+    assert np.all(host(out, bf16=True) == 0)
 
 
 def test_forward_m1_and_empty():
@@ -146,9 +202,11 @@ def test_forward_m1_and_empty():
     cfg = gen.small_config(M=1, K=128, N=128, Eg=4, El=4, topk=1, routing="softmax", seed=9)
     inp = gen.make_inputs(cfg)
     layer = _layer(inp)
-    got, _ = _gpu_forward(layer, inp, 1, 0)
-    ref, _ = _oracle_forward(inp, 1, 0)
-    assert_bf16_close(got, ref, "M=1")
+    d = dict(x=dev(inp.x), ids=dev(inp.topk_ids), w=dev(inp.topk_weights))
+    got, _ = _forward(layer, d, 1, 1, 0)
+    ref = oracle.forward_chunked(inp.x, inp.topk_ids, inp.topk_weights, None, inp.w13, inp.w13_s, inp.w2,
+                                 inp.w2_s, cfg.Eg)
+    assert np.all(np.abs(bf16_f64(got) - bf16_f64(ref)) <= 1e-2 + 5e-2 * np.abs(bf16_f64(ref)))
     out = layer.forward(dev(inp.x[:0]), dev(inp.topk_ids[:0]), dev(inp.topk_weights[:0]))
     assert out.shape == (0, 128)
 
@@ -158,6 +216,7 @@ def test_forward_is_deterministic():
     cfg = gen.small_config(M=512, K=512, N=256, Eg=32, El=32, topk=4, routing="zipf", seed=5)
     inp = gen.make_inputs(cfg)
     layer = _layer(inp)
-    a, _ = _gpu_forward(layer, inp, 0, 0)
-    b, _ = _gpu_forward(layer, inp, 0, 0)
+    d = dict(x=dev(inp.x), ids=dev(inp.topk_ids), w=dev(inp.topk_weights))
+    a, _ = _forward(layer, d, cfg.M, 0, 0)
+    b, _ = _forward(layer, d, cfg.M, 0, 0)
     np.testing.assert_array_equal(a, b)

@@ -260,3 +260,19 @@ def test_silu_mul_quant_rows_masked_by_offsets():
     np.testing.assert_array_equal(q[valid], qa[valid])
     np.testing.assert_array_equal(s[valid], sa[valid])
     assert np.all(q[~valid] == 0) and np.all(s[~valid] == 0)
+
+
+def test_quant_group_skips_quiet_and_signalling_nans():
+    v = np.linspace(-3, 3, 128).astype(np.float32)
+    bits = v.view(np.uint32).copy()
+    bits[5] = 0x7FC00000   # quiet NaN
+    bits[9] = 0x7F800001   # signalling NaN
+    bits[77] = 0xFFA00000  # negative signalling NaN
+    w = bits.view(np.float32)
+    q, s = oracle.quant_group(w)
+    finite = np.ones(128, bool)
+    finite[[5, 9, 77]] = False
+    assert s == np.float32(np.abs(v[finite]).max()) / np.float32(448)
+    assert q[5] == 0x7F and q[9] == 0x7F and q[77] == 0xFF
+    q2, _ = oracle.quant_group(np.where(finite, v, 0).astype(np.float32))
+    np.testing.assert_array_equal(q[finite], q2[finite])

@@ -79,12 +79,20 @@ __global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restri
                 x.v[i] = bf16_to_f32(f32_to_bf16(prod));
             }
         }
+        // largest non-NaN magnitude: a compare-select skips quiet and
+        // signalling NaNs alike (v_max_f32 would turn a signalling NaN
+        // into NaN)
         float amax = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x.v[i]));
+        for (int i = 0; i < 8; ++i) {
+            const float a = __builtin_fabsf(x.v[i]);
+            amax = a > amax ? a : amax;
+        }
 #pragma unroll
-        for (int d = kLanesPerGroup / 2; d >= 1; d >>= 1)
-            amax = __builtin_fmaxf(amax, __shfl_xor(amax, d, kWave));
+        for (int d = kLanesPerGroup / 2; d >= 1; d >>= 1) {
+            const float o = __shfl_xor(amax, d, kWave);
+            amax = o > amax ? o : amax;
+        }
         const float dd = __builtin_fmaxf(amax, 1e-10f);
         const float scale = dd / 448.0f;
         const float inv = 448.0f / dd;

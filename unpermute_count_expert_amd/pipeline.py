@@ -1,0 +1,62 @@
+"""The layer as a sequence of separate C-ABI calls, with every intermediate
+kept in its own buffer (for inspection, per-op timing and op-by-op checks).
+
+moe_forward_chunked runs the same kernels in the same order on one reused
+workspace; this form trades memory for visibility.
+"""
+from __future__ import annotations
+
+from collections import OrderedDict
+
+import torch
+
+from . import _lib
+
+
+class StepBuffers:
+    def __init__(self, layer, M: int, topk: int, device="cuda:0"):
+        K, N, El = layer.K, layer.N, layer.El
+        self.M, self.topk = M, topk
+        self.cap = _lib.moe_max_rows(M, topk, El, layer.align)
+        cap = self.cap
+        e = lambda shape, dt: torch.empty(shape, dtype=dt, device=device)
+        u8, f32, i32, b16 = torch.uint8, torch.float32, torch.int32, torch.int16
+        self.a_q, self.a_s = e((M, K), u8), e((M, K // 128), f32)
+        self.a_perm, self.a_perm_s = e((cap, K), u8), e((cap, K // 128), f32)
+        self.counts, self.offsets = e((El,), i32), e((El + 1,), i32)
+        self.inv_perm, self.row_src = e((M, topk), i32), e((cap,), i32)
+        self.permute_ws = e((_lib.moe_permute_workspace_size(M, topk, El),), u8)
+        self.h = e((cap, 2 * N), b16)
+        self.act_q, self.act_s = e((cap, N), u8), e((cap, N // 128), f32)
+        self.y = e((cap, K), b16)
+        self.out = e((M, K), b16)
+        self.count_only = e((El,), i32)
+
+
+def step_ops(layer, x, topk_ids, topk_weights, apply_on_input: int, b: StepBuffers):
+    """Ordered {name: thunk}; running them in order computes the layer into b.out."""
+    Eg, El, K, N, A = layer.Eg, layer.El, layer.K, layer.N, layer.align
+    emap = layer.expert_map
+    ops = OrderedDict()
+    ops["input_quant"] = lambda: _lib.moe_act_quant(x, K, _lib.MOE_ACT_IDENTITY, b.a_q, b.a_s)
+    ops["count"] = lambda: _lib.moe_count(topk_ids, emap, Eg, El, b.count_only)
+    ops["permute"] = lambda: _lib.moe_permute(b.a_q, b.a_s, topk_ids, topk_weights, apply_on_input, emap, Eg,
+                                              El, A, b.cap, b.a_perm, b.a_perm_s, b.counts, b.offsets,
+                                              b.inv_perm, b.row_src, b.permute_ws)
+    ops["gemm_w13"] = lambda: _lib.moe_grouped_gemm_fp8(b.a_perm, b.a_perm_s, layer.w13, layer.w13_s,
+                                                        b.offsets, b.counts, b.h)
+    ops["silu_mul_quant"] = lambda: _lib.moe_act_quant(b.h, N, _lib.MOE_ACT_SILU_MUL, b.act_q, b.act_s,
+                                                       b.offsets, b.counts, El)
+    ops["gemm_w2"] = lambda: _lib.moe_grouped_gemm_fp8(b.act_q, b.act_s, layer.w2, layer.w2_s, b.offsets,
+                                                       b.counts, b.y)
+    ops["unpermute"] = lambda: _lib.moe_unpermute_weight_reduce(b.y, b.inv_perm, topk_weights,
+                                                                apply_on_input, b.out)
+    return ops
+
+
+def run_steps(layer, x, topk_ids, topk_weights, apply_on_input: int = 0, b: StepBuffers = None):
+    if b is None:
+        b = StepBuffers(layer, x.shape[0], topk_ids.shape[1], x.device)
+    for fn in step_ops(layer, x, topk_ids, topk_weights, apply_on_input, b).values():
+        fn()
+    return b
