@@ -68,14 +68,16 @@ def bf16_ulp(v: np.ndarray) -> np.ndarray:
 def gemm_tolerance(ref_bits: np.ndarray, absterm_bits: np.ndarray) -> np.ndarray:
     """Allowed |gpu - ref| for a block-scaled fp8 GEMM output.
 
-    The GPU sums each 128-group in the MFMA and folds 16-ish groups with fp32
-    FMAs: its error is at most ~(128 + groups + 2) * 2^-24 times the sum of
-    the absolute terms T = sum_g s_g sum_k |a_k w_k| (bounded here by 2^-16 T),
-    plus the two bf16 roundings.  Where the terms do not cancel this is far
-    inside the benchmark spec's tolerance 1e-3 + 1e-2|ref|, which is always allowed."""
+    The GPU sums each 128-group inside the fp8 MFMA and folds the groups with
+    fp32 FMAs, so its error scales with the sum of the absolute terms
+    T = sum_g s_g sum_k |a_k w_k|, not with |ref|: where terms cancel, |ref|
+    can be tiny while the error is not.  The bound is 2^-14 T plus the two
+    bf16 roundings (sequential fp32 summation alone would give ~2^-17 T; on
+    random full-range e4m3 codes the MFMA's own summation was seen up to
+    ~2^-15.3 T).  The benchmark spec's tolerance 1e-3 + 1e-2|ref| is always allowed."""
     ref = bf16_f64(ref_bits)
     T = bf16_f64(absterm_bits) * 1.01
-    return np.maximum(ATOL + RTOL * np.abs(ref), 2.0 ** -16 * T + bf16_ulp(np.abs(ref) + 2.0 ** -16 * T))
+    return np.maximum(ATOL + RTOL * np.abs(ref), 2.0 ** -14 * T + bf16_ulp(np.abs(ref) + 2.0 ** -14 * T))
 
 
 def assert_gemm_close(got_bits, ref_bits, absterm_bits, what=""):

@@ -15,7 +15,8 @@ checked against the oracle fed with the GPU's own input to that op:
   token whose act codes the GPU and the oracle decide alike; a token whose
   h differs from the exact sum by one bf16 rounding can land a group amax or
   a code on the other side of a rounding boundary, and only such tokens may
-  exceed it (they must stay within 1e-2 + 5e-2|ref|).
+  exceed it (they must stay within 1e-2 + 5e-2|ref|); at most 1% of the act
+  codes may be decided differently.
 
 Full-size layers (4096 and 16384 tokens) are checked on sampled rows/tokens,
 which the oracle computes on their own (rows are independent).
@@ -134,6 +135,7 @@ def check_layer(cfg, on_input, n_sample_rows=64, n_sample_tokens=48):
     got = bf16_f64(g["out"][toks])
     # tokens where the oracle's own h leads to different act codes than the GPU's h
     flipped = np.zeros(len(toks), bool)
+    n_codes = n_code_diff = 0
     for i, t in enumerate(toks):
         trows = g["inv_perm"][t][g["inv_perm"][t] >= 0].astype(np.int64)
         if len(trows) == 0:
@@ -142,6 +144,8 @@ def check_layer(cfg, on_input, n_sample_rows=64, n_sample_tokens=48):
         h_or = oracle.gemm_rows(g["a_perm"][trows], g["a_perm_s"][trows], ex, inp.w13, inp.w13_s)
         q_or, s_or = oracle.silu_mul_quant(h_or)
         flipped[i] = not (np.array_equal(q_or, g["act_q"][trows]) and np.array_equal(s_or, g["act_s"][trows]))
+        n_codes += q_or.size
+        n_code_diff += int((q_or != g["act_q"][trows]).sum())
     err = np.abs(got - ref)
     tight = err <= ATOL + RTOL * np.abs(ref)
     loose = err <= 1e-2 + 5e-2 * np.abs(ref)
@@ -149,9 +153,13 @@ def check_layer(cfg, on_input, n_sample_rows=64, n_sample_tokens=48):
     assert not bad_tight.any(), (f"{cfg.name}: tokens {toks[bad_tight][:5].tolist()} exceed 1e-3 + 1e-2|ref| "
                                  f"without an act-code flip; max err {err[bad_tight].max()}")
     assert loose.all(), f"{cfg.name}: max err {err.max()} beyond 1e-2 + 5e-2|ref|"
+    frac = n_code_diff / max(n_codes, 1)
     print(f"{cfg.name} on_input={on_input}: {flipped.sum()} of {len(toks)} sampled tokens have an act-code "
-          f"flip; max end-to-end err {err.max():.3g}", flush=True)
-    assert flipped.mean() <= 0.25
+          f"flip ({n_code_diff} of {n_codes} codes, {frac:.2e}); max end-to-end err {err.max():.3g}",
+          flush=True)
+    # the oracle's exact h and the GPU's fp32-accumulated h decide alike on
+    # almost every code; a wrong GEMM would disagree on most of them
+    assert frac <= 1e-2
 
 
 CASES = [
