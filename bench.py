@@ -75,9 +75,12 @@ def timed(fn, iters, stream):
 
 def per_op_times(layer, d, on_input, iters, stream, only=None):
     """Times each op of the pipeline through its own C-ABI entry point (the
-    kernels the fused call runs), with HIP events on the launching stream.
-    With `only`, the ops before it run once to fill its inputs and only it is
-    timed (so a profiler sees no other launch of the same kernel)."""
+    kernels the fused call runs, plus the standalone count).  Each of `iters`
+    passes runs the whole sequence with a HIP event recorded on the launching
+    stream before every op, so every op is timed in place, between its real
+    neighbours.  With `only`, the ops before it run once to fill its inputs and
+    only it is launched repeatedly (so a profiler sees no other launch of the
+    same kernel)."""
     b = StepBuffers(layer, d["x"].shape[0], d["ids"].shape[1])
     ops = step_ops(layer, d["x"], d["ids"], d["w"], on_input, b)
     names = list(ops)
@@ -86,8 +89,18 @@ def per_op_times(layer, d, on_input, iters, stream, only=None):
     for name in names:          # fill every buffer once, in order
         ops[name]()
     torch.cuda.synchronize()
-    timed_names = [only] if only is not None else names
-    res = {name: timed(ops[name], iters, stream) for name in timed_names}
+    if only is not None:
+        res = {only: timed(ops[only], iters, stream)}
+    else:
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(iters)]
+        for it in range(iters):
+            for i, name in enumerate(names):
+                evs[it][i].record(stream)
+                ops[name]()
+            evs[it][-1].record(stream)
+        torch.cuda.synchronize()
+        res = {name: float(np.mean([evs[it][i].elapsed_time(evs[it][i + 1]) for it in range(iters)]))
+               for i, name in enumerate(names)}
     return res, b.counts.cpu().numpy(), int(b.offsets[-1].item())
 
 
@@ -148,7 +161,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="C5u", choices=sorted(gen.CONFIGS))
     ap.add_argument("--op-iters", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
