@@ -63,8 +63,8 @@ typedef enum {
 
 typedef struct {
     int64_t M;                         /* tokens in the layer call */
-    int32_t K;                         /* hidden size, multiple of 128 */
-    int32_t N;                         /* expert intermediate size, multiple of 128 */
+    int32_t K;                         /* hidden size, multiple of 128, <= 65536 */
+    int32_t N;                         /* expert intermediate size, multiple of 128, <= 32768 */
     int32_t topk;
     int32_t num_global_experts;        /* Eg */
     int32_t num_local_experts;         /* El */
@@ -127,7 +127,9 @@ int moe_permute(const uint8_t* a_q, const float* a_s, const int32_t* topk_ids,
  *                    sum_{k in group g} a[r,k] * w[e,n,k] ),
  * fp32 accumulation.  a [cap_rows,k_in] e4m3, a_s [cap_rows,k_in/128] f32,
  * w [El,n_out,k_in] e4m3, w_s [El,n_out/128,k_in/128] f32,
- * out [cap_rows,n_out] bf16.  Rows that are not valid are not written. */
+ * out [cap_rows,n_out] bf16.  Rows that are not valid are not written.
+ * n_out and k_in: positive multiples of 128, at most 65536 (MOE_ERR_SHAPE
+ * otherwise). */
 int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const uint8_t* w, const float* w_s,
                          const int32_t* expert_offsets, const int32_t* counts, int32_t El,
                          int64_t cap_rows, int32_t n_out, int32_t k_in, uint16_t* out,

@@ -125,8 +125,10 @@ Plan make_plan(const moe_problem& p) {
 int check_problem(const moe_problem* p) {
     REQUIRE(p != nullptr, MOE_ERR_INVALID_ARG, "problem is NULL");
     REQUIRE(p->M >= 0, MOE_ERR_SHAPE, "M=%lld < 0", (long long)p->M);
-    REQUIRE(p->K > 0 && p->K % moe::kGroup == 0, MOE_ERR_SHAPE, "K=%d is not a positive multiple of 128", p->K);
-    REQUIRE(p->N > 0 && p->N % moe::kGroup == 0, MOE_ERR_SHAPE, "N=%d is not a positive multiple of 128", p->N);
+    REQUIRE(p->K > 0 && p->K % moe::kGroup == 0 && p->K <= 65536, MOE_ERR_SHAPE,
+            "K=%d is not a positive multiple of 128 up to 65536", p->K);
+    REQUIRE(p->N > 0 && p->N % moe::kGroup == 0 && p->N <= 32768, MOE_ERR_SHAPE,
+            "N=%d is not a positive multiple of 128 up to 32768", p->N);
     REQUIRE(p->topk >= 1 && p->topk <= 256, MOE_ERR_SHAPE, "topk=%d outside [1,256]", p->topk);
     REQUIRE(p->num_global_experts >= 1, MOE_ERR_SHAPE, "Eg=%d", p->num_global_experts);
     REQUIRE(p->num_local_experts >= 1 && p->num_local_experts <= moe::kMaxLocalExperts, MOE_ERR_SHAPE,
@@ -245,8 +247,10 @@ int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const uint8_t* w, c
                          int64_t cap_rows, int32_t n_out, int32_t k_in, uint16_t* out,
                          void* stream) {
     REQUIRE(El >= 1 && El <= moe::kMaxLocalExperts, MOE_ERR_SHAPE, "El=%d outside [1,1024]", El);
-    REQUIRE(n_out > 0 && n_out % moe::kGroup == 0, MOE_ERR_SHAPE, "n_out=%d is not a positive multiple of 128", n_out);
-    REQUIRE(k_in > 0 && k_in % moe::kGroup == 0, MOE_ERR_SHAPE, "k_in=%d is not a positive multiple of 128", k_in);
+    REQUIRE(n_out > 0 && n_out % moe::kGroup == 0 && n_out <= 65536, MOE_ERR_SHAPE,
+            "n_out=%d is not a positive multiple of 128 up to 65536", n_out);
+    REQUIRE(k_in > 0 && k_in % moe::kGroup == 0 && k_in <= 65536, MOE_ERR_SHAPE,
+            "k_in=%d is not a positive multiple of 128 up to 65536", k_in);
     REQUIRE(cap_rows >= 0 && cap_rows < (int64_t(1) << 31), MOE_ERR_SHAPE, "cap_rows=%lld", (long long)cap_rows);
     if (cap_rows == 0) return MOE_OK;
     REQUIRE_PTR(a);

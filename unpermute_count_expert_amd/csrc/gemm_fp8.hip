@@ -13,18 +13,22 @@
 //    fp32 values, so they cannot ride in the MFMA's power-of-two block-scale
 //    operands; and the MFMA's own summation keeps only ~14 bits below the
 //    largest product of each 8-wide K block, so promoting every 128 K to fp32
-//    also bounds that error.  The per-row products a_s * w_s are formed once
-//    per step when the scales are staged, and the MFMAs of row block i+1 are
-//    issued before the promotion FMAs of row block i.
-//  * K loop in 128-byte steps through a double-buffered LDS stage (48 KB):
-//    the next step's A and B tiles (or the next tile's first step) are
-//    fetched into registers while the MFMAs consume the current stage, then
-//    written to the other stage; one barrier per step and no bubble between
-//    tiles.
+//    also bounds that error.  The MFMAs of row block i+1 are issued before
+//    the promotion FMAs of row block i.
+//  * Operands move global -> LDS by LDS DMA (global_load_lds_dwordx4: each
+//    lane's 16 bytes land at M0 + 16*lane) through a ring of three 48 KB
+//    stages, so the loads of steps i+1 and i+2 are in flight while the MFMAs
+//    consume step i, with no staging registers and no LDS store
+//    instructions.  A wave waits only for its own DMAs of the step it is
+//    about to read (loads retire in issue order), and one barrier per step
+//    publishes every wave's.  The activation scales of a step ride in the same
+//    ring (dword DMA); the weight block scale is wave-uniform and comes
+//    through the scalar cache.
 //  * LDS rows are 128 bytes, the 16-byte chunk c of row r stored at position
-//    c ^ ((r ^ r/8) mod 8): the 16 lanes feeding one MFMA row block and the 16
-//    lanes storing two global rows both touch 16 distinct bank groups
-//    (measured on gfx950: no conflict cycles for either pattern).
+//    c ^ ((r ^ r/8) mod 8), so the 16 lanes feeding one MFMA row block read 16
+//    distinct bank groups (measured on gfx950: no conflict cycles).  A DMA
+//    writes 8 whole LDS rows, so each lane fetches the global chunk that the
+//    swizzle places at its LDS position.
 //  * Weight rows are placed so that lane j of MFMA column block b holds output
 //    column 4j + b: each lane owns 4 adjacent columns and the epilogue writes
 //    8-byte bf16 quads straight from registers, 128 contiguous bytes per row.
@@ -34,7 +38,8 @@
 //  * Persistent grid with an XCD-aware tile order: workgroups are dealt to the
 //    8 XCDs round-robin, so XCD x walks the contiguous x-th eighth of the
 //    (expert, m-tile, n-tile) sequence and an expert's weights stay hot in
-//    that XCD's L2.
+//    that XCD's L2.  Tiles are walked without divisions, and the DMA stream
+//    runs two steps ahead across tile boundaries.
 //  * Row indices are clamped on the device, so even inconsistent
 //    offsets/counts cannot move an access out of bounds.
 #include "moe_device.hpp"
@@ -50,6 +55,8 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;   // 8: 2 along M, 4 along N
 constexpr int kStageA = BM * BK;           // bytes
 constexpr int kStage = kStageA + BN * BK;  // 48 KB
+constexpr int kStages = 3;
+constexpr int kDmaPerStep = 7;             // per wave and step: 2 A + 4 B + 1 scale
 
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -66,12 +73,14 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
     return v;
 }
 
-// byte offset of 16-byte chunk c of LDS tile row r
-__device__ __forceinline__ int swz(int c, int r) { return r * 128 + ((c ^ ((r ^ (r >> 3)) & 7)) << 4); }
+// position (0..7) of 16-byte chunk c in LDS tile row r, and its inverse
+__device__ __forceinline__ int swz_pos(int c, int r) { return c ^ ((r ^ (r >> 3)) & 7); }
+__device__ __forceinline__ int swz(int c, int r) { return r * 128 + (swz_pos(c, r) << 4); }
 
 // LDS row of weight row n of the tile: within each 64-row quarter, row 4j+b
 // goes to 16b+j, so MFMA column j of column block b is weight row 4j+b
 __device__ __forceinline__ int b_row(int n) { return (n & ~63) | ((n & 3) << 4) | ((n >> 2) & 15); }
+__device__ __forceinline__ int b_row_inv(int R) { return (R & ~63) | ((R & 15) << 2) | ((R >> 4) & 3); }
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b) {
     const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -88,9 +97,117 @@ __device__ __forceinline__ v8i frag(const uint8_t* p, int off_lo) {
     return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
-struct Tile {
-    int e, m0, row_end, n0;
+// LDS DMA: lane l's 16 (4) bytes from sbase + voff land at LDS byte m0 + 16*l (4*l)
+__device__ __forceinline__ void dma16(uint32_t m0, uint32_t voff, const void* sbase) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(uint32_t m0, uint32_t voff, const void* sbase) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(m0), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+
+// Wait until at most n of this wave's vector-memory loads issued after the
+// one waited for are outstanding, then the workgroup barrier.  Loads retire
+// in issue order, so a younger load can never be the reason the count is
+// low; stores may retire in any order, which only makes the wait longer.
+#define MOE_WAIT_CASE(n)                                                              \
+    case n:                                                                           \
+        asm volatile("s_waitcnt vmcnt(" #n ") lgkmcnt(0)\n\ts_barrier" ::: "memory"); \
+        break;
+__device__ __forceinline__ void wait_loads_barrier(int n) {
+    switch (n) {
+        MOE_WAIT_CASE(1) MOE_WAIT_CASE(2) MOE_WAIT_CASE(3) MOE_WAIT_CASE(4) MOE_WAIT_CASE(5)
+        MOE_WAIT_CASE(6) MOE_WAIT_CASE(7) MOE_WAIT_CASE(8) MOE_WAIT_CASE(9) MOE_WAIT_CASE(10)
+        MOE_WAIT_CASE(11) MOE_WAIT_CASE(12) MOE_WAIT_CASE(13) MOE_WAIT_CASE(14) MOE_WAIT_CASE(15)
+        MOE_WAIT_CASE(16) MOE_WAIT_CASE(17) MOE_WAIT_CASE(18) MOE_WAIT_CASE(19) MOE_WAIT_CASE(20)
+        default:
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+}
+#undef MOE_WAIT_CASE
+
+// rows [lo, hi) of expert e, clamped to [0, cap_rows)
+__device__ __forceinline__ void rows_of(const int32_t* __restrict__ offsets, const int32_t* __restrict__ counts,
+                                        int64_t cap_rows, int e, int64_t& lo, int64_t& hi) {
+    lo = offsets[e];
+    lo = lo < 0 ? 0 : (lo > cap_rows ? cap_rows : lo);
+    int64_t c = counts[e];
+    c = c < 0 ? 0 : c;
+    hi = lo + c > cap_rows ? cap_rows : lo + c;
+}
+
+// Walks one block's tiles t_lo, t_lo + nslots, ... of the (expert, m-tile,
+// n-tile) sequence without divisions: the m-tile/n-tile pair advances by a
+// precomputed quotient and remainder, and the expert by a forward scan of
+// s_tpre (s_tpre[e] = first m-tile of expert e).  All fields are
+// wave-uniform.
+struct TileCursor {
+    int64_t t;           // tile index
+    int tm, tn;          // m-tile, n-tile
+    int e;               // expert of m-tile tm
+    int e_lo, e_hi;      // its rows [e_lo, e_hi)
     bool valid;
+    int m0, row_end, n0; // the tile: rows [m0, min(m0 + BM, row_end)), columns n0..
+};
+
+struct TileWalk {
+    const int32_t* offsets;
+    const int32_t* counts;
+    int64_t cap_rows;
+    const int* s_tpre;
+    int El, ntn, step_q, step_r;   // nslots = step_q * ntn + step_r
+    int64_t t_hi, nslots;
+
+    __device__ __forceinline__ void fill(TileCursor& c) const {
+        int64_t lo, hi;
+        rows_of(offsets, counts, cap_rows, c.e, lo, hi);
+        c.e_lo = __builtin_amdgcn_readfirstlane((int)lo);
+        c.e_hi = __builtin_amdgcn_readfirstlane((int)hi);
+    }
+    __device__ __forceinline__ void tile(TileCursor& c) const {
+        // clamped so that every row this tile touches is in [0, cap_rows)
+        int m0 = c.e_lo + (c.tm - s_tpre[c.e]) * BM;
+        m0 = max(c.e_lo, min(m0, c.e_hi - 1));
+        c.m0 = __builtin_amdgcn_readfirstlane(min(m0, (int)cap_rows - 1));
+        c.row_end = c.e_hi;
+        c.n0 = c.tn * BN;
+    }
+    __device__ __forceinline__ void start(TileCursor& c, int64_t t) const {
+        c.t = t;
+        c.valid = t < t_hi;
+        c.tm = c.tn = c.e = c.e_lo = c.e_hi = c.m0 = c.row_end = c.n0 = 0;
+        if (!c.valid) return;
+        c.tm = (int)(t / ntn);
+        c.tn = (int)(t - (int64_t)c.tm * ntn);
+        int lo = 0, hi = El - 1;  // largest e < El with s_tpre[e] <= tm
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_tpre[mid] <= c.tm) lo = mid; else hi = mid - 1;
+        }
+        c.e = __builtin_amdgcn_readfirstlane(lo);
+        fill(c);
+        tile(c);
+    }
+    __device__ __forceinline__ void next(TileCursor& c) const {
+        c.t += nslots;
+        c.valid = c.t < t_hi;
+        if (!c.valid) return;
+        c.tn += step_r;
+        c.tm += step_q;
+        if (c.tn >= ntn) {
+            c.tn -= ntn;
+            c.tm += 1;
+        }
+        bool moved = false;
+        while (c.e + 1 < El && s_tpre[c.e + 1] <= c.tm) {
+            ++c.e;
+            moved = true;
+        }
+        c.e = __builtin_amdgcn_readfirstlane(c.e);
+        if (moved) fill(c);
+        tile(c);
+    }
 };
 
 __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
@@ -98,8 +215,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
     const float* __restrict__ w_s, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ counts, int El, int64_t cap_rows, int n_out, int k_in,
     uint16_t* __restrict__ out) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
-    __shared__ __attribute__((aligned(16))) float sSc[2][2][BM];   // [stage][128-col block][row]
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStage];
+    __shared__ __attribute__((aligned(16))) float sAs[kStages][BM];   // [stage][row]
     __shared__ int s_tpre[kMaxLocalExperts + 1];
     __shared__ int s_wsum[kWaves];
 
@@ -108,13 +225,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
 
     // ---- m-tile prefix over the experts' valid row counts ------------------
-    auto rows_of = [&](int e, int64_t& lo, int64_t& hi) {
-        lo = offsets[e];
-        lo = lo < 0 ? 0 : (lo > cap_rows ? cap_rows : lo);
-        int64_t c = counts[e];
-        c = c < 0 ? 0 : c;
-        hi = lo + c > cap_rows ? cap_rows : lo + c;
-    };
     int ntl[2];
     int tsum = 0;
 #pragma unroll
@@ -123,7 +233,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
         int nt = 0;
         if (e < El) {
             int64_t lo, hi;
-            rows_of(e, lo, hi);
+            rows_of(offsets, counts, cap_rows, e, lo, hi);
             nt = (int)((hi - lo + BM - 1) / BM);
         }
         ntl[j] = nt;
@@ -143,111 +253,132 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
     if (tid == kThreads - 1) s_tpre[El] = excl;
     __syncthreads();
 
-    const int mtiles = s_tpre[El];
+    const int mtiles = __builtin_amdgcn_readfirstlane(s_tpre[El]);
     const int ntn = (n_out + BN - 1) / BN;   // the last n-tile may hold only 128 columns
     const int nb128 = n_out / 128;
     const int kg = k_in / BK;
     const int64_t total = (int64_t)mtiles * ntn;
     const int xcd = blockIdx.x & 7;
     const int nslots = gridDim.x >> 3;
+    const int64_t t_lo = total * xcd / 8 + (blockIdx.x >> 3);
     const int64_t t_hi = total * (xcd + 1) / 8;
-    int64_t t_cur = total * xcd / 8 + (blockIdx.x >> 3);
+    const int64_t ntiles = t_lo < t_hi ? (t_hi - t_lo + nslots - 1) / nslots : 0;
+    const int64_t S = ntiles * kg;   // this block's K steps, over all its tiles
 
-    auto tile_at = [&](int64_t t) {
-        Tile T;
-        T.valid = t < t_hi;
-        if (!T.valid) {
-            T.e = T.m0 = T.row_end = T.n0 = 0;
-            return T;
-        }
-        const int tm = (int)(t / ntn);
-        int lo = 0, hi = El - 1;  // largest e < El with s_tpre[e] <= tm
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_tpre[mid] <= tm) lo = mid; else hi = mid - 1;
-        }
-        T.e = __builtin_amdgcn_readfirstlane(lo);
-        int64_t rlo, rhi;
-        rows_of(T.e, rlo, rhi);
-        T.m0 = __builtin_amdgcn_readfirstlane((int)rlo + (tm - s_tpre[T.e]) * BM);
-        T.row_end = __builtin_amdgcn_readfirstlane((int)rhi);
-        T.n0 = (int)(t - (int64_t)tm * ntn) * BN;
-        return T;
-    };
+    TileWalk walk;
+    walk.offsets = offsets;
+    walk.counts = counts;
+    walk.cap_rows = cap_rows;
+    walk.s_tpre = s_tpre;
+    walk.El = El;
+    walk.ntn = ntn;
+    walk.step_q = nslots / ntn;
+    walk.step_r = nslots - walk.step_q * ntn;
+    walk.t_hi = t_hi;
+    walk.nslots = nslots;
 
     const int wm = wave >> 2;   // 0..1
     const int wn = wave & 3;    // 0..3
-    // global -> register assignment: chunk j = tid + 512*q, row j>>3, chunk j&7
-    const int ld_r = tid >> 3;  // + 64*q
-    const int ld_c = tid & 7;
     const int fr = lane & 15;
     const int fc = 2 * (lane >> 4);   // this lane's K chunk pair
-    // per-lane LDS offsets (stage 0) of the fragments and of the stash slots
-    int offA[4], offB[4], stA[2], stB[4];
+    // per-lane LDS offsets (within a stage) of the MFMA fragments
+    int offA[4], offB[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         offA[i] = swz(fc, wm * 64 + i * 16 + fr);
         offB[i] = kStageA + swz(fc, wn * 64 + i * 16 + fr);
     }
-#pragma unroll
-    for (int q = 0; q < 2; ++q) stA[q] = swz(ld_c, ld_r + 64 * q);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) stB[q] = kStageA + swz(ld_c, b_row(ld_r + 64 * q));
-    const int sc_row = tid & (BM - 1);   // threads 0..255 stage one scale product
-    const int sc_nb = (tid >> 7) & 1;
 
-    v4i ra[2], rb[4];
-    float ras = 0.0f, rws = 0.0f;
-    auto fetch = [&](const Tile& T, int g) {
-        const int last = T.row_end - 1 - T.m0;   // last valid row of the tile (>= 0)
-        const int nlast = min(BN, n_out - T.n0) - 1;
-        const uint8_t* abase = a + (int64_t)T.m0 * k_in + g * BK;
-        const uint8_t* bbase = w + ((int64_t)T.e * n_out + T.n0) * k_in + g * BK;
+    // ---- DMA side: which global chunk this lane fetches ---------------------
+    // Wave w fills LDS rows 16w..16w+15 of A (two 8-row DMAs) and 32w..32w+31
+    // of B (four), and the scales of rows 16w..16w+15 (lanes 0..15).
+    const int rA0 = (wave * 2) * 8 + (lane >> 3), rA1 = rA0 + 8;
+    const int cA0 = swz_pos(lane & 7, rA0), cA1 = swz_pos(lane & 7, rA1);   // the swizzle is an involution
+    int nB[4], cB[4];
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-            ra[q] = *reinterpret_cast<const v4i*>(abase + (uint32_t)(min(ld_r + 64 * q, last) * k_in + ld_c * 16));
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            rb[q] = *reinterpret_cast<const v4i*>(bbase + (uint32_t)(min(ld_r + 64 * q, nlast) * k_in + ld_c * 16));
-        // every thread loads (threads >= 256 duplicate 0..255 and never stash),
-        // so there is no divergent branch, and the product is formed at stash
-        // time: nothing in the compute waits on these loads
-        ras = a_s[((int64_t)T.m0 + min(sc_row, last)) * kg + g];
-        rws = w_s[((int64_t)T.e * nb128 + min(T.n0 / 128 + sc_nb, nb128 - 1)) * kg + g];
-    };
-    auto stash = [&](int stage) {
-        uint8_t* base = smem + stage * kStage;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) *reinterpret_cast<v4i*>(base + stA[q]) = ra[q];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) *reinterpret_cast<v4i*>(base + stB[q]) = rb[q];
-        if (tid < 2 * BM) sSc[stage][sc_nb][sc_row] = ras * rws;
-    };
-
-    Tile cur = tile_at(t_cur);
-    if (cur.valid) {
-        fetch(cur, 0);
-        stash(0);
+    for (int q = 0; q < 4; ++q) {
+        const int R = (wave * 4 + q) * 8 + (lane >> 3);
+        nB[q] = b_row_inv(R);
+        cB[q] = swz_pos(lane & 7, R);
     }
-    __syncthreads();
-    int stage = 0;
+    const int rS = wave * 16 + (lane & 15);
+    const uint32_t lds_smem = (uint32_t)(uintptr_t)smem;
+    const uint32_t lds_as = (uint32_t)(uintptr_t)&sAs[0][0];
+
+    // Loads issued by this wave so far, and the count right after each
+    // pending step's DMAs (by ring slot).
+    int loads = 0;
+    int d_end0 = 0, d_end1 = 0, d_end2 = 0;
+
+    // DMA cursor: tile, K step, ring slot, and the per-lane offsets
+    TileCursor dT;
+    walk.start(dT, t_lo);
+    int d_g = 0, d_slot = 0;
+    uint32_t voA0 = 0, voA1 = 0, voB0 = 0, voB1 = 0, voB2 = 0, voB3 = 0, voS = 0;
+#define MOE_DMA_OFFSETS()                                                             \
+    do {                                                                              \
+        const int last_ = max(dT.row_end - 1 - dT.m0, 0);                             \
+        const int nlast_ = min(BN, n_out - dT.n0) - 1;                                \
+        voA0 = (uint32_t)(min(rA0, last_) * k_in + cA0 * 16);                         \
+        voA1 = (uint32_t)(min(rA1, last_) * k_in + cA1 * 16);                         \
+        voB0 = (uint32_t)(min(nB[0], nlast_) * k_in + cB[0] * 16);                    \
+        voB1 = (uint32_t)(min(nB[1], nlast_) * k_in + cB[1] * 16);                    \
+        voB2 = (uint32_t)(min(nB[2], nlast_) * k_in + cB[2] * 16);                    \
+        voB3 = (uint32_t)(min(nB[3], nlast_) * k_in + cB[3] * 16);                    \
+        voS = (uint32_t)(min(rS, last_) * kg * 4);                                    \
+    } while (0)
+    // one step of DMAs into ring slot d_slot, then advance the cursor
+#define MOE_DMA_NEXT()                                                                \
+    do {                                                                              \
+        const uint8_t* sa_ = a + ((int64_t)dT.m0 * k_in + d_g * BK);                  \
+        const uint8_t* sb_ = w + (((int64_t)dT.e * n_out + dT.n0) * k_in + d_g * BK); \
+        const float* ss_ = a_s + ((int64_t)dT.m0 * kg + d_g);                         \
+        const uint32_t base_ = lds_smem + d_slot * kStage;                            \
+        dma16(base_ + (wave * 2) * 1024, voA0, sa_);                                  \
+        dma16(base_ + (wave * 2 + 1) * 1024, voA1, sa_);                              \
+        dma16(base_ + kStageA + (wave * 4) * 1024, voB0, sb_);                        \
+        dma16(base_ + kStageA + (wave * 4 + 1) * 1024, voB1, sb_);                    \
+        dma16(base_ + kStageA + (wave * 4 + 2) * 1024, voB2, sb_);                    \
+        dma16(base_ + kStageA + (wave * 4 + 3) * 1024, voB3, sb_);                    \
+        if (lane < 16) dma4(lds_as + d_slot * (BM * 4) + wave * 64, voS, ss_);        \
+        loads += kDmaPerStep;                                                         \
+        if (d_slot == 0) d_end0 = loads;                                              \
+        else if (d_slot == 1) d_end1 = loads;                                         \
+        else d_end2 = loads;                                                          \
+        d_slot = d_slot == kStages - 1 ? 0 : d_slot + 1;                              \
+        if (++d_g == kg) {                                                            \
+            d_g = 0;                                                                  \
+            walk.next(dT);                                                            \
+            if (dT.valid) MOE_DMA_OFFSETS();                                          \
+        }                                                                             \
+    } while (0)
+    if (dT.valid) MOE_DMA_OFFSETS();
+    if (S > 0) MOE_DMA_NEXT();
+    if (S > 1) MOE_DMA_NEXT();
+
+    int64_t i = 0;   // compute step
+    int slot = 0;    // its ring slot
+    TileCursor cur;
+    walk.start(cur, t_lo);
     while (cur.valid) {
-        const Tile nxt = tile_at(t_cur + nslots);
         const int n_valid = min(BN, n_out - cur.n0);
         const bool wave_has_rows = (cur.m0 + wm * 64) < cur.row_end && wn * 64 < n_valid;
+        const int64_t ws_row = ((int64_t)cur.e * nb128 + min(cur.n0 / 128 + (wn >> 1), nb128 - 1)) * kg;
         v4f acc[4][4];
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-        for (int g = 0; g < kg; ++g) {
-            const bool more = (g + 1 < kg) || nxt.valid;
-            if (g + 1 < kg) fetch(cur, g + 1);
-            else if (nxt.valid) fetch(nxt, 0);
+        for (int g = 0; g < kg; ++g, ++i) {
+            // step i's DMAs complete, in every wave
+            wait_loads_barrier(__builtin_amdgcn_readfirstlane(
+                loads - (slot == 0 ? d_end0 : (slot == 1 ? d_end1 : d_end2))));
+            if (i + 2 < S) MOE_DMA_NEXT();   // into the slot step i-1 has released
             if (wave_has_rows) {
-                const uint8_t* base = smem + stage * kStage;
-                const float* scs = &sSc[stage][wn >> 1][wm * 64 + (lane >> 4) * 4];
+                const uint8_t* base = smem + slot * kStage;
+                const float* scs = &sAs[slot][wm * 64 + (lane >> 4) * 4];
+                const float ws = w_s[ws_row + g];
                 v8i bf[4];
 #pragma unroll
                 for (int ni = 0; ni < 4; ++ni) bf[ni] = frag(base, offB[ni]);
@@ -266,7 +397,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
 #pragma unroll
                         for (int ni = 0; ni < 4; ++ni) p[(mi + 1) & 1][ni] = mfma_fp8(af, bf[ni]);
                     }
-                    const v4f sc = *reinterpret_cast<const v4f*>(scs + mi * 16);
+                    const v4f sa4 = *reinterpret_cast<const v4f*>(scs + mi * 16);
+                    const v4f sc = {sa4.x * ws, sa4.y * ws, sa4.z * ws, sa4.w * ws};
 #pragma unroll
                     for (int ni = 0; ni < 4; ++ni) {
                         const v4f pr = p[mi & 1][ni];
@@ -277,9 +409,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
                     }
                 }
             }
-            if (more) stash(stage ^ 1);
-            __syncthreads();
-            stage ^= 1;
+            slot = slot == kStages - 1 ? 0 : slot + 1;
         }
 
         // ---- epilogue: each lane owns 4 adjacent columns of 16 rows --------
@@ -300,9 +430,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
                     }
                 }
         }
-        cur = nxt;
-        t_cur += nslots;
+        walk.next(cur);
     }
+#undef MOE_DMA_OFFSETS
+#undef MOE_DMA_NEXT
 }
 
 }  // namespace
@@ -313,7 +444,7 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_s, const uint8_t
                                int num_cus, hipStream_t s) {
     const int64_t ntn = (n_out + BN - 1) / BN;
     const int64_t bound = ((cap_rows + BM - 1) / BM + El) * ntn;
-    int64_t grid = num_cus;            // one 8-wave block per CU (97 KB of LDS)
+    int64_t grid = num_cus;            // one 8-wave block per CU (150 KB of LDS)
     if (bound < grid) grid = bound;
     grid = ((grid + 7) / 8) * 8;
     if (grid < 8) grid = 8;
