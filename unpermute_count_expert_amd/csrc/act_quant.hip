@@ -71,12 +71,19 @@ __global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restri
             const uint16_t* base = in + r * 2 * (int64_t)n + gi * kGroup + sub * 8;
             const Vals8 g = unpack_bf16x8(*reinterpret_cast<const uint4*>(base));
             const Vals8 u = unpack_bf16x8(*reinterpret_cast<const uint4*>(base + n));
+            float prod[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float e = exp_pinned(-g.v[i]);
                 const float s = g.v[i] / (1.0f + e);
-                const float prod = s * u.v[i];
-                x.v[i] = bf16_to_f32(f32_to_bf16(prod));
+                prod[i] = s * u.v[i];
+            }
+            // the activation is rounded to bf16 before it is quantised
+#pragma unroll
+            for (int i = 0; i < 8; i += 2) {
+                const uint32_t pk = f32x2_to_bf16x2(prod[i], prod[i + 1]);
+                x.v[i] = __uint_as_float(pk << 16);
+                x.v[i + 1] = __uint_as_float(pk & 0xffff0000u);
             }
         }
         // largest non-NaN magnitude: a compare-select skips quiet and
@@ -100,8 +107,9 @@ __global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restri
 #pragma unroll
         for (int i = 0; i < 8; ++i) t[i] = x.v[i] * inv;
         uint2 codes;
-        codes.x = f32x4_to_e4m3(t[0], t[1], t[2], t[3]);
-        codes.y = f32x4_to_e4m3(t[4], t[5], t[6], t[7]);
+        // |t| <= 448 (1 + 2^-23) unless t is NaN: d >= every |x| of the group
+        codes.x = f32x4_to_e4m3_bounded(t[0], t[1], t[2], t[3]);
+        codes.y = f32x4_to_e4m3_bounded(t[4], t[5], t[6], t[7]);
         if (valid) {
             *reinterpret_cast<uint2*>(q + r * n + gi * kGroup + sub * 8) = codes;
             if (sub == 0) q_s[r * ng + gi] = scale;

@@ -102,8 +102,11 @@ __global__ __launch_bounds__(kScanThreads) void k_permute_scan(
         const int col = c0 + lane;
         const bool valid = col < El;
         int sum = 0;
-        if (valid)
+        if (valid) {
+            // independent loads, eight in flight per lane
+#pragma unroll 8
             for (int b = b_lo; b < b_hi; ++b) sum += hist[(int64_t)b * El + col];
+        }
         band[wave][lane] = sum;
         __syncthreads();
         if (wave == 0) {
@@ -131,6 +134,7 @@ __global__ __launch_bounds__(kScanThreads) void k_permute_scan(
         __syncthreads();
         if (valid) {
             int base = s_off[col] + band[wave][lane];
+#pragma unroll 8
             for (int b = b_lo; b < b_hi; ++b) {
                 int64_t idx = (int64_t)b * El + col;
                 int t = hist[idx];
@@ -195,19 +199,43 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
     }
     __syncthreads();
 
-    // copies: one wave per token, 16 bytes per lane, each source row read once
+    // copies: each wave takes every fourth token of the block; a lane reads
+    // 16-byte chunks of the token rows, up to kBatch of them in flight at
+    // once, and writes each to the token's expert rows
+    constexpr int kBatch = 8;
     const int kg = K / kGroup;
     const int nchunk = K / 16;
+    const int cpl = (nchunk + kWave - 1) / kWave;        // chunks per lane per token
+    const int my_tokens = ntok > wave ? (ntok - wave + kWaves - 1) / kWaves : 0;
+    const int items = my_tokens * cpl;
+    for (int q0 = 0; q0 < items; q0 += kBatch) {
+        uint4 v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int q = q0 + u;
+            const int tl = wave + (q / cpl) * kWaves;
+            const int c = lane + (q % cpl) * kWave;
+            v[u] = uint4{0, 0, 0, 0};
+            if (q < items && c < nchunk)
+                v[u] = *reinterpret_cast<const uint4*>(a_q + (t0 + tl) * K + (int64_t)c * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int q = q0 + u;
+            const int tl = wave + (q / cpl) * kWaves;
+            const int c = lane + (q % cpl) * kWave;
+            if (q < items && c < nchunk) {
+                const int* rm = rowmap + tl * topk;
+                for (int k = 0; k < topk; ++k) {
+                    const int r = rm[k];
+                    if (r >= 0) *reinterpret_cast<uint4*>(a_perm + (int64_t)r * K + (int64_t)c * 16) = v[u];
+                }
+            }
+        }
+    }
     for (int tl = wave; tl < ntok; tl += kWaves) {
         const int64_t t = t0 + tl;
         const int* rm = rowmap + tl * topk;
-        for (int c = lane; c < nchunk; c += kWave) {
-            const uint4 v = *reinterpret_cast<const uint4*>(a_q + t * K + (int64_t)c * 16);
-            for (int k = 0; k < topk; ++k) {
-                const int r = rm[k];
-                if (r >= 0) *reinterpret_cast<uint4*>(a_perm + (int64_t)r * K + (int64_t)c * 16) = v;
-            }
-        }
         for (int g = lane; g < kg; g += kWave) {
             const float s = a_s[t * kg + g];
             for (int k = 0; k < topk; ++k) {

@@ -422,10 +422,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
                     const int row = cur.m0 + wm * 64 + mi * 16 + (lane >> 4) * 4 + v;
                     if (row < cur.row_end) {
                         v2i q;
-                        q.x = (int)((uint32_t)f32_to_bf16(acc[mi][0][v]) |
-                                    ((uint32_t)f32_to_bf16(acc[mi][1][v]) << 16));
-                        q.y = (int)((uint32_t)f32_to_bf16(acc[mi][2][v]) |
-                                    ((uint32_t)f32_to_bf16(acc[mi][3][v]) << 16));
+                        q.x = (int)f32x2_to_bf16x2(acc[mi][0][v], acc[mi][1][v]);
+                        q.y = (int)f32x2_to_bf16x2(acc[mi][2][v], acc[mi][3][v]);
                         *reinterpret_cast<v2i*>(out + (int64_t)row * n_out + col) = q;
                     }
                 }

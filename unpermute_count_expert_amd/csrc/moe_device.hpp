@@ -15,16 +15,30 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// fp32 -> bf16, round to nearest even (NaN kept quiet).
-__device__ __forceinline__ uint16_t f32_to_bf16(float v) {
-    uint32_t u = __float_as_uint(v);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-    return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+// fp32 -> bf16, round to nearest even; a NaN keeps its sign and top payload
+// bits and is made quiet.  The gfx950 conversion (v_cvt_pk_bf16_f32) does
+// exactly this: it matches the bit-level definition
+//   NaN: (u >> 16) | 0x40,  otherwise: (u + 0x7fff + ((u >> 16) & 1)) >> 16
+// on all 2^32 inputs.
+typedef float moe_f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 moe_bf2 __attribute__((ext_vector_type(2)));
+
+// two values packed lo | hi << 16, one instruction
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+    const moe_bf2 r = __builtin_convertvector((moe_f2){lo, hi}, moe_bf2);
+    uint32_t u;
+    __builtin_memcpy(&u, &r, 4);
+    return u;
 }
 
-// Four fp32 -> four OCP E4M3FN codes packed little-endian in one dword.
-// The hardware conversion rounds to nearest even; saturation to +-448 is
-// done by the clamp, and NaN maps to 0x7F with its sign.
+__device__ __forceinline__ uint16_t f32_to_bf16(float v) {
+    return static_cast<uint16_t>(f32x2_to_bf16x2(v, 0.0f));
+}
+
+// Four fp32 -> four OCP E4M3FN codes packed little-endian in one dword,
+// saturating: the hardware conversion rounds to nearest even but turns
+// out-of-range values into the NaN code, so they are clamped to +-448
+// first; NaN maps to 0x7F with its sign.
 __device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, float d) {
     float ca = __builtin_fminf(__builtin_fmaxf(a, -448.0f), 448.0f);
     float cb = __builtin_fminf(__builtin_fmaxf(b, -448.0f), 448.0f);
@@ -38,6 +52,23 @@ __device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, flo
     if (b != b) r = (r & 0xffff00ffu) | ((((__float_as_uint(b) >> 24) & 0x80u) | 0x7fu) << 8);
     if (c != c) r = (r & 0xff00ffffu) | ((((__float_as_uint(c) >> 24) & 0x80u) | 0x7fu) << 16);
     if (d != d) r = (r & 0x00ffffffu) | ((((__float_as_uint(d) >> 24) & 0x80u) | 0x7fu) << 24);
+    return r;
+}
+
+// The same encoding for values that are NaN or below 464 in magnitude, such
+// as v * (448 / d) with d >= |v| (at most 448 * (1 + 2^-23)): without the
+// clamp the hardware conversion gives the same codes there (checked on all
+// 2^32 inputs), and the NaN repair runs only when a NaN is present.
+__device__ __forceinline__ uint32_t f32x4_to_e4m3_bounded(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    uint32_t r = static_cast<uint32_t>(w);
+    if (__builtin_expect((a != a) | (b != b) | (c != c) | (d != d), 0)) {
+        if (a != a) r = (r & 0xffffff00u) | ((__float_as_uint(a) >> 24) & 0x80u) | 0x7fu;
+        if (b != b) r = (r & 0xffff00ffu) | ((((__float_as_uint(b) >> 24) & 0x80u) | 0x7fu) << 8);
+        if (c != c) r = (r & 0xff00ffffu) | ((((__float_as_uint(c) >> 24) & 0x80u) | 0x7fu) << 16);
+        if (d != d) r = (r & 0x00ffffffu) | ((((__float_as_uint(d) >> 24) & 0x80u) | 0x7fu) << 24);
+    }
     return r;
 }
 

@@ -30,23 +30,34 @@ __global__ __launch_bounds__(kThreads) void k_unpermute(const uint16_t* __restri
         float acc[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-        for (int k = 0; k < topk; ++k) {
-            const int r = rows[k];
-            if (r < 0 || r >= y_rows) continue;
-            const float wk = apply_on_input ? 1.0f : wts[k];
-            const uint4 v = *reinterpret_cast<const uint4*>(y + (int64_t)r * K + c0);
-            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+        // eight of the token's rows at a time: all eight loads are issued
+        // before the first use, then folded strictly in k order
+        for (int k0 = 0; k0 < topk; k0 += 8) {
+            uint4 v[8];
+            bool ok[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[2 * i] = __builtin_fmaf(wk, __uint_as_float(u[i] << 16), acc[2 * i]);
-                acc[2 * i + 1] = __builtin_fmaf(wk, __uint_as_float(u[i] & 0xffff0000u), acc[2 * i + 1]);
+            for (int j = 0; j < 8; ++j) {
+                const int r = k0 + j < topk ? rows[k0 + j] : -1;
+                ok[j] = r >= 0 && r < y_rows;
+                v[j] = ok[j] ? *reinterpret_cast<const uint4*>(y + (int64_t)r * K + c0) : uint4{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (!ok[j]) continue;
+                const float wk = apply_on_input ? 1.0f : wts[k0 + j];
+                const uint32_t u[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[2 * i] = __builtin_fmaf(wk, __uint_as_float(u[i] << 16), acc[2 * i]);
+                    acc[2 * i + 1] = __builtin_fmaf(wk, __uint_as_float(u[i] & 0xffff0000u), acc[2 * i + 1]);
+                }
             }
         }
         uint4 o;
-        o.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
-        o.y = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
-        o.z = (uint32_t)f32_to_bf16(acc[4]) | ((uint32_t)f32_to_bf16(acc[5]) << 16);
-        o.w = (uint32_t)f32_to_bf16(acc[6]) | ((uint32_t)f32_to_bf16(acc[7]) << 16);
+        o.x = f32x2_to_bf16x2(acc[0], acc[1]);
+        o.y = f32x2_to_bf16x2(acc[2], acc[3]);
+        o.z = f32x2_to_bf16x2(acc[4], acc[5]);
+        o.w = f32x2_to_bf16x2(acc[6], acc[7]);
         *reinterpret_cast<uint4*>(out + t * K + c0) = o;
     }
 }
