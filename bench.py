@@ -7,9 +7,12 @@ one moe_forward_chunked call over the whole batch (input quant, count,
 permute, GEMM w13, SiLU-mul requant, GEMM w2, unpermute-reduce), inputs
 already resident in HBM.
 
-Prints one JSON line: tokens/s for the layer, plus per-op times, GEMM TFLOP/s,
-per-op algorithmic GB/s, the roofline of the dominant kernel (GEMM w13) and
-the CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line: tokens/s for the layer (steps back to back), the step
+time distribution warm and cold (caches flushed before each step), per-op
+times measured in place (median, p10, p90, and cold), GEMM TFLOP/s, per-op
+algorithmic GB/s, the roofline of the dominant kernel (GEMM w13), the count
+on a 2^24-pair case, measured HBM ceilings, and the CPU oracle timed on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -73,14 +76,34 @@ def timed(fn, iters, stream):
     return start.elapsed_time(end) / iters  # ms
 
 
-def per_op_times(layer, d, on_input, iters, stream, only=None):
+def stats(ms_list):
+    a = np.asarray(ms_list, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 5), "p10": round(float(np.percentile(a, 10)), 5),
+            "p90": round(float(np.percentile(a, 90)), 5), "n": int(a.size)}
+
+
+class Flusher:
+    """Writes a 512 MiB buffer, more than the MALL (256 MB) and the L2s hold,
+    so that the next kernel starts with cold caches."""
+
+    def __init__(self):
+        self.buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+        self.v = 0
+
+    def __call__(self):
+        self.v = (self.v + 1) & 0xFF
+        self.buf.fill_(self.v)
+
+
+def per_op_times(layer, d, on_input, iters, stream, only=None, flush=None):
     """Times each op of the pipeline through its own C-ABI entry point (the
     kernels the fused call runs, plus the standalone count).  Each of `iters`
     passes runs the whole sequence with a HIP event recorded on the launching
-    stream before every op, so every op is timed in place, between its real
-    neighbours.  With `only`, the ops before it run once to fill its inputs and
+    stream before and after every op, so every op is timed in place, between
+    its real neighbours; with `flush`, the caches are flushed (untimed) before
+    every op.  With `only`, the ops before it run once to fill its inputs and
     only it is launched repeatedly (so a profiler sees no other launch of the
-    same kernel)."""
+    same kernel).  Returns {op: [ms per pass]}."""
     b = StepBuffers(layer, d["x"].shape[0], d["ids"].shape[1])
     ops = step_ops(layer, d["x"], d["ids"], d["w"], on_input, b)
     names = list(ops)
@@ -90,18 +113,49 @@ def per_op_times(layer, d, on_input, iters, stream, only=None):
         ops[name]()
     torch.cuda.synchronize()
     if only is not None:
-        res = {only: timed(ops[only], iters, stream)}
+        res = {only: [timed(ops[only], iters, stream)]}
     else:
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(iters)]
+        evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
+               for _ in range(iters)]
         for it in range(iters):
             for i, name in enumerate(names):
-                evs[it][i].record(stream)
+                if flush is not None:
+                    flush()
+                evs[it][i][0].record(stream)
                 ops[name]()
-            evs[it][-1].record(stream)
+                evs[it][i][1].record(stream)
         torch.cuda.synchronize()
-        res = {name: float(np.mean([evs[it][i].elapsed_time(evs[it][i + 1]) for it in range(iters)]))
+        res = {name: [evs[it][i][0].elapsed_time(evs[it][i][1]) for it in range(iters)]
                for i, name in enumerate(names)}
     return res, b.counts.cpu().numpy(), int(b.offsets[-1].item())
+
+
+def count_scaled(iters, stream):
+    """moe_count on 2^24 (token, k) pairs (2^21 tokens x top-8 over 128
+    experts, 64 MiB of ids): the layer's own count moves 0.5 MB, too little
+    for bandwidth to show."""
+    g = torch.Generator(device="cpu").manual_seed(7)
+    ids = torch.randint(0, 128, (1 << 21, 8), generator=g, dtype=torch.int32).to("cuda:0")
+    counts = torch.empty(128, dtype=torch.int32, device="cuda:0")
+    fn = lambda: moe._lib.moe_count(ids, None, 128, 128, counts)
+    fn()
+    torch.cuda.synchronize()
+    ms = [timed(fn, 1, stream) for _ in range(iters)]
+    st = stats(ms)
+    st["GB/s"] = round(4 * (1 << 24) / (st["median"] * 1e-3) / 1e9, 1)
+    st["hbm_frac"] = round(st["GB/s"] / PEAK_HBM_GBS, 4)
+    return st
+
+
+def ceilings(iters, stream):
+    """Measured HBM ceiling on this GPU for context: a 1 GiB device copy
+    (read + write)."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    cp = stats([timed(lambda: b.copy_(a), 1, stream) for _ in range(iters)])
+    return {"copy_GB/s": round(2 * n / (cp["median"] * 1e-3) / 1e9, 1),
+            "note": "torch copy_ of 1 GiB (read + write), median of %d" % iters}
 
 
 def algorithmic(cfg, counts: np.ndarray, R: int):
@@ -163,7 +217,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="C5u", choices=sorted(gen.CONFIGS))
-    ap.add_argument("--op-iters", type=int, default=10)
+    ap.add_argument("--op-iters", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--profile-op", default=None,
@@ -195,32 +249,58 @@ def main():
     if args.profile_op is not None:
         ops, counts, R = per_op_times(layer, d, on_input, args.op_iters, stream, only=args.profile_op)
         print(json.dumps({"mode": "profile_op", "op": args.profile_op, "iters": args.op_iters,
-                          "ms": round(ops[args.profile_op], 5), "config": cfg.name}), flush=True)
+                          "ms": round(ops[args.profile_op][0], 5), "config": cfg.name}), flush=True)
         return
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms = timed(step, args.steps, stream)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for k in range(args.steps):
+        step()
+        evs[k + 1].record(stream)
+    evs[-1].synchronize()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    warm = [evs[k].elapsed_time(evs[k + 1]) for k in range(args.steps)]
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+
+    flush = Flusher()
+    cold = []
+    for _ in range(args.steps):
+        flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        e1.synchronize()
+        cold.append(e0.elapsed_time(e1))
 
     ops, counts, R = per_op_times(layer, d, on_input, args.op_iters, stream)
+    ops_cold, _, _ = per_op_times(layer, d, on_input, args.op_iters, stream, flush=flush)
     P, Ene, g1f, g2f, by = algorithmic(cfg, counts, R)
     ops_out = {}
-    for name, t in ops.items():
-        rec = {"ms": round(t, 5), "GB/s": round(by[name] / (t * 1e-3) / 1e9, 1)}
+    for name in ops:
+        st = stats(ops[name])
+        t = st["median"]
+        rec = {"ms": t, "p10": st["p10"], "p90": st["p90"], "GB/s": round(by[name] / (t * 1e-3) / 1e9, 1)}
         rec["hbm_frac"] = round(rec["GB/s"] / PEAK_HBM_GBS, 4)
         if name == "gemm_w13":
             rec["TFLOP/s"] = round(g1f / (t * 1e-3) / 1e12, 1)
         if name == "gemm_w2":
             rec["TFLOP/s"] = round(g2f / (t * 1e-3) / 1e12, 1)
+        tc = stats(ops_cold[name])["median"]
+        rec["cold_ms"] = tc
+        rec["cold_GB/s"] = round(by[name] / (tc * 1e-3) / 1e9, 1)
         ops_out[name] = rec
-    t_g1 = ops["gemm_w13"]
+    t_g1 = stats(ops["gemm_w13"])["median"]
     achieved = g1f / (t_g1 * 1e-3) / 1e12
-    gemm_both = (g1f + g2f) / ((ops["gemm_w13"] + ops["gemm_w2"]) * 1e-3) / 1e12
+    t_g2 = stats(ops["gemm_w2"])["median"]
+    gemm_both = (g1f + g2f) / ((t_g1 + t_g2) * 1e-3) / 1e12
     traffic = measured_traffic()
+    wst, cst = stats(warm), stats(cold)
     line = {
         "metric": METRIC,
         "value": round(cfg.M / (ms * 1e-3), 1),
@@ -241,9 +321,13 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "grouped GEMM w13 (k_grouped_gemm)",
                      "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic},
+        "step": {"warm": wst, "cold": cst, "cold_tokens/s": round(cfg.M / (cst["median"] * 1e-3), 1),
+                 "note": "warm: steps back to back; cold: a 512 MiB write before each step (untimed)"},
         "gemm_tflops_both": round(gemm_both, 1),
         "gemm_frac_both": round(gemm_both / PEAK_FP8_TFLOPS, 4),
         "ops": ops_out,
+        "count_scaled_2^24_pairs": count_scaled(args.op_iters, stream),
+        "ceilings": ceilings(5, stream),
         "wall_s_timed": round(wall, 3),
         "input_gen_s": round(t_gen, 1),
     }

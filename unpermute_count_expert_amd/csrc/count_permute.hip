@@ -4,10 +4,14 @@
 //
 // Permute runs in three launches:
 //   hist    one block per 256 (token, k) pairs: per-block expert histogram
-//   scan    one block: counts, aligned offsets, per-block row bases, padding
-//   scatter one block per 256 pairs: wave-ballot ranks (stable in flat pair
-//           order), inverse indices, then each token row is read once and
-//           written to each of its expert rows with 16-byte lanes.
+//   colscan one block per expert: exclusive scan of its column of the
+//           histogram (the block's first row within the expert's segment)
+//           and the expert's count
+//   scatter one block per 256 pairs: aligned offsets (every block scans the
+//           El counts itself; block 0 also publishes offsets and padding
+//           marks), wave-ballot ranks (stable in flat pair order), inverse
+//           indices, then each token row is read once and written to each of
+//           its expert rows with 16-byte lanes.
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 
@@ -34,13 +38,33 @@ __global__ __launch_bounds__(256) void k_count(const int32_t* __restrict__ ids, 
     if (threadIdx.x == 0) bad = 0;
     __syncthreads();
     int my_bad = 0;
-    for (int64_t f = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; f < num_pairs;
-         f += (int64_t)gridDim.x * blockDim.x) {
-        int id = ids[f];
-        int e = local_expert(id, emap, Eg, El);
+    auto add = [&](int id) __attribute__((always_inline)) {
+        const int e = local_expert(id, emap, Eg, El);
         if (e >= 0) atomicAdd(&h[e], 1);
         my_bad += (id < -1 || id >= Eg) ? 1 : 0;
+    };
+    // 16-byte loads of four ids, four loads in flight per lane before the
+    // LDS atomics that consume them
+    const int4* ids4 = reinterpret_cast<const int4*>(ids);
+    const int64_t nvec = num_pairs / 4;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t v0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; v0 < nvec; v0 += 4 * stride) {
+        int4 q[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t v = v0 + u * stride;
+            q[u] = v < nvec ? ids4[v] : int4{-1, -1, -1, -1};
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            add(q[u].x);
+            add(q[u].y);
+            add(q[u].z);
+            add(q[u].w);
+        }
     }
+    for (int64_t f = nvec * 4 + blockIdx.x * (int64_t)blockDim.x + threadIdx.x; f < num_pairs; f += stride)
+        add(ids[f]);
     if (my_bad) atomicAdd(&bad, my_bad);
     __syncthreads();
     for (int e = threadIdx.x; e < El; e += blockDim.x)
@@ -80,77 +104,40 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
     return v;
 }
 
-// Column scan of hist [nblk, El]: counts, aligned offsets and, in place, the
-// first row of each expert's segment that block b fills.  Also marks padding
-// rows and rows past the last segment with row_src = -1.
-__global__ __launch_bounds__(kScanThreads) void k_permute_scan(
-    int32_t* __restrict__ hist, int nblk, int El, int align, int64_t cap_rows,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ row_src,
-    int32_t* __restrict__ counts_copy) {
-    __shared__ int band[kScanWaves][kWave];
-    __shared__ int s_off[kMaxLocalExperts + 1];
-    __shared__ int s_cnt[kMaxLocalExperts];
-    __shared__ int running;
+__device__ __forceinline__ int wave_exclusive_scan(int v) { return wave_inclusive_scan(v) - v; }
+
+// Column e of hist [nblk, El] (one block per expert): replaced in place by
+// its exclusive prefix (the first row of expert e's segment that block b
+// fills, relative to the segment start); the column total is counts[e].
+__global__ __launch_bounds__(kScanThreads) void k_permute_colscan(int32_t* __restrict__ hist, int nblk, int El,
+                                                                  int32_t* __restrict__ counts,
+                                                                  int32_t* __restrict__ counts_copy) {
+    __shared__ int wsum[kScanWaves];
+    const int e = blockIdx.x;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int per_band = (nblk + kScanWaves - 1) / kScanWaves;
-    const int b_lo = wave * per_band;
-    const int b_hi = min(nblk, b_lo + per_band);
-    if (threadIdx.x == 0) running = 0;
+    const int per = (nblk + kScanThreads - 1) / kScanThreads;   // rows per thread, contiguous
+    const int b_lo = min(nblk, (int)threadIdx.x * per);
+    const int b_hi = min(nblk, b_lo + per);
+    int sum = 0;
+#pragma unroll 8
+    for (int b = b_lo; b < b_hi; ++b) sum += hist[(int64_t)b * El + e];
+    const int incl = wave_inclusive_scan(sum);
+    if (lane == kWave - 1) wsum[wave] = incl;
     __syncthreads();
-    for (int c0 = 0; c0 < El; c0 += kWave) {
-        const int col = c0 + lane;
-        const bool valid = col < El;
-        int sum = 0;
-        if (valid) {
-            // independent loads, eight in flight per lane
+    int base = incl - sum;
+    for (int w = 0; w < wave; ++w) base += wsum[w];
 #pragma unroll 8
-            for (int b = b_lo; b < b_hi; ++b) sum += hist[(int64_t)b * El + col];
-        }
-        band[wave][lane] = sum;
-        __syncthreads();
-        if (wave == 0) {
-            int acc = 0;
-            for (int w = 0; w < kScanWaves; ++w) {
-                int t = band[w][lane];
-                band[w][lane] = acc;
-                acc += t;
-            }
-            const int cnt = valid ? acc : 0;
-            const int seg = ((cnt + align - 1) / align) * align;
-            const int incl = wave_inclusive_scan(seg);
-            const int base = running;
-            const int off = base + incl - seg;
-            if (valid) {
-                s_off[col] = off;
-                s_cnt[col] = cnt;
-                counts[col] = cnt;
-                offsets[col] = off;
-                if (counts_copy) counts_copy[col] = cnt;
-            }
-            const int total = __shfl(incl, kWave - 1, kWave);
-            if (lane == 0) running = base + total;
-        }
-        __syncthreads();
-        if (valid) {
-            int base = s_off[col] + band[wave][lane];
-#pragma unroll 8
-            for (int b = b_lo; b < b_hi; ++b) {
-                int64_t idx = (int64_t)b * El + col;
-                int t = hist[idx];
-                hist[idx] = base;
-                base += t;
-            }
-        }
-        __syncthreads();
+    for (int b = b_lo; b < b_hi; ++b) {
+        const int64_t idx = (int64_t)b * El + e;
+        const int t = hist[idx];
+        hist[idx] = base;
+        base += t;
     }
-    const int R = running;
-    if (threadIdx.x == 0) offsets[El] = R;
-    s_off[El] = R;  // every thread writes the same value; read after the barrier
-    __syncthreads();
-    for (int e = threadIdx.x; e < El; e += blockDim.x)
-        for (int r = s_off[e] + s_cnt[e]; r < s_off[e + 1]; ++r) row_src[r] = -1;
-    for (int64_t r = R + threadIdx.x; r < cap_rows; r += blockDim.x) row_src[r] = -1;
+    if (threadIdx.x == kScanThreads - 1) {
+        counts[e] = base;   // the last thread ends on the column total
+        if (counts_copy) counts_copy[e] = base;
+    }
 }
 
 // Stable rank of every local pair, inverse indices, then the row copies.
@@ -158,14 +145,49 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
     const uint8_t* __restrict__ a_q, const float* __restrict__ a_s, const int32_t* __restrict__ ids,
     const float* __restrict__ topk_w, int apply_on_input, int64_t Mc, int K, int topk, int tpb,
     const int32_t* __restrict__ emap, int Eg, int El, int nbits, const int32_t* __restrict__ base,
+    const int32_t* __restrict__ counts, int align, int64_t cap_rows, int32_t* __restrict__ offsets,
     uint8_t* __restrict__ a_perm, float* __restrict__ a_perm_s, int32_t* __restrict__ inv_perm,
     int32_t* __restrict__ row_src) {
     constexpr int kWaves = kPermThreads / kWave;
     __shared__ int wcnt[kWaves][kMaxLocalExperts];
     __shared__ int rowmap[kPermThreads];
+    __shared__ int s_off[kMaxLocalExperts + 1];
+    __shared__ int s_wsum[kWaves];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     for (int j = threadIdx.x; j < kWaves * El; j += blockDim.x) wcnt[j / El][j % El] = 0;
+
+    // aligned segment offsets: exclusive scan of align * ceil(counts / align)
+    // over the experts, four experts per thread
+    {
+        int seg[4], tsum = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int ex = threadIdx.x * 4 + j;
+            const int c = ex < El ? counts[ex] : 0;
+            seg[j] = ((c + align - 1) / align) * align;
+            tsum += seg[j];
+        }
+        const int incl = wave_inclusive_scan(tsum);
+        if (lane == kWave - 1) s_wsum[wave] = incl;
+        __syncthreads();
+        int run = incl - tsum;
+        for (int w = 0; w < wave; ++w) run += s_wsum[w];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int ex = threadIdx.x * 4 + j;
+            if (ex < El) s_off[ex] = run;
+            run += seg[j];
+        }
+        if (threadIdx.x == kPermThreads - 1) s_off[El] = run;
+        __syncthreads();
+    }
+    if (blockIdx.x == 0) {   // publish the offsets; mark padding rows and rows past the end
+        for (int ex = threadIdx.x; ex <= El; ex += blockDim.x) offsets[ex] = s_off[ex];
+        for (int ex = threadIdx.x; ex < El; ex += blockDim.x)
+            for (int r = s_off[ex] + counts[ex]; r < s_off[ex + 1]; ++r) row_src[r] = -1;
+        for (int64_t r = s_off[El] + threadIdx.x; r < cap_rows; r += blockDim.x) row_src[r] = -1;
+    }
 
     const int64_t t0 = (int64_t)blockIdx.x * tpb;
     const int ntok = (int)((Mc - t0) < tpb ? (Mc - t0) : tpb);
@@ -190,7 +212,7 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
     if (e >= 0) {
         int pre = 0;
         for (int w = 0; w < wave; ++w) pre += wcnt[w][e];
-        row = base[(int64_t)blockIdx.x * El + e] + pre + rank_w;
+        row = s_off[e] + base[(int64_t)blockIdx.x * El + e] + pre + rank_w;
     }
     if (active) {
         inv_perm[f] = row;
@@ -276,12 +298,12 @@ hipError_t launch_permute(const uint8_t* a_q, const float* a_s, const int32_t* i
     const int64_t nblk = permute_num_blocks(Mc, topk);
     if (nblk > 0)
         k_permute_hist<<<(unsigned)nblk, kPermThreads, 0, s>>>(ids, Mc, topk, tpb, emap, Eg, El, hist);
-    k_permute_scan<<<1, kScanThreads, 0, s>>>(hist, (int)nblk, El, align, cap_rows, counts, offsets,
-                                              row_src, counts_copy);
-    if (nblk > 0)
-        k_permute_scatter<<<(unsigned)nblk, kPermThreads, 0, s>>>(
-            a_q, a_s, ids, topk_w, apply_on_input, Mc, K, topk, tpb, emap, Eg, El, bits_for(El), hist,
-            a_perm, a_perm_s, inv_perm, row_src);
+    k_permute_colscan<<<(unsigned)El, kScanThreads, 0, s>>>(hist, (int)nblk, El, counts, counts_copy);
+    // at least one block, so that the offsets and padding marks are written
+    // even for an empty chunk
+    k_permute_scatter<<<(unsigned)(nblk > 0 ? nblk : 1), kPermThreads, 0, s>>>(
+        a_q, a_s, ids, topk_w, apply_on_input, Mc, K, topk, tpb, emap, Eg, El, bits_for(El), hist, counts,
+        align, cap_rows, offsets, a_perm, a_perm_s, inv_perm, row_src);
     return hipGetLastError();
 }
 
