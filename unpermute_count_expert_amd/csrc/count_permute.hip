@@ -28,35 +28,41 @@ __global__ void k_fill_i32(int32_t* __restrict__ p, int64_t n, int32_t v) {
         p[i] = v;
 }
 
+// Each wave of the block keeps its own LDS histogram (fewer conflicting
+// atomics), and each block adds its totals to counts with one global atomic
+// per expert.
 __global__ __launch_bounds__(256) void k_count(const int32_t* __restrict__ ids, int64_t num_pairs,
                                                const int32_t* __restrict__ emap, int Eg, int El,
                                                int32_t* __restrict__ counts,
                                                int32_t* __restrict__ invalid) {
-    __shared__ int h[kMaxLocalExperts];
+    constexpr int kWaves = 256 / kWave;
+    __shared__ int h[kWaves][kMaxLocalExperts];
     __shared__ int bad;
-    for (int e = threadIdx.x; e < El; e += blockDim.x) h[e] = 0;
+    for (int j = threadIdx.x; j < kWaves * El; j += blockDim.x) h[j / El][j % El] = 0;
     if (threadIdx.x == 0) bad = 0;
     __syncthreads();
+    int* hw = h[threadIdx.x / kWave];
     int my_bad = 0;
     auto add = [&](int id) __attribute__((always_inline)) {
         const int e = local_expert(id, emap, Eg, El);
-        if (e >= 0) atomicAdd(&h[e], 1);
+        if (e >= 0) atomicAdd(&hw[e], 1);
         my_bad += (id < -1 || id >= Eg) ? 1 : 0;
     };
     // 16-byte loads of four ids, four loads in flight per lane before the
     // LDS atomics that consume them
+    constexpr int kLoads = 4;
     const int4* ids4 = reinterpret_cast<const int4*>(ids);
     const int64_t nvec = num_pairs / 4;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t v0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; v0 < nvec; v0 += 4 * stride) {
-        int4 q[4];
+    for (int64_t v0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; v0 < nvec; v0 += kLoads * stride) {
+        int4 q[kLoads];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < kLoads; ++u) {
             const int64_t v = v0 + u * stride;
             q[u] = v < nvec ? ids4[v] : int4{-1, -1, -1, -1};
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < kLoads; ++u) {
             add(q[u].x);
             add(q[u].y);
             add(q[u].z);
@@ -67,8 +73,12 @@ __global__ __launch_bounds__(256) void k_count(const int32_t* __restrict__ ids, 
         add(ids[f]);
     if (my_bad) atomicAdd(&bad, my_bad);
     __syncthreads();
-    for (int e = threadIdx.x; e < El; e += blockDim.x)
-        if (h[e]) atomicAdd(&counts[e], h[e]);
+    for (int e = threadIdx.x; e < El; e += blockDim.x) {
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) c += h[w][e];
+        if (c) atomicAdd(&counts[e], c);
+    }
     if (threadIdx.x == 0 && invalid && bad) atomicAdd(invalid, bad);
 }
 
@@ -281,8 +291,10 @@ hipError_t launch_count(const int32_t* ids, int64_t num_pairs, const int32_t* em
     k_fill_i32<<<1, 256, 0, s>>>(counts, El, 0);
     if (invalid) k_fill_i32<<<1, 64, 0, s>>>(invalid, 1, 0);
     if (num_pairs > 0) {
-        int64_t blocks = (num_pairs + 256 * 8 - 1) / (256 * 8);
-        if (blocks > 2048) blocks = 2048;
+        // few enough blocks that the per-block flush of the histogram (one
+        // global atomic per expert per block) stays small next to the reads
+        int64_t blocks = (num_pairs + 256 * 32 - 1) / (256 * 32);
+        if (blocks > 1024) blocks = 1024;
         k_count<<<(unsigned)blocks, 256, 0, s>>>(ids, num_pairs, emap, Eg, El, counts, invalid);
     }
     return hipGetLastError();
