@@ -293,8 +293,8 @@ hipError_t launch_count(const int32_t* ids, int64_t num_pairs, const int32_t* em
     if (num_pairs > 0) {
         // few enough blocks that the per-block flush of the histogram (one
         // global atomic per expert per block) stays small next to the reads
-        int64_t blocks = (num_pairs + 256 * 32 - 1) / (256 * 32);
-        if (blocks > 1024) blocks = 1024;
+        int64_t blocks = (num_pairs + 256 * 16 - 1) / (256 * 16);
+        if (blocks > 512) blocks = 512;
         k_count<<<(unsigned)blocks, 256, 0, s>>>(ids, num_pairs, emap, Eg, El, counts, invalid);
     }
     return hipGetLastError();
