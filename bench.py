@@ -10,7 +10,8 @@ already resident in HBM.
 Prints one JSON line: tokens/s for the layer (steps back to back), the step
 time distribution warm and cold (caches flushed before each step), per-op
 times measured in place (median, p10, p90, and cold), GEMM TFLOP/s, per-op
-algorithmic GB/s, the roofline of the dominant kernel (GEMM w13), the count
+algorithmic GB/s (and the GEMM w13 fused with the SiLU-mul requant, timed
+on the same buffers), the roofline of the dominant kernel (GEMM w13), the count
 on a 2^24-pair case, measured HBM ceilings, and the CPU oracle timed on a
 bounded sample of the same workload.
 """
@@ -105,7 +106,7 @@ def per_op_times(layer, d, on_input, iters, stream, only=None, flush=None):
     only it is launched repeatedly (so a profiler sees no other launch of the
     same kernel).  Returns {op: [ms per pass]}."""
     b = StepBuffers(layer, d["x"].shape[0], d["ids"].shape[1])
-    ops = step_ops(layer, d["x"], d["ids"], d["w"], on_input, b)
+    ops = step_ops(layer, d["x"], d["ids"], d["w"], on_input, b, fused=(only == "gemm_w13_act"))
     names = list(ops)
     if only is not None:
         names = names[:names.index(only) + 1]
@@ -169,6 +170,9 @@ def algorithmic(cfg, counts: np.ndarray, R: int):
         "input_quant": 2 * M * K + M * K + 4 * M * K / 128,
         "permute": M * K + 4 * M * K / 128 + P * K + 4 * P * K / 128 + 8 * M * T + 4 * R,
         "gemm_w13": P * K + Ene * 2 * N * K + 4 * P * N + 4 * P * K / 128 + 4 * Ene * (2 * N // 128) * (K // 128),
+        # fused with the SiLU-mul requant: h never reaches memory
+        "gemm_w13_act": P * K + Ene * 2 * N * K + P * N + 4 * P * N / 128 + 4 * P * K / 128
+                        + 4 * Ene * (2 * N // 128) * (K // 128),
         "silu_mul_quant": 4 * P * N + P * N + 4 * P * N / 128,
         "gemm_w2": P * N + Ene * K * N + 2 * P * K + 4 * P * N / 128 + 4 * Ene * (K // 128) * (N // 128),
         "unpermute": 2 * P * K + 8 * M * T + 2 * M * K,
@@ -222,7 +226,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--profile-op", default=None,
                     help="time only this op (input_quant, count, permute, gemm_w13, silu_mul_quant, "
-                         "gemm_w2, unpermute) or 'copy'; for profiler runs")
+                         "gemm_w2, unpermute, or gemm_w13_act: the fused variant) or 'copy'; for profiler runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -280,6 +284,7 @@ def main():
 
     ops, counts, R = per_op_times(layer, d, on_input, args.op_iters, stream)
     ops_cold, _, _ = per_op_times(layer, d, on_input, args.op_iters, stream, flush=flush)
+    fused, _, _ = per_op_times(layer, d, on_input, args.op_iters, stream, only="gemm_w13_act")
     P, Ene, g1f, g2f, by = algorithmic(cfg, counts, R)
     ops_out = {}
     for name in ops:
@@ -287,7 +292,7 @@ def main():
         t = st["median"]
         rec = {"ms": t, "p10": st["p10"], "p90": st["p90"], "GB/s": round(by[name] / (t * 1e-3) / 1e9, 1)}
         rec["hbm_frac"] = round(rec["GB/s"] / PEAK_HBM_GBS, 4)
-        if name == "gemm_w13":
+        if name in ("gemm_w13", "gemm_w13_act"):
             rec["TFLOP/s"] = round(g1f / (t * 1e-3) / 1e12, 1)
         if name == "gemm_w2":
             rec["TFLOP/s"] = round(g2f / (t * 1e-3) / 1e12, 1)
@@ -295,6 +300,10 @@ def main():
         rec["cold_ms"] = tc
         rec["cold_GB/s"] = round(by[name] / (tc * 1e-3) / 1e9, 1)
         ops_out[name] = rec
+    tf = fused["gemm_w13_act"][0]
+    ops_out["gemm_w13_act (fused variant, not on the forward path)"] = {
+        "ms": round(tf, 5), "GB/s": round(by["gemm_w13_act"] / (tf * 1e-3) / 1e9, 1),
+        "TFLOP/s": round(g1f / (tf * 1e-3) / 1e12, 1)}
     t_g1 = stats(ops["gemm_w13"])["median"]
     achieved = g1f / (t_g1 * 1e-3) / 1e12
     t_g2 = stats(ops["gemm_w2"])["median"]
@@ -318,7 +327,7 @@ def main():
                                f"topk={cfg.topk} routing={cfg.routing} on_input={on_input}",
                    "M": cfg.M, "K": cfg.K, "N": cfg.N, "experts": cfg.El, "topk": cfg.topk,
                    "chunk_size": cfg.chunk_size, "align": cfg.align, "pairs": P, "padded_rows": R},
-        "roofline": {"bound": "mfma", "kernel": "grouped GEMM w13 (k_grouped_gemm)",
+        "roofline": {"bound": "mfma", "kernel": "grouped GEMM w13 (k_grouped_gemm<false>)",
                      "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic},
         "step": {"warm": wst, "cold": cst, "cold_tokens/s": round(cfg.M / (cst["median"] * 1e-3), 1),

@@ -135,6 +135,25 @@ int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const uint8_t* w, c
                          int64_t cap_rows, int32_t n_out, int32_t k_in, uint16_t* out,
                          void* stream);
 
+/* The gate/up grouped GEMM fused with SiLU-and-mul and the per-token-group
+ * requant: moe_grouped_gemm_fp8 on w13 followed by moe_act_quant in
+ * MOE_ACT_SILU_MUL mode, with the same results bit for bit, but without
+ * writing h [cap_rows, 2N] to memory.  For every valid row r (as in
+ * moe_grouped_gemm_fp8) and group j of 128 columns of N:
+ *   h   = bf16(GEMM(a, w13)) over the 2N outputs (gate = columns [0, N),
+ *         up = [N, 2N)),
+ *   act = bf16(silu(h[r, c]) * h[r, N + c]),
+ *   q_s[r, j] = d/448, q[r, c] = e4m3(act * (448/d)), d = max(amax|act|, 1e-10).
+ * a [cap_rows,k_in] e4m3, a_s [cap_rows,k_in/128] f32, w13 [El,2N,k_in]
+ * e4m3, w13_s [El,2N/128,k_in/128] f32, q [cap_rows,N] e4m3,
+ * q_s [cap_rows,N/128] f32; rows that are not valid are not written.
+ * N: positive multiple of 128 up to 32768; k_in: positive multiple of 128
+ * up to 65536 (MOE_ERR_SHAPE otherwise). */
+int moe_grouped_gemm_fp8_act_quant(const uint8_t* a, const float* a_s, const uint8_t* w13,
+                                   const float* w13_s, const int32_t* expert_offsets,
+                                   const int32_t* counts, int32_t El, int64_t cap_rows, int32_t N,
+                                   int32_t k_in, uint8_t* q, float* q_s, void* stream);
+
 /* Per-token-group (1x128) fp8 quantisation.
  *   MOE_ACT_IDENTITY: v = in[r, :n]                        (in is [rows, n])
  *   MOE_ACT_SILU_MUL: v = bf16(silu(in[r, :n]) * in[r, n:2n]) (in is [rows, 2n])

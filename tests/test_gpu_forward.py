@@ -107,6 +107,18 @@ def check_layer(cfg, on_input, n_sample_rows=64, n_sample_tokens=48):
     np.testing.assert_array_equal(g["act_q"][rows], q)
     np.testing.assert_array_equal(g["act_s"][rows], s)
 
+    # -- GEMM w13 fused with the SiLU-mul requant: the same bits as the chain
+    #    (h never leaves the kernel), on every valid row
+    fq = filled(tuple(b.act_q.shape), torch.uint8, 0xA5)
+    fs = filled(tuple(b.act_s.shape), torch.float32, -7.0)
+    moe._lib.moe_grouped_gemm_fp8_act_quant(b.a_perm, b.a_perm_s, layer.w13, layer.w13_s, b.offsets, b.counts,
+                                            fq, fs)
+    fq, fs = host(fq), host(fs)
+    np.testing.assert_array_equal(fq[rows], g["act_q"][rows])
+    np.testing.assert_array_equal(fs[rows], g["act_s"][rows])
+    pad = np.setdiff1d(np.arange(fq.shape[0]), rows)
+    assert (fq[pad] == 0xA5).all() and (fs[pad] == -7.0).all(), "fused GEMM wrote a padding row"
+
     # -- GEMM w2 on the GPU's act_q, sampled rows
     y_ref = oracle.gemm_rows(g["act_q"][sr], g["act_s"][sr], se, inp.w2, inp.w2_s)
     y_abs = oracle.gemm_rows(g["act_q"][sr] & 0x7F, g["act_s"][sr], se, inp.w2 & 0x7F, inp.w2_s)

@@ -37,7 +37,8 @@ class MoeProblem(C.Structure):
 
 EXPORTS = ["moe_status_string", "moe_last_error", "moe_max_rows", "moe_forward_workspace_size",
            "moe_permute_workspace_size", "moe_count", "moe_permute", "moe_grouped_gemm_fp8",
-           "moe_act_quant", "moe_unpermute_weight_reduce", "moe_forward_chunked"]
+           "moe_grouped_gemm_fp8_act_quant", "moe_act_quant", "moe_unpermute_weight_reduce",
+           "moe_forward_chunked"]
 
 _lib = None
 
@@ -59,6 +60,7 @@ def load() -> C.CDLL:
         L.moe_permute.argtypes = [P, P, P, P, I32, I64, I32, I32, P, I32, I32, I32, I64,
                                   P, P, P, P, P, P, P, SZ, P]
         L.moe_grouped_gemm_fp8.argtypes = [P, P, P, P, P, P, I32, I64, I32, I32, P, P]
+        L.moe_grouped_gemm_fp8_act_quant.argtypes = [P, P, P, P, P, P, I32, I64, I32, I32, P, P, P]
         L.moe_act_quant.argtypes = [P, I64, I32, I32, P, P, I32, P, P, P]
         L.moe_unpermute_weight_reduce.argtypes = [P, I64, P, P, I64, I32, I32, I32, P, P]
         L.moe_forward_chunked.argtypes = [C.POINTER(MoeProblem), P, P, P, P, P, P, P, P, P, P, SZ,
@@ -130,6 +132,15 @@ def moe_grouped_gemm_fp8(a, a_s, w, w_s, expert_offsets, counts, out, stream=Non
     _check(load().moe_grouped_gemm_fp8(_ptr(a), _ptr(a_s), _ptr(w), _ptr(w_s), _ptr(expert_offsets),
                                        _ptr(counts), El, cap_rows, n_out, k_in, _ptr(out),
                                        _stream(stream)), "moe_grouped_gemm_fp8")
+
+
+def moe_grouped_gemm_fp8_act_quant(a, a_s, w13, w13_s, expert_offsets, counts, q, q_s, stream=None):
+    cap_rows, k_in = a.shape
+    El, two_n, _ = w13.shape
+    _check(load().moe_grouped_gemm_fp8_act_quant(_ptr(a), _ptr(a_s), _ptr(w13), _ptr(w13_s),
+                                                 _ptr(expert_offsets), _ptr(counts), El, cap_rows, two_n // 2,
+                                                 k_in, _ptr(q), _ptr(q_s), _stream(stream)),
+           "moe_grouped_gemm_fp8_act_quant")
 
 
 def moe_act_quant(inp, n, mode, q, q_s, expert_offsets=None, counts=None, El=0, stream=None):

@@ -268,6 +268,33 @@ int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const uint8_t* w, c
     return MOE_OK;
 }
 
+int moe_grouped_gemm_fp8_act_quant(const uint8_t* a, const float* a_s, const uint8_t* w13,
+                                   const float* w13_s, const int32_t* expert_offsets,
+                                   const int32_t* counts, int32_t El, int64_t cap_rows, int32_t N,
+                                   int32_t k_in, uint8_t* q, float* q_s, void* stream) {
+    REQUIRE(El >= 1 && El <= moe::kMaxLocalExperts, MOE_ERR_SHAPE, "El=%d outside [1,1024]", El);
+    REQUIRE(N > 0 && N % moe::kGroup == 0 && N <= 32768, MOE_ERR_SHAPE,
+            "N=%d is not a positive multiple of 128 up to 32768", N);
+    REQUIRE(k_in > 0 && k_in % moe::kGroup == 0 && k_in <= 65536, MOE_ERR_SHAPE,
+            "k_in=%d is not a positive multiple of 128 up to 65536", k_in);
+    REQUIRE(cap_rows >= 0 && cap_rows < (int64_t(1) << 31), MOE_ERR_SHAPE, "cap_rows=%lld", (long long)cap_rows);
+    if (cap_rows == 0) return MOE_OK;
+    REQUIRE_PTR(a);
+    REQUIRE_PTR(a_s);
+    REQUIRE_PTR(w13);
+    REQUIRE_PTR(w13_s);
+    REQUIRE_PTR(expert_offsets);
+    REQUIRE_PTR(counts);
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(q_s);
+    int cus = 0;
+    int st = check_device(&cus);
+    if (st) return st;
+    HIP_OK(moe::launch_grouped_gemm_act(a, a_s, w13, w13_s, expert_offsets, counts, El, cap_rows, N, k_in, q,
+                                        q_s, cus, static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
 int moe_act_quant(const uint16_t* in, int64_t rows, int32_t n, int32_t mode,
                   const int32_t* expert_offsets, const int32_t* counts, int32_t El, uint8_t* q,
                   float* q_s, void* stream) {

@@ -210,15 +210,28 @@ struct TileWalk {
     }
 };
 
+// KACT = false: out[r, n] = bf16(GEMM), n < n_out.
+// KACT = true (the gate/up GEMM fused with SiLU-and-mul and requant): n_out =
+// 2N, w rows [0, N) are the gate and [N, 2N) the up projection; for every
+// valid row r and act column c < N,
+//   h = bf16(GEMM(r, c)), h' = bf16(GEMM(r, N + c)),
+//   act = bf16(silu(h) * h'), then per 1x128 group of act: amax, scale and
+//   e4m3 codes exactly as the SiLU-mul requant of act_quant.hip,
+// written to q [rows, N] and q_s [rows, N/128].  A tile then holds 128 gate
+// and the matching 128 up columns, and each lane owns matched gate/up pairs,
+// so no intermediate h is stored.
+template <bool KACT>
 __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
     const uint8_t* __restrict__ a, const float* __restrict__ a_s, const uint8_t* __restrict__ w,
     const float* __restrict__ w_s, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ counts, int El, int64_t cap_rows, int n_out, int k_in,
-    uint16_t* __restrict__ out) {
+    uint16_t* __restrict__ out, uint8_t* __restrict__ q, float* __restrict__ q_s) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStage];
     __shared__ __attribute__((aligned(16))) float sAs[kStages][BM];   // [stage][row]
     __shared__ int s_tpre[kMaxLocalExperts + 1];
     __shared__ int s_wsum[kWaves];
+    __shared__ float s_amax[KACT ? 4 : 1][BM];   // per-wave-column partial group maxima
+    const int n_half = n_out / 2;                 // N when KACT
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -294,12 +307,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
     // of B (four), and the scales of rows 16w..16w+15 (lanes 0..15).
     const int rA0 = (wave * 2) * 8 + (lane >> 3), rA1 = rA0 + 8;
     const int cA0 = swz_pos(lane & 7, rA0), cA1 = swz_pos(lane & 7, rA1);   // the swizzle is an involution
+    // B: LDS row R holds weight row nB of the tile.  Plain: within each
+    // 64-row quarter, row 4j+b goes to 16b+j, so lane j of MFMA column block
+    // b computes output column 4j+b.  KACT: in the quarter of wave column wn,
+    // MFMA blocks 0/1 are gate columns 2j / 2j+1 and blocks 2/3 the up
+    // columns 2j / 2j+1 of the same 32-column slice; waves with even index
+    // fill gate rows and odd ones up rows, nB counted from their half.
     int nB[4], cB[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int R = (wave * 4 + q) * 8 + (lane >> 3);
-        nB[q] = b_row_inv(R);
-        cB[q] = swz_pos(lane & 7, R);
+    for (int qq = 0; qq < 4; ++qq) {
+        const int R = (wave * 4 + qq) * 8 + (lane >> 3);
+        nB[qq] = KACT ? (R >> 6) * 32 + 2 * (R & 15) + ((R >> 4) & 1) : b_row_inv(R);
+        cB[qq] = swz_pos(lane & 7, R);
     }
     const int rS = wave * 16 + (lane & 15);
     const uint32_t lds_smem = (uint32_t)(uintptr_t)smem;
@@ -318,7 +337,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
 #define MOE_DMA_OFFSETS()                                                             \
     do {                                                                              \
         const int last_ = max(dT.row_end - 1 - dT.m0, 0);                             \
-        const int nlast_ = min(BN, n_out - dT.n0) - 1;                                \
+        const int nlast_ = KACT ? 127 : min(BN, n_out - dT.n0) - 1;                   \
         voA0 = (uint32_t)(min(rA0, last_) * k_in + cA0 * 16);                         \
         voA1 = (uint32_t)(min(rA1, last_) * k_in + cA1 * 16);                         \
         voB0 = (uint32_t)(min(nB[0], nlast_) * k_in + cB[0] * 16);                    \
@@ -331,7 +350,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
 #define MOE_DMA_NEXT()                                                                \
     do {                                                                              \
         const uint8_t* sa_ = a + ((int64_t)dT.m0 * k_in + d_g * BK);                  \
-        const uint8_t* sb_ = w + (((int64_t)dT.e * n_out + dT.n0) * k_in + d_g * BK); \
+        const int64_t brow_ = KACT ? (int64_t)((wave & 1) ? n_half : 0) + (dT.n0 >> 1)  \
+                                   : (int64_t)dT.n0;                                  \
+        const uint8_t* sb_ = w + (((int64_t)dT.e * n_out + brow_) * k_in + d_g * BK); \
         const float* ss_ = a_s + ((int64_t)dT.m0 * kg + d_g);                         \
         const uint32_t base_ = lds_smem + d_slot * kStage;                            \
         dma16(base_ + (wave * 2) * 1024, voA0, sa_);                                  \
@@ -361,9 +382,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
     TileCursor cur;
     walk.start(cur, t_lo);
     while (cur.valid) {
-        const int n_valid = min(BN, n_out - cur.n0);
+        const int n_valid = KACT ? BN : min(BN, n_out - cur.n0);
         const bool wave_has_rows = (cur.m0 + wm * 64) < cur.row_end && wn * 64 < n_valid;
-        const int64_t ws_row = ((int64_t)cur.e * nb128 + min(cur.n0 / 128 + (wn >> 1), nb128 - 1)) * kg;
+        // weight block-scale rows: plain, the 128-column block of this wave;
+        // KACT, the gate block (MFMA blocks 0/1) and the up block (2/3)
+        const int64_t ws_row = KACT ? ((int64_t)cur.e * nb128 + (cur.n0 >> 8)) * kg
+                                    : ((int64_t)cur.e * nb128 + min(cur.n0 / 128 + (wn >> 1), nb128 - 1)) * kg;
+        const int64_t ws_row_up = ws_row + (int64_t)(n_half / 128) * kg;
         v4f acc[4][4];
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
@@ -379,6 +404,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
                 const uint8_t* base = smem + slot * kStage;
                 const float* scs = &sAs[slot][wm * 64 + (lane >> 4) * 4];
                 const float ws = w_s[ws_row + g];
+                const float ws_up = KACT ? w_s[ws_row_up + g] : ws;
                 v8i bf[4];
 #pragma unroll
                 for (int ni = 0; ni < 4; ++ni) bf[ni] = frag(base, offB[ni]);
@@ -398,9 +424,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
                         for (int ni = 0; ni < 4; ++ni) p[(mi + 1) & 1][ni] = mfma_fp8(af, bf[ni]);
                     }
                     const v4f sa4 = *reinterpret_cast<const v4f*>(scs + mi * 16);
-                    const v4f sc = {sa4.x * ws, sa4.y * ws, sa4.z * ws, sa4.w * ws};
+                    const v4f sc_lo = {sa4.x * ws, sa4.y * ws, sa4.z * ws, sa4.w * ws};
+                    v4f sc_hi = sc_lo;
+                    if (KACT) sc_hi = v4f{sa4.x * ws_up, sa4.y * ws_up, sa4.z * ws_up, sa4.w * ws_up};
 #pragma unroll
                     for (int ni = 0; ni < 4; ++ni) {
+                        const v4f sc = ni < 2 ? sc_lo : sc_hi;
                         const v4f pr = p[mi & 1][ni];
                         acc[mi][ni].x = __builtin_fmaf(sc.x, pr.x, acc[mi][ni].x);
                         acc[mi][ni].y = __builtin_fmaf(sc.y, pr.y, acc[mi][ni].y);
@@ -412,19 +441,88 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
             slot = slot == kStages - 1 ? 0 : slot + 1;
         }
 
-        // ---- epilogue: each lane owns 4 adjacent columns of 16 rows --------
-        if (wave_has_rows) {
-            const int col = cur.n0 + wn * 64 + 4 * fr;
+        if (!KACT) {
+            // ---- epilogue: each lane owns 4 adjacent columns of 16 rows ----
+            if (wave_has_rows) {
+                const int col = cur.n0 + wn * 64 + 4 * fr;
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int row = cur.m0 + wm * 64 + mi * 16 + (lane >> 4) * 4 + v;
+                        if (row < cur.row_end) {
+                            v2i qv;
+                            qv.x = (int)f32x2_to_bf16x2(acc[mi][0][v], acc[mi][1][v]);
+                            qv.y = (int)f32x2_to_bf16x2(acc[mi][2][v], acc[mi][3][v]);
+                            *reinterpret_cast<v2i*>(out + (int64_t)row * n_out + col) = qv;
+                        }
+                    }
+            }
+        } else {
+            // ---- epilogue: SiLU-and-mul and per-128 requant ----------------
+            // This lane holds, for 16 rows, act columns 2fr and 2fr+1 of the
+            // wave's 32-column slice (gate in blocks 0/1, up in 2/3).  The
+            // group of a row is the tile's 128 act columns, spread over the
+            // 16 lanes of a row quad and the 4 waves of the same wm.
+            const int j = cur.n0 >> 8;   // act column block
+            float act[4][4][2];
+            float amax[4][4];
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const int row = cur.m0 + wm * 64 + mi * 16 + (lane >> 4) * 4 + v;
-                    if (row < cur.row_end) {
-                        v2i q;
-                        q.x = (int)f32x2_to_bf16x2(acc[mi][0][v], acc[mi][1][v]);
-                        q.y = (int)f32x2_to_bf16x2(acc[mi][2][v], acc[mi][3][v]);
-                        *reinterpret_cast<v2i*>(out + (int64_t)row * n_out + col) = q;
+                    const uint32_t hg = f32x2_to_bf16x2(acc[mi][0][v], acc[mi][1][v]);
+                    const uint32_t hu = f32x2_to_bf16x2(acc[mi][2][v], acc[mi][3][v]);
+                    const float g0 = __uint_as_float(hg << 16), g1 = __uint_as_float(hg & 0xffff0000u);
+                    const float u0 = __uint_as_float(hu << 16), u1 = __uint_as_float(hu & 0xffff0000u);
+                    const float p0 = (g0 / (1.0f + exp_pinned(-g0))) * u0;
+                    const float p1 = (g1 / (1.0f + exp_pinned(-g1))) * u1;
+                    const uint32_t pk = f32x2_to_bf16x2(p0, p1);   // act is rounded to bf16
+                    act[mi][v][0] = __uint_as_float(pk << 16);
+                    act[mi][v][1] = __uint_as_float(pk & 0xffff0000u);
+                    // largest non-NaN magnitude, by compare-select
+                    float m = 0.0f;
+                    const float a0 = __builtin_fabsf(act[mi][v][0]), a1 = __builtin_fabsf(act[mi][v][1]);
+                    m = a0 > m ? a0 : m;
+                    m = a1 > m ? a1 : m;
+#pragma unroll
+                    for (int d = 1; d < 16; d <<= 1) {
+                        const float o = __shfl_xor(m, d, kWave);
+                        m = o > m ? o : m;
+                    }
+                    amax[mi][v] = m;
+                }
+            if (fr == 0) {
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) s_amax[wn][wm * 64 + mi * 16 + (lane >> 4) * 4 + v] = amax[mi][v];
+            }
+            // publish the partial maxima (LDS only: the DMAs in flight for
+            // the next steps are not waited for)
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            const int ng = n_half / 128;
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int rl = wm * 64 + mi * 16 + (lane >> 4) * 4 + v;
+                    float m = s_amax[0][rl];
+#pragma unroll
+                    for (int ww = 1; ww < 4; ++ww) {
+                        const float o = s_amax[ww][rl];
+                        m = o > m ? o : m;
+                    }
+                    const float dd = __builtin_fmaxf(m, 1e-10f);
+                    const float inv = 448.0f / dd;
+                    // |act * inv| <= 448 (1 + 2^-23) unless NaN: dd >= every |act| of the group
+                    const uint32_t codes =
+                        f32x4_to_e4m3_bounded(act[mi][v][0] * inv, act[mi][v][1] * inv, 0.0f, 0.0f);
+                    const int row = cur.m0 + rl;
+                    if (wave_has_rows && row < cur.row_end) {
+                        *reinterpret_cast<uint16_t*>(q + (int64_t)row * n_half + j * 128 + wn * 32 + 2 * fr) =
+                            (uint16_t)codes;
+                        if (wn == 0 && fr == 0) q_s[(int64_t)row * ng + j] = dd / 448.0f;
                     }
                 }
         }
@@ -436,18 +534,37 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
 
 }  // namespace
 
-hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_s, const uint8_t* w,
-                               const float* w_s, const int32_t* offsets, const int32_t* counts,
-                               int El, int64_t cap_rows, int n_out, int k_in, uint16_t* out,
-                               int num_cus, hipStream_t s) {
+namespace {
+
+int64_t gemm_grid(int64_t cap_rows, int El, int n_out, int num_cus) {
     const int64_t ntn = (n_out + BN - 1) / BN;
     const int64_t bound = ((cap_rows + BM - 1) / BM + El) * ntn;
     int64_t grid = num_cus;            // one 8-wave block per CU (150 KB of LDS)
     if (bound < grid) grid = bound;
     grid = ((grid + 7) / 8) * 8;
     if (grid < 8) grid = 8;
-    k_grouped_gemm<<<(unsigned)grid, kThreads, 0, s>>>(a, a_s, w, w_s, offsets, counts, El, cap_rows,
-                                                        n_out, k_in, out);
+    return grid;
+}
+
+}  // namespace
+
+hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_s, const uint8_t* w,
+                               const float* w_s, const int32_t* offsets, const int32_t* counts,
+                               int El, int64_t cap_rows, int n_out, int k_in, uint16_t* out,
+                               int num_cus, hipStream_t s) {
+    const int64_t grid = gemm_grid(cap_rows, El, n_out, num_cus);
+    k_grouped_gemm<false><<<(unsigned)grid, kThreads, 0, s>>>(a, a_s, w, w_s, offsets, counts, El, cap_rows,
+                                                               n_out, k_in, out, nullptr, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm_act(const uint8_t* a, const float* a_s, const uint8_t* w13,
+                                   const float* w13_s, const int32_t* offsets, const int32_t* counts,
+                                   int El, int64_t cap_rows, int N, int k_in, uint8_t* q, float* q_s,
+                                   int num_cus, hipStream_t s) {
+    const int64_t grid = gemm_grid(cap_rows, El, 2 * N, num_cus);
+    k_grouped_gemm<true><<<(unsigned)grid, kThreads, 0, s>>>(a, a_s, w13, w13_s, offsets, counts, El, cap_rows,
+                                                              2 * N, k_in, nullptr, q, q_s);
     return hipGetLastError();
 }
 

@@ -43,6 +43,13 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_s, const uint8_t
                                int El, int64_t cap_rows, int n_out, int k_in, uint16_t* out,
                                int num_cus, hipStream_t s);
 
+// The gate/up GEMM (w13 [El, 2N, k_in]) fused with SiLU-and-mul and the
+// per-128 requant: writes q [cap_rows, N] e4m3 and q_s [cap_rows, N/128].
+hipError_t launch_grouped_gemm_act(const uint8_t* a, const float* a_s, const uint8_t* w13,
+                                   const float* w13_s, const int32_t* offsets, const int32_t* counts,
+                                   int El, int64_t cap_rows, int N, int k_in, uint8_t* q, float* q_s,
+                                   int num_cus, hipStream_t s);
+
 // ---- unpermute ----------------------------------------------------------------
 hipError_t launch_unpermute(const uint16_t* y, int64_t y_rows, const int32_t* inv_perm,
                             const float* topk_w, int64_t Mc, int K, int topk, int apply_on_input, uint16_t* out,

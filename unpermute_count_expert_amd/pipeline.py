@@ -1,8 +1,11 @@
 """The layer as a sequence of separate C-ABI calls, with every intermediate
 kept in its own buffer (for inspection, per-op timing and op-by-op checks).
 
-moe_forward_chunked runs the same kernels in the same order on one reused
-workspace; this form trades memory for visibility.
+With fused=False the ops are exactly the kernels moe_forward_chunked runs,
+in its order (the gate/up GEMM writes h, a separate SiLU-mul requant
+follows); with fused=True the gate/up GEMM is the one fused with the SiLU-mul
+requant (moe_grouped_gemm_fp8_act_quant) and h never reaches memory.  The forward call runs on one reused workspace; this form trades
+memory for visibility.
 """
 from __future__ import annotations
 
@@ -33,7 +36,7 @@ class StepBuffers:
         self.count_only = e((El,), i32)
 
 
-def step_ops(layer, x, topk_ids, topk_weights, apply_on_input: int, b: StepBuffers):
+def step_ops(layer, x, topk_ids, topk_weights, apply_on_input: int, b: StepBuffers, fused: bool = False):
     """Ordered {name: thunk}; running them in order computes the layer into b.out."""
     Eg, El, K, N, A = layer.Eg, layer.El, layer.K, layer.N, layer.align
     emap = layer.expert_map
@@ -43,10 +46,15 @@ def step_ops(layer, x, topk_ids, topk_weights, apply_on_input: int, b: StepBuffe
     ops["permute"] = lambda: _lib.moe_permute(b.a_q, b.a_s, topk_ids, topk_weights, apply_on_input, emap, Eg,
                                               El, A, b.cap, b.a_perm, b.a_perm_s, b.counts, b.offsets,
                                               b.inv_perm, b.row_src, b.permute_ws)
-    ops["gemm_w13"] = lambda: _lib.moe_grouped_gemm_fp8(b.a_perm, b.a_perm_s, layer.w13, layer.w13_s,
-                                                        b.offsets, b.counts, b.h)
-    ops["silu_mul_quant"] = lambda: _lib.moe_act_quant(b.h, N, _lib.MOE_ACT_SILU_MUL, b.act_q, b.act_s,
-                                                       b.offsets, b.counts, El)
+    if fused:
+        ops["gemm_w13_act"] = lambda: _lib.moe_grouped_gemm_fp8_act_quant(b.a_perm, b.a_perm_s, layer.w13,
+                                                                          layer.w13_s, b.offsets, b.counts,
+                                                                          b.act_q, b.act_s)
+    else:
+        ops["gemm_w13"] = lambda: _lib.moe_grouped_gemm_fp8(b.a_perm, b.a_perm_s, layer.w13, layer.w13_s,
+                                                            b.offsets, b.counts, b.h)
+        ops["silu_mul_quant"] = lambda: _lib.moe_act_quant(b.h, N, _lib.MOE_ACT_SILU_MUL, b.act_q, b.act_s,
+                                                           b.offsets, b.counts, El)
     ops["gemm_w2"] = lambda: _lib.moe_grouped_gemm_fp8(b.act_q, b.act_s, layer.w2, layer.w2_s, b.offsets,
                                                        b.counts, b.y)
     ops["unpermute"] = lambda: _lib.moe_unpermute_weight_reduce(b.y, b.inv_perm, topk_weights,
@@ -54,9 +62,10 @@ def step_ops(layer, x, topk_ids, topk_weights, apply_on_input: int, b: StepBuffe
     return ops
 
 
-def run_steps(layer, x, topk_ids, topk_weights, apply_on_input: int = 0, b: StepBuffers = None):
+def run_steps(layer, x, topk_ids, topk_weights, apply_on_input: int = 0, b: StepBuffers = None,
+              fused: bool = False):
     if b is None:
         b = StepBuffers(layer, x.shape[0], topk_ids.shape[1], x.device)
-    for fn in step_ops(layer, x, topk_ids, topk_weights, apply_on_input, b).values():
+    for fn in step_ops(layer, x, topk_ids, topk_weights, apply_on_input, b, fused).values():
         fn()
     return b
