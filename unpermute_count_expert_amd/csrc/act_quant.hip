@@ -49,19 +49,43 @@ __global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restri
     const int ng = n / kGroup;
     const int64_t total = rows * ng;
     const int sub = threadIdx.x & (kLanesPerGroup - 1);
-    for (int64_t grp = (int64_t)blockIdx.x * kGroupsPerBlock + threadIdx.x / kLanesPerGroup; grp < total;
-         grp += (int64_t)gridDim.x * kGroupsPerBlock) {
+    // each block takes a contiguous range of groups, 16 at a time, so a
+    // thread's rows advance slowly and the expert segment found for one row
+    // is reused for the next ones
+    const int64_t per_block = ((total + gridDim.x - 1) / gridDim.x + kGroupsPerBlock - 1) / kGroupsPerBlock *
+                              kGroupsPerBlock;
+    const int64_t g_lo = (int64_t)blockIdx.x * per_block;
+    const int64_t g_hi = g_lo + per_block < total ? g_lo + per_block : total;
+    int64_t seg_lo = 0, seg_hi = -1;   // rows [seg_lo, seg_hi) share one validity, seg_valid
+    bool seg_valid = true;
+    for (int64_t grp = g_lo + threadIdx.x / kLanesPerGroup; grp < g_hi; grp += kGroupsPerBlock) {
         const int64_t r = grp / ng;
         const int gi = (int)(grp - r * ng);
         bool valid = true;
         if (masked) {
-            // the expert segment holding row r: largest e with s_off[e] <= r
-            int lo = 0, hi = El;  // answer in [0, El]
-            while (lo < hi) {
-                int mid = (lo + hi + 1) >> 1;
-                if (s_off[mid] <= r) lo = mid; else hi = mid - 1;
+            if (r < seg_lo || r >= seg_hi) {
+                // the expert segment holding row r: largest e with s_off[e] <= r
+                int lo = 0, hi = El;  // answer in [0, El]
+                while (lo < hi) {
+                    int mid = (lo + hi + 1) >> 1;
+                    if (s_off[mid] <= r) lo = mid; else hi = mid - 1;
+                }
+                if (lo < El && r < s_end[lo]) {   // valid rows of expert lo
+                    seg_lo = s_off[lo];
+                    seg_hi = s_end[lo];
+                    seg_valid = true;
+                } else if (lo < El) {             // its padding rows
+                    seg_lo = s_end[lo];
+                    seg_hi = s_off[lo + 1];
+                    seg_valid = false;
+                } else {                          // past the last segment
+                    seg_lo = s_off[El];
+                    seg_hi = INT64_MAX;
+                    seg_valid = false;
+                }
             }
-            valid = lo < El && r < s_end[lo];
+            valid = seg_valid;
+            if (!valid) continue;   // padding rows are neither read nor written
         }
         Vals8 x;
         if (MODE == MOE_ACT_IDENTITY_K) {
