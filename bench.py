@@ -12,8 +12,9 @@ time distribution warm and cold (caches flushed before each step), per-op
 times measured in place (median, p10, p90, and cold), GEMM TFLOP/s, per-op
 algorithmic GB/s (and the GEMM w13 fused with the SiLU-mul requant, timed
 on the same buffers), the roofline of the dominant kernel (GEMM w13), the count
-on a 2^24-pair case, measured HBM ceilings, and the CPU oracle timed on a
-bounded sample of the same workload.
+on a 2^24-pair case, a measured HBM copy ceiling, the CPU oracle timed on a
+bounded sample of the same workload, and (with --other-layers) short step
+timings of the other layer configurations.
 """
 from __future__ import annotations
 
@@ -203,6 +204,33 @@ def cpu_baseline(inp, on_input, target_s=15.0):
                       f"{ts:.1f} s"}
 
 
+def other_layers(names, warmup=3, steps=5):
+    """Step time of the fused forward on the other layer configurations (hot
+    routing, router weight on input, the 4096-token prefill chunk, the
+    8192-token layer in chunks of 64 with 64 of 128 experts local, and the
+    64-token profiling shape), each on its own seeded inputs."""
+    res = {}
+    stream = torch.cuda.current_stream()
+    for name in names:
+        c = gen.CONFIGS[name]
+        inp = gen.make_inputs(c)
+        emap = dev(inp.expert_map) if inp.expert_map is not None else None
+        layer = moe.MoeLayer(dev(inp.w13), dev(inp.w13_s), dev(inp.w2), dev(inp.w2_s), c.Eg, emap, c.align)
+        x, ids, w = dev(inp.x), dev(inp.topk_ids), dev(inp.topk_weights)
+        out = torch.empty((c.M, c.K), dtype=torch.int16, device="cuda:0")
+        fn = lambda: layer.forward(x, ids, w, chunk_size=c.chunk_size, apply_on_input=c.apply_router_weight_on_input,
+                                   out=out)
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ms = timed(fn, steps, stream)
+        res[name] = {"workload": f"M={c.M} chunk={c.chunk_size} K={c.K} N={c.N} E={c.El}/{c.Eg} topk={c.topk} "
+                                 f"routing={c.routing} on_input={c.apply_router_weight_on_input}",
+                     "ms_per_step": round(ms, 5), "tokens/s": round(c.M / (ms * 1e-3), 1)}
+        del layer, x, ids, w, out
+    return res
+
+
 def copy_calibration(iters):
     """A plain device copy of known size (256 MiB read + 256 MiB written),
     for scaling HBM byte counters."""
@@ -223,6 +251,8 @@ def main():
     ap.add_argument("--config", default="C5u", choices=sorted(gen.CONFIGS))
     ap.add_argument("--op-iters", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--other-layers", action="store_true",
+                    help="also time short runs of the other layer configurations")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--profile-op", default=None,
                     help="time only this op (input_quant, count, permute, gemm_w13, silu_mul_quant, "
@@ -340,6 +370,8 @@ def main():
         "wall_s_timed": round(wall, 3),
         "input_gen_s": round(t_gen, 1),
     }
+    if args.other_layers:
+        line["other_layers"] = other_layers([n for n in ("C5h", "C5u_on", "C3", "C4", "C2") if n != cfg.name])
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, on_input, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -58,19 +58,31 @@ __global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restri
     const int64_t g_hi = g_lo + per_block < total ? g_lo + per_block : total;
     int64_t seg_lo = 0, seg_hi = -1;   // rows [seg_lo, seg_hi) share one validity, seg_valid
     bool seg_valid = true;
-    for (int64_t grp = g_lo + threadIdx.x / kLanesPerGroup; grp < g_hi; grp += kGroupsPerBlock) {
-        const int64_t r = grp / ng;
-        const int gi = (int)(grp - r * ng);
+    // (row, group in row) of this thread's group, advanced by 16 groups per
+    // iteration without a division
+    int64_t grp = g_lo + threadIdx.x / kLanesPerGroup;
+    int64_t r = grp / ng;
+    int gi = (int)(grp - r * ng);
+    const int adv_r = kGroupsPerBlock / ng, adv_g = kGroupsPerBlock % ng;
+    for (; grp < g_hi; grp += kGroupsPerBlock) {
+        const int64_t r_this = r;
+        const int gi_this = gi;
+        gi += adv_g;
+        r += adv_r;
+        if (gi >= ng) {
+            gi -= ng;
+            ++r;
+        }
         bool valid = true;
         if (masked) {
-            if (r < seg_lo || r >= seg_hi) {
-                // the expert segment holding row r: largest e with s_off[e] <= r
+            if (r_this < seg_lo || r_this >= seg_hi) {
+                // the expert segment holding row r_this: largest e with s_off[e] <= r_this
                 int lo = 0, hi = El;  // answer in [0, El]
                 while (lo < hi) {
                     int mid = (lo + hi + 1) >> 1;
-                    if (s_off[mid] <= r) lo = mid; else hi = mid - 1;
+                    if (s_off[mid] <= r_this) lo = mid; else hi = mid - 1;
                 }
-                if (lo < El && r < s_end[lo]) {   // valid rows of expert lo
+                if (lo < El && r_this < s_end[lo]) {   // valid rows of expert lo
                     seg_lo = s_off[lo];
                     seg_hi = s_end[lo];
                     seg_valid = true;
@@ -89,10 +101,10 @@ __global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restri
         }
         Vals8 x;
         if (MODE == MOE_ACT_IDENTITY_K) {
-            const uint4 u = *reinterpret_cast<const uint4*>(in + r * n + gi * kGroup + sub * 8);
+            const uint4 u = *reinterpret_cast<const uint4*>(in + r_this * n + gi_this * kGroup + sub * 8);
             x = unpack_bf16x8(u);
         } else {
-            const uint16_t* base = in + r * 2 * (int64_t)n + gi * kGroup + sub * 8;
+            const uint16_t* base = in + r_this * 2 * (int64_t)n + gi_this * kGroup + sub * 8;
             const Vals8 g = unpack_bf16x8(*reinterpret_cast<const uint4*>(base));
             const Vals8 u = unpack_bf16x8(*reinterpret_cast<const uint4*>(base + n));
             float prod[8];
@@ -135,8 +147,8 @@ __global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restri
         codes.x = f32x4_to_e4m3_bounded(t[0], t[1], t[2], t[3]);
         codes.y = f32x4_to_e4m3_bounded(t[4], t[5], t[6], t[7]);
         if (valid) {
-            *reinterpret_cast<uint2*>(q + r * n + gi * kGroup + sub * 8) = codes;
-            if (sub == 0) q_s[r * ng + gi] = scale;
+            *reinterpret_cast<uint2*>(q + r_this * n + gi_this * kGroup + sub * 8) = codes;
+            if (sub == 0) q_s[r_this * ng + gi_this] = scale;
         }
     }
 }
