@@ -5,8 +5,14 @@
 //   out[r, n] = bf16( sum_g a_s[r,g] * w_s[e,n/128,g] * sum_{k in g} a[r,k] w[e,n,k] )
 //
 // Design:
-//  * 128x256 output tile per 512-thread block: 8 waves in 2 (M) x 4 (N),
-//    64x64 per wave = 4x4 MFMA 16x16x128 fp8 tiles, one block per CU.
+//  * 256x256 output tile per 512-thread block: 8 waves in 2 (M) x 4 (N),
+//    128x64 per wave = 8x4 MFMA 16x16x128 fp8 tiles, one block per CU.  The
+//    operand stream from L2 and HBM is what bounds this kernel on gfx950, so
+//    the tile is as large as the 256 VGPRs of two waves per SIMD allow: a
+//    step moves 64 KB for 16.8 MFLOP (128x256 tiles: 48 KB for 8.4), and
+//    each expert's weights are re-read by half as many m-tiles.  The fused
+//    gate/up + SiLU-mul requant variant keeps 128x256 tiles (its epilogue
+//    needs the registers).
 //  * One MFMA spans exactly one K group, so each MFMA result is a whole
 //    group's partial sum; it is scaled by a_s * w_s and folded into the fp32
 //    accumulator with one FMA per output.  The group scales are arbitrary
@@ -16,17 +22,19 @@
 //    also bounds that error.  The MFMAs of row block i+1 are issued before
 //    the promotion FMAs of row block i.
 //  * Operands move global -> LDS by LDS DMA (global_load_lds_dwordx4: each
-//    lane's 16 bytes land at M0 + 16*lane) through a ring of three 48 KB
-//    stages, so the loads of steps i+1 and i+2 are in flight while the MFMAs
-//    consume step i, with no staging registers and no LDS store
-//    instructions.  A wave waits only for its own DMAs of the step it is
+//    lane's 16 bytes land at M0 + 16*lane) through a ring of two 64 KB
+//    stages (three 48 KB stages for 128-row tiles), so the next step's loads
+//    are in flight while the MFMAs consume step i, with no staging registers
+//    and no LDS store instructions.  A wave waits only for its own DMAs of the step it is
 //    about to read (loads retire in issue order), and one barrier per step
 //    publishes every wave's.  The activation scales of a step ride in the same
 //    ring (dword DMA); the weight block scale is wave-uniform and comes
 //    through the scalar cache.
 //  * LDS rows are 128 bytes, the 16-byte chunk c of row r stored at position
-//    c ^ ((r ^ r/8) mod 8), so the 16 lanes feeding one MFMA row block read 16
-//    distinct bank groups (measured on gfx950: no conflict cycles).  A DMA
+//    c ^ (r mod 8) ^ (r/8 mod 2), so the 16 lanes feeding one MFMA row block
+//    read 16 distinct bank groups (measured on gfx950: no conflict cycles);
+//    the pattern repeats every 16 rows, so a lane's fragment addresses in
+//    the row blocks of a stage differ by constants.  A DMA
 //    writes 8 whole LDS rows, so each lane fetches the global chunk that the
 //    swizzle places at its LDS position.
 //  * Weight rows are placed so that lane j of MFMA column block b holds output
@@ -39,7 +47,7 @@
 //    8 XCDs round-robin, so XCD x walks the contiguous x-th eighth of the
 //    (expert, m-tile, n-tile) sequence and an expert's weights stay hot in
 //    that XCD's L2.  Tiles are walked without divisions, and the DMA stream
-//    runs two steps ahead across tile boundaries.
+//    runs one step (two for 128-row tiles) ahead across tile boundaries.
 //  * Row indices are clamped on the device, so even inconsistent
 //    offsets/counts cannot move an access out of bounds.
 #include "moe_device.hpp"
@@ -48,15 +56,23 @@
 namespace moe {
 namespace {
 
-constexpr int BM = 128;
 constexpr int BN = 256;
 constexpr int BK = 128;
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;   // 8: 2 along M, 4 along N
-constexpr int kStageA = BM * BK;           // bytes
-constexpr int kStage = kStageA + BN * BK;  // 48 KB
-constexpr int kStages = 3;
-constexpr int kDmaPerStep = 7;             // per wave and step: 2 A + 4 B + 1 scale
+// Tile shape by MI, the 16-row MFMA blocks per wave (the tile has 2 * 16 * MI
+// rows): MI = 8 gives 256x256 tiles with two 64 KB LDS stages, MI = 4 gives
+// 128x256 tiles with three 48 KB stages.
+template <int MI>
+struct Shape {
+    static constexpr int BM = 32 * MI;
+    static constexpr int kStageA = BM * BK;              // bytes
+    static constexpr int kStage = kStageA + BN * BK;
+    static constexpr int kStages = MI == 4 ? 3 : 2;
+    static constexpr int kADma = MI / 2;                  // 8-row A DMAs per wave and step
+    static constexpr int kDmaPerStep = kADma + 4 + 1;     // + 4 B + 1 scale
+    static constexpr int kScaleRows = 4 * MI;             // A scale rows per wave
+};
 
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -74,7 +90,7 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 }
 
 // position (0..7) of 16-byte chunk c in LDS tile row r, and its inverse
-__device__ __forceinline__ int swz_pos(int c, int r) { return c ^ ((r ^ (r >> 3)) & 7); }
+__device__ __forceinline__ int swz_pos(int c, int r) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int swz(int c, int r) { return r * 128 + (swz_pos(c, r) << 4); }
 
 // LDS row of weight row n of the tile: within each 64-row quarter, row 4j+b
@@ -89,12 +105,13 @@ __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
 }
 
-__device__ __forceinline__ v8i frag(const uint8_t* p, int off_lo) {
-    // the two 16-byte halves of a lane's 32 K-bytes: chunks 2h and 2h+1 sit
-    // at positions x and x^1 of the same row
-    const v4i lo = *reinterpret_cast<const v4i*>(p + off_lo);
-    const v4i hi = *reinterpret_cast<const v4i*>(p + (off_lo ^ 16));
-    return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+// A lane's 32 K-bytes of one MFMA operand: the two 16-byte halves (chunks
+// 2h and 2h+1 of the row, at swizzled positions x and x^1) at LDS byte
+// offsets lo + imm and hi + imm
+__device__ __forceinline__ v8i frag2(const uint8_t* lo, const uint8_t* hi, int imm) {
+    const v4i l = *reinterpret_cast<const v4i*>(lo + imm);
+    const v4i h = *reinterpret_cast<const v4i*>(hi + imm);
+    return v8i{l.x, l.y, l.z, l.w, h.x, h.y, h.z, h.w};
 }
 
 // LDS DMA: lane l's 16 (4) bytes from sbase + voff land at LDS byte m0 + 16*l (4*l)
@@ -148,7 +165,7 @@ struct TileCursor {
     int e;               // expert of m-tile tm
     int e_lo, e_hi;      // its rows [e_lo, e_hi)
     bool valid;
-    int m0, row_end, n0; // the tile: rows [m0, min(m0 + BM, row_end)), columns n0..
+    int m0, row_end, n0; // the tile: rows [m0, min(m0 + bm, row_end)), columns n0..
 };
 
 struct TileWalk {
@@ -157,6 +174,7 @@ struct TileWalk {
     int64_t cap_rows;
     const int* s_tpre;
     int El, ntn, step_q, step_r;   // nslots = step_q * ntn + step_r
+    int bm;                        // tile rows
     int64_t t_hi, nslots;
 
     __device__ __forceinline__ void fill(TileCursor& c) const {
@@ -167,7 +185,7 @@ struct TileWalk {
     }
     __device__ __forceinline__ void tile(TileCursor& c) const {
         // clamped so that every row this tile touches is in [0, cap_rows)
-        int m0 = c.e_lo + (c.tm - s_tpre[c.e]) * BM;
+        int m0 = c.e_lo + (c.tm - s_tpre[c.e]) * bm;
         m0 = max(c.e_lo, min(m0, c.e_hi - 1));
         c.m0 = __builtin_amdgcn_readfirstlane(min(m0, (int)cap_rows - 1));
         c.row_end = c.e_hi;
@@ -220,17 +238,21 @@ struct TileWalk {
 // written to q [rows, N] and q_s [rows, N/128].  A tile then holds 128 gate
 // and the matching 128 up columns, and each lane owns matched gate/up pairs,
 // so no intermediate h is stored.
-template <bool KACT>
+template <bool KACT, int MI>
 __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
     const uint8_t* __restrict__ a, const float* __restrict__ a_s, const uint8_t* __restrict__ w,
     const float* __restrict__ w_s, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ counts, int El, int64_t cap_rows, int n_out, int k_in,
     uint16_t* __restrict__ out, uint8_t* __restrict__ q, float* __restrict__ q_s) {
+    using Sh = Shape<MI>;
+    constexpr int BM = Sh::BM, kStageA = Sh::kStageA, kStage = Sh::kStage, kStages = Sh::kStages;
+    constexpr int kADma = Sh::kADma, kDmaPerStep = Sh::kDmaPerStep, kScaleRows = Sh::kScaleRows;
+    static_assert(!KACT || MI == 4, "the fused epilogue is laid out for 128-row tiles");
     __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStage];
     __shared__ __attribute__((aligned(16))) float sAs[kStages][BM];   // [stage][row]
     __shared__ int s_tpre[kMaxLocalExperts + 1];
     __shared__ int s_wsum[kWaves];
-    __shared__ float s_amax[KACT ? 4 : 1][BM];   // per-wave-column partial group maxima
+    __shared__ float s_amax[KACT ? 4 : 1][KACT ? BM : 1];   // per-wave-column partial group maxima
     const int n_half = n_out / 2;                 // N when KACT
 
     const int tid = threadIdx.x;
@@ -289,24 +311,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
     walk.step_r = nslots - walk.step_q * ntn;
     walk.t_hi = t_hi;
     walk.nslots = nslots;
+    walk.bm = BM;
 
     const int wm = wave >> 2;   // 0..1
     const int wn = wave & 3;    // 0..3
     const int fr = lane & 15;
     const int fc = 2 * (lane >> 4);   // this lane's K chunk pair
-    // per-lane LDS offsets (within a stage) of the MFMA fragments
-    int offA[4], offB[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        offA[i] = swz(fc, wm * 64 + i * 16 + fr);
-        offB[i] = kStageA + swz(fc, wn * 64 + i * 16 + fr);
-    }
+    // per-lane LDS byte offsets (within a stage) of this lane's two fragment
+    // halves in row block 0 of A and of B; row block j adds j * 2048
+    const uint32_t fA_lo = (uint32_t)swz(fc, wm * 16 * MI + fr), fA_hi = fA_lo ^ 16u;
+    const uint32_t fB_lo = (uint32_t)(kStageA + swz(fc, wn * 64 + fr)), fB_hi = fB_lo ^ 16u;
 
     // ---- DMA side: which global chunk this lane fetches ---------------------
-    // Wave w fills LDS rows 16w..16w+15 of A (two 8-row DMAs) and 32w..32w+31
-    // of B (four), and the scales of rows 16w..16w+15 (lanes 0..15).
-    const int rA0 = (wave * 2) * 8 + (lane >> 3), rA1 = rA0 + 8;
-    const int cA0 = swz_pos(lane & 7, rA0), cA1 = swz_pos(lane & 7, rA1);   // the swizzle is an involution
+    // Wave w fills LDS rows 4*MI*w .. 4*MI*w + 4*MI-1 of A (MI/2 8-row DMAs)
+    // and 32w..32w+31 of B (four), and the scales of its A rows (lanes
+    // 0..4*MI-1).
+    int rA[kADma], cA[kADma];
+#pragma unroll
+    for (int j = 0; j < kADma; ++j) {
+        rA[j] = (wave * kADma + j) * 8 + (lane >> 3);
+        cA[j] = swz_pos(lane & 7, rA[j]);   // the swizzle is an involution
+    }
     // B: LDS row R holds weight row nB of the tile.  Plain: within each
     // 64-row quarter, row 4j+b goes to 16b+j, so lane j of MFMA column block
     // b computes output column 4j+b.  KACT: in the quarter of wave column wn,
@@ -320,7 +345,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
         nB[qq] = KACT ? (R >> 6) * 32 + 2 * (R & 15) + ((R >> 4) & 1) : b_row_inv(R);
         cB[qq] = swz_pos(lane & 7, R);
     }
-    const int rS = wave * 16 + (lane & 15);
+    const int rS = wave * kScaleRows + (lane & (kScaleRows - 1));
     const uint32_t lds_smem = (uint32_t)(uintptr_t)smem;
     const uint32_t lds_as = (uint32_t)(uintptr_t)&sAs[0][0];
 
@@ -333,13 +358,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
     TileCursor dT;
     walk.start(dT, t_lo);
     int d_g = 0, d_slot = 0;
-    uint32_t voA0 = 0, voA1 = 0, voB0 = 0, voB1 = 0, voB2 = 0, voB3 = 0, voS = 0;
+    uint32_t voA[kADma], voB0 = 0, voB1 = 0, voB2 = 0, voB3 = 0, voS = 0;
+#pragma unroll
+    for (int j = 0; j < kADma; ++j) voA[j] = 0;
 #define MOE_DMA_OFFSETS()                                                             \
     do {                                                                              \
         const int last_ = max(dT.row_end - 1 - dT.m0, 0);                             \
         const int nlast_ = KACT ? 127 : min(BN, n_out - dT.n0) - 1;                   \
-        voA0 = (uint32_t)(min(rA0, last_) * k_in + cA0 * 16);                         \
-        voA1 = (uint32_t)(min(rA1, last_) * k_in + cA1 * 16);                         \
+        _Pragma("unroll") for (int j_ = 0; j_ < kADma; ++j_)                          \
+            voA[j_] = (uint32_t)(min(rA[j_], last_) * k_in + cA[j_] * 16);           \
         voB0 = (uint32_t)(min(nB[0], nlast_) * k_in + cB[0] * 16);                    \
         voB1 = (uint32_t)(min(nB[1], nlast_) * k_in + cB[1] * 16);                    \
         voB2 = (uint32_t)(min(nB[2], nlast_) * k_in + cB[2] * 16);                    \
@@ -355,13 +382,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
         const uint8_t* sb_ = w + (((int64_t)dT.e * n_out + brow_) * k_in + d_g * BK); \
         const float* ss_ = a_s + ((int64_t)dT.m0 * kg + d_g);                         \
         const uint32_t base_ = lds_smem + d_slot * kStage;                            \
-        dma16(base_ + (wave * 2) * 1024, voA0, sa_);                                  \
-        dma16(base_ + (wave * 2 + 1) * 1024, voA1, sa_);                              \
+        _Pragma("unroll") for (int j_ = 0; j_ < kADma; ++j_)                          \
+            dma16(base_ + (wave * kADma + j_) * 1024, voA[j_], sa_);                  \
         dma16(base_ + kStageA + (wave * 4) * 1024, voB0, sb_);                        \
         dma16(base_ + kStageA + (wave * 4 + 1) * 1024, voB1, sb_);                    \
         dma16(base_ + kStageA + (wave * 4 + 2) * 1024, voB2, sb_);                    \
         dma16(base_ + kStageA + (wave * 4 + 3) * 1024, voB3, sb_);                    \
-        if (lane < 16) dma4(lds_as + d_slot * (BM * 4) + wave * 64, voS, ss_);        \
+        if (lane < kScaleRows)                                                        \
+            dma4(lds_as + d_slot * (BM * 4) + wave * (kScaleRows * 4), voS, ss_);     \
         loads += kDmaPerStep;                                                         \
         if (d_slot == 0) d_end0 = loads;                                              \
         else if (d_slot == 1) d_end1 = loads;                                         \
@@ -374,8 +402,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
         }                                                                             \
     } while (0)
     if (dT.valid) MOE_DMA_OFFSETS();
+    // the DMA stream runs kStages - 1 steps ahead
     if (S > 0) MOE_DMA_NEXT();
-    if (S > 1) MOE_DMA_NEXT();
+    if (kStages > 2 && S > 1) MOE_DMA_NEXT();
 
     int64_t i = 0;   // compute step
     int slot = 0;    // its ring slot
@@ -383,15 +412,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
     walk.start(cur, t_lo);
     while (cur.valid) {
         const int n_valid = KACT ? BN : min(BN, n_out - cur.n0);
-        const bool wave_has_rows = (cur.m0 + wm * 64) < cur.row_end && wn * 64 < n_valid;
+        const bool wave_has_rows = (cur.m0 + wm * 16 * MI) < cur.row_end && wn * 64 < n_valid;
         // weight block-scale rows: plain, the 128-column block of this wave;
         // KACT, the gate block (MFMA blocks 0/1) and the up block (2/3)
         const int64_t ws_row = KACT ? ((int64_t)cur.e * nb128 + (cur.n0 >> 8)) * kg
                                     : ((int64_t)cur.e * nb128 + min(cur.n0 / 128 + (wn >> 1), nb128 - 1)) * kg;
         const int64_t ws_row_up = ws_row + (int64_t)(n_half / 128) * kg;
-        v4f acc[4][4];
+        v4f acc[MI][4];
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
@@ -399,27 +428,31 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
             // step i's DMAs complete, in every wave
             wait_loads_barrier(__builtin_amdgcn_readfirstlane(
                 loads - (slot == 0 ? d_end0 : (slot == 1 ? d_end1 : d_end2))));
-            if (i + 2 < S) MOE_DMA_NEXT();   // into the slot step i-1 has released
+            if (i + kStages - 1 < S) MOE_DMA_NEXT();   // into the slot step i-1 has released
             if (wave_has_rows) {
-                const uint8_t* base = smem + slot * kStage;
-                const float* scs = &sAs[slot][wm * 64 + (lane >> 4) * 4];
+                const uint32_t sb = (uint32_t)slot * kStage;
+                const uint8_t* alo = smem + (sb + fA_lo);
+                const uint8_t* ahi = smem + (sb + fA_hi);
+                const uint8_t* blo = smem + (sb + fB_lo);
+                const uint8_t* bhi = smem + (sb + fB_hi);
+                const float* scs = &sAs[slot][wm * 16 * MI + (lane >> 4) * 4];
                 const float ws = w_s[ws_row + g];
                 const float ws_up = KACT ? w_s[ws_row_up + g] : ws;
                 v8i bf[4];
 #pragma unroll
-                for (int ni = 0; ni < 4; ++ni) bf[ni] = frag(base, offB[ni]);
+                for (int ni = 0; ni < 4; ++ni) bf[ni] = frag2(blo, bhi, ni * 2048);
                 // software-pipelined over the four row blocks: the MFMAs of
                 // row block mi+1 are in flight while row block mi is promoted
                 v4f p[2][4];
                 {
-                    const v8i af = frag(base, offA[0]);
+                    const v8i af = frag2(alo, ahi, 0);
 #pragma unroll
                     for (int ni = 0; ni < 4; ++ni) p[0][ni] = mfma_fp8(af, bf[ni]);
                 }
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi) {
-                    if (mi + 1 < 4) {
-                        const v8i af = frag(base, offA[mi + 1]);
+                for (int mi = 0; mi < MI; ++mi) {
+                    if (mi + 1 < MI) {
+                        const v8i af = frag2(alo, ahi, (mi + 1) * 2048);
 #pragma unroll
                         for (int ni = 0; ni < 4; ++ni) p[(mi + 1) & 1][ni] = mfma_fp8(af, bf[ni]);
                     }
@@ -441,15 +474,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
             slot = slot == kStages - 1 ? 0 : slot + 1;
         }
 
-        if (!KACT) {
+        if constexpr (!KACT) {
             // ---- epilogue: each lane owns 4 adjacent columns of 16 rows ----
             if (wave_has_rows) {
                 const int col = cur.n0 + wn * 64 + 4 * fr;
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
+                for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
-                        const int row = cur.m0 + wm * 64 + mi * 16 + (lane >> 4) * 4 + v;
+                        const int row = cur.m0 + wm * 16 * MI + mi * 16 + (lane >> 4) * 4 + v;
                         if (row < cur.row_end) {
                             v2i qv;
                             qv.x = (int)f32x2_to_bf16x2(acc[mi][0][v], acc[mi][1][v]);
@@ -536,10 +569,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
 
 namespace {
 
-int64_t gemm_grid(int64_t cap_rows, int El, int n_out, int num_cus) {
+#ifndef MOE_GEMM_PLAIN_MI
+#define MOE_GEMM_PLAIN_MI 8
+#endif
+constexpr int kPlainMI = MOE_GEMM_PLAIN_MI;   // 16-row MFMA blocks per wave of the plain GEMM
+
+int64_t gemm_grid(int64_t cap_rows, int El, int n_out, int bm, int num_cus) {
     const int64_t ntn = (n_out + BN - 1) / BN;
-    const int64_t bound = ((cap_rows + BM - 1) / BM + El) * ntn;
-    int64_t grid = num_cus;            // one 8-wave block per CU (150 KB of LDS)
+    const int64_t bound = ((cap_rows + bm - 1) / bm + El) * ntn;
+    int64_t grid = num_cus;            // one 8-wave block per CU (up to 150 KB of LDS)
     if (bound < grid) grid = bound;
     grid = ((grid + 7) / 8) * 8;
     if (grid < 8) grid = 8;
@@ -552,9 +590,10 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_s, const uint8_t
                                const float* w_s, const int32_t* offsets, const int32_t* counts,
                                int El, int64_t cap_rows, int n_out, int k_in, uint16_t* out,
                                int num_cus, hipStream_t s) {
-    const int64_t grid = gemm_grid(cap_rows, El, n_out, num_cus);
-    k_grouped_gemm<false><<<(unsigned)grid, kThreads, 0, s>>>(a, a_s, w, w_s, offsets, counts, El, cap_rows,
-                                                               n_out, k_in, out, nullptr, nullptr);
+    constexpr int MI = kPlainMI;
+    const int64_t grid = gemm_grid(cap_rows, El, n_out, Shape<MI>::BM, num_cus);
+    k_grouped_gemm<false, MI><<<(unsigned)grid, kThreads, 0, s>>>(a, a_s, w, w_s, offsets, counts, El,
+                                                                   cap_rows, n_out, k_in, out, nullptr, nullptr);
     return hipGetLastError();
 }
 
@@ -562,9 +601,9 @@ hipError_t launch_grouped_gemm_act(const uint8_t* a, const float* a_s, const uin
                                    const float* w13_s, const int32_t* offsets, const int32_t* counts,
                                    int El, int64_t cap_rows, int N, int k_in, uint8_t* q, float* q_s,
                                    int num_cus, hipStream_t s) {
-    const int64_t grid = gemm_grid(cap_rows, El, 2 * N, num_cus);
-    k_grouped_gemm<true><<<(unsigned)grid, kThreads, 0, s>>>(a, a_s, w13, w13_s, offsets, counts, El, cap_rows,
-                                                              2 * N, k_in, nullptr, q, q_s);
+    const int64_t grid = gemm_grid(cap_rows, El, 2 * N, Shape<4>::BM, num_cus);
+    k_grouped_gemm<true, 4><<<(unsigned)grid, kThreads, 0, s>>>(a, a_s, w13, w13_s, offsets, counts, El,
+                                                                 cap_rows, 2 * N, k_in, nullptr, q, q_s);
     return hipGetLastError();
 }
 
