@@ -357,7 +357,7 @@ def main():
                                f"topk={cfg.topk} routing={cfg.routing} on_input={on_input}",
                    "M": cfg.M, "K": cfg.K, "N": cfg.N, "experts": cfg.El, "topk": cfg.topk,
                    "chunk_size": cfg.chunk_size, "align": cfg.align, "pairs": P, "padded_rows": R},
-        "roofline": {"bound": "mfma", "kernel": "grouped GEMM w13 (k_grouped_gemm<false>)",
+        "roofline": {"bound": "mfma", "kernel": "grouped GEMM w13 (k_grouped_gemm<false, 8>, 256x256 tiles)",
                      "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic},
         "step": {"warm": wst, "cold": cst, "cold_tokens/s": round(cfg.M / (cst["median"] * 1e-3), 1),
