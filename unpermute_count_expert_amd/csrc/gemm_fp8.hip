@@ -487,7 +487,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
                             v2i qv;
                             qv.x = (int)f32x2_to_bf16x2(acc[mi][0][v], acc[mi][1][v]);
                             qv.y = (int)f32x2_to_bf16x2(acc[mi][2][v], acc[mi][3][v]);
-                            *reinterpret_cast<v2i*>(out + (int64_t)row * n_out + col) = qv;
+                            // streaming store: the output is read back from HBM by the
+                            // next kernel, so it need not take L2 lines from the operands
+                            __builtin_nontemporal_store(qv, reinterpret_cast<v2i*>(out + (int64_t)row * n_out + col));
                         }
                     }
             }
