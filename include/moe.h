@@ -120,6 +120,14 @@ int moe_permute(const uint8_t* a_q, const float* a_s, const int32_t* topk_ids,
                 int32_t* expert_offsets, int32_t* inv_perm, int32_t* row_src, void* workspace,
                 size_t workspace_bytes, void* stream);
 
+/* Output-tile rows (128 or 256) the grouped GEMM uses for rows_hint routed
+ * rows over El local experts: 256 once the experts average at least 256 rows,
+ * else 128.  moe_grouped_gemm_fp8 passes cap_rows as the hint and
+ * moe_forward_chunked the chunk's token-expert pairs (Mc * topk).  The tile
+ * changes only speed: outputs are identical either way.  Returns -1 when
+ * El < 1. */
+int32_t moe_grouped_gemm_tile_rows(int64_t rows_hint, int32_t El);
+
 /* Block-scaled fp8 grouped GEMM (the DeepGEMM grouped GEMM of [P20903],
  * Optimizations: e4m3, 128x128 blocks).  For every valid row r of expert e
  * (expert_offsets[e] <= r < expert_offsets[e] + counts[e]) and n < n_out:

@@ -40,6 +40,16 @@ def test_max_rows_bound():
     assert moe.moe_max_rows(10, 2, 8, 48) == -1
 
 
+def test_gemm_tile_rows_choice():
+    # 256-row tiles once the experts average 256 rows, 128-row tiles below
+    assert moe.moe_grouped_gemm_tile_rows(16384 * 8, 128) == 256
+    assert moe.moe_grouped_gemm_tile_rows(4096 * 8, 128) == 256
+    assert moe.moe_grouped_gemm_tile_rows(4096 * 8 - 1, 128) == 128
+    assert moe.moe_grouped_gemm_tile_rows(64 * 8, 64) == 128
+    assert moe.moe_grouped_gemm_tile_rows(0, 8) == 128
+    assert moe.moe_grouped_gemm_tile_rows(1000, 0) == -1
+
+
 def test_workspace_size_monotone_in_chunk():
     full = moe.moe_forward_workspace_size(moe.problem(8192, 2048, 768, 8, 128, 64, chunk_size=0))
     small = moe.moe_forward_workspace_size(moe.problem(8192, 2048, 768, 8, 128, 64, chunk_size=64))

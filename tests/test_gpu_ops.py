@@ -215,15 +215,18 @@ def _segments(counts, align):
     return offs, counts
 
 
-def test_gemm_integer_case_bit_exact():
+@pytest.mark.parametrize("counts,tile", [([1, 130, 0, 257, 64], 128),
+                                         ([1, 300, 0, 513, 129], 256)])
+def test_gemm_integer_case_bit_exact(counts, tile):
     """Codes in {0, +1, -1} with unit scales: every partial and total is an
     integer of magnitude <= 256, so the result is exact and must equal an
-    int64 matmul bit for bit."""
-    announce("gemm integer")
+    int64 matmul bit for bit, on both output-tile shapes."""
+    announce("gemm integer", counts, tile)
     rng = np.random.default_rng(4)
     El, n_out, k_in = 5, 384, 256
-    offs, cnt = _segments([1, 130, 0, 257, 64], 128)
+    offs, cnt = _segments(counts, 128)
     cap = int(offs[-1]) + 40
+    assert moe.moe_grouped_gemm_tile_rows(cap, El) == tile
     pm1 = np.array([0x00, 0x38, 0xB8], np.uint8)
     a_i = rng.integers(-1, 2, (cap, k_in))
     w_i = rng.integers(-1, 2, (El, n_out, k_in))
@@ -286,17 +289,23 @@ def _spec_values():
     return SPEC
 
 
-@pytest.mark.parametrize("El,n_out,k_in,counts,align", [
-    (4, 256, 512, [1, 127, 128, 300], 128),
-    (3, 384, 256, [17, 0, 250], 16),
-    (6, 128, 1024, [5, 33, 64, 1, 0, 129], 32),
-    (2, 1536, 2048, [200, 77], 128),
+@pytest.mark.parametrize("El,n_out,k_in,counts,align,tile", [
+    (4, 256, 512, [1, 127, 128, 300], 128, 128),
+    (3, 384, 256, [17, 0, 250], 16, 128),
+    (6, 128, 1024, [5, 33, 64, 1, 0, 129], 32, 128),
+    (2, 1536, 2048, [200, 77], 128, 128),
+    # 256-row tiles: a full tile, tails of 1..255 rows, the second 128-row
+    # half of a tile empty or partial, a 128-column last n-tile
+    (3, 384, 768, [600, 1, 300], 128, 256),
+    (2, 1536, 2048, [513, 256], 128, 256),
+    (4, 640, 384, [0, 129, 767, 64], 64, 256),
 ])
-def test_gemm_random_parity(El, n_out, k_in, counts, align):
-    announce("gemm random", El, n_out, k_in, counts, align)
+def test_gemm_random_parity(El, n_out, k_in, counts, align, tile):
+    announce("gemm random", El, n_out, k_in, counts, align, tile)
     rng = np.random.default_rng(n_out + k_in)
     offs, cnt = _segments(counts, align)
     cap = int(offs[-1]) + 3
+    assert moe.moe_grouped_gemm_tile_rows(cap, El) == tile
     a = gen.random_codes(rng, (cap, k_in))
     w = gen.random_codes(rng, (El, n_out, k_in))
     a_s = rng.uniform(1e-3, 1, (cap, k_in // 128)).astype(np.float32)

@@ -35,7 +35,8 @@ class MoeProblem(C.Structure):
                 ("chunk_size", C.c_int64)]
 
 
-EXPORTS = ["moe_status_string", "moe_last_error", "moe_max_rows", "moe_forward_workspace_size",
+EXPORTS = ["moe_status_string", "moe_last_error", "moe_max_rows", "moe_grouped_gemm_tile_rows",
+           "moe_forward_workspace_size",
            "moe_permute_workspace_size", "moe_count", "moe_permute", "moe_grouped_gemm_fp8",
            "moe_grouped_gemm_fp8_act_quant", "moe_act_quant", "moe_unpermute_weight_reduce",
            "moe_forward_chunked"]
@@ -54,6 +55,7 @@ def load() -> C.CDLL:
         L.moe_status_string.argtypes = [C.c_int]; L.moe_status_string.restype = C.c_char_p
         L.moe_last_error.argtypes = []; L.moe_last_error.restype = C.c_char_p
         L.moe_max_rows.argtypes = [I64, I32, I32, I32]; L.moe_max_rows.restype = I64
+        L.moe_grouped_gemm_tile_rows.argtypes = [I64, I32]; L.moe_grouped_gemm_tile_rows.restype = I32
         L.moe_forward_workspace_size.argtypes = [C.POINTER(MoeProblem), C.POINTER(SZ)]
         L.moe_permute_workspace_size.argtypes = [I64, I32, I32, C.POINTER(SZ)]
         L.moe_count.argtypes = [P, I64, P, I32, I32, P, P, P]
@@ -66,7 +68,7 @@ def load() -> C.CDLL:
         L.moe_forward_chunked.argtypes = [C.POINTER(MoeProblem), P, P, P, P, P, P, P, P, P, P, SZ,
                                           P, P]
         for name in EXPORTS:
-            if name not in ("moe_status_string", "moe_last_error", "moe_max_rows"):
+            if name not in ("moe_status_string", "moe_last_error", "moe_max_rows", "moe_grouped_gemm_tile_rows"):
                 getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -92,6 +94,10 @@ def _stream(stream=None):
 
 def moe_max_rows(Mc: int, topk: int, El: int, align: int = 128) -> int:
     return int(load().moe_max_rows(Mc, topk, El, align))
+
+
+def moe_grouped_gemm_tile_rows(rows_hint: int, El: int) -> int:
+    return int(load().moe_grouped_gemm_tile_rows(rows_hint, El))
 
 
 def problem(M, K, N, topk, Eg, El, align=128, apply_on_input=0, chunk_size=0) -> MoeProblem:

@@ -165,6 +165,10 @@ int64_t moe_max_rows(int64_t Mc, int32_t topk, int32_t El, int32_t align) {
     return max_rows(Mc, topk, El, align);
 }
 
+int32_t moe_grouped_gemm_tile_rows(int64_t rows_hint, int32_t El) {
+    return El < 1 ? -1 : moe::gemm_tile_rows(rows_hint, El);
+}
+
 int moe_forward_workspace_size(const moe_problem* p, size_t* bytes) {
     int st = check_problem(p);
     if (st) return st;
@@ -264,7 +268,7 @@ int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const uint8_t* w, c
     int st = check_device(&cus);
     if (st) return st;
     HIP_OK(moe::launch_grouped_gemm(a, a_s, w, w_s, expert_offsets, counts, El, cap_rows, n_out, k_in, out,
-                                    cus, static_cast<hipStream_t>(stream)));
+                                    cap_rows, cus, static_cast<hipStream_t>(stream)));
     return MOE_OK;
 }
 
@@ -402,11 +406,11 @@ int moe_forward_chunked(const moe_problem* p, const uint16_t* x, const int32_t* 
                                    offsets, inv, rsrc, hist,
                                    per_chunk_counts ? per_chunk_counts + c * El : nullptr, s));
         HIP_OK(moe::launch_grouped_gemm(bufA, bufAs, w13, w13_s, offsets, counts, (int)El, pl.cap,
-                                        (int)(2 * N), (int)K, hy, cus, s));
+                                        (int)(2 * N), (int)K, hy, Mc * T, cus, s));
         HIP_OK(moe::launch_act_quant(hy, pl.cap, (int)N, moe::MOE_ACT_SILU_MUL_K, offsets, counts, (int)El,
                                      bufA, bufAs, s));
         HIP_OK(moe::launch_grouped_gemm(bufA, bufAs, w2, w2_s, offsets, counts, (int)El, pl.cap, (int)K,
-                                        (int)N, hy, cus, s));
+                                        (int)N, hy, Mc * T, cus, s));
         HIP_OK(moe::launch_unpermute(hy, pl.cap, inv, w_c, Mc, (int)K, (int)T, on_in, out + t0 * K, s));
     }
     return MOE_OK;

@@ -38,10 +38,13 @@ hipError_t launch_act_quant(const uint16_t* in, int64_t rows, int n, int mode,
                             float* q_s, hipStream_t s);
 
 // ---- grouped GEMM ------------------------------------------------------------
+// Output-tile rows of the plain GEMM for rows_hint routed rows over El
+// experts: 256 once the experts average 256 rows, else 128.
+int gemm_tile_rows(int64_t rows_hint, int El);
 hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_s, const uint8_t* w,
                                const float* w_s, const int32_t* offsets, const int32_t* counts,
                                int El, int64_t cap_rows, int n_out, int k_in, uint16_t* out,
-                               int num_cus, hipStream_t s);
+                               int64_t rows_hint, int num_cus, hipStream_t s);
 
 // The gate/up GEMM (w13 [El, 2N, k_in]) fused with SiLU-and-mul and the
 // per-128 requant: writes q [cap_rows, N] e4m3 and q_s [cap_rows, N/128].
