@@ -97,7 +97,7 @@ class Flusher:
         self.buf.fill_(self.v)
 
 
-def per_op_times(layer, d, on_input, iters, stream, only=None, flush=None):
+def per_op_times(layer, d, on_input, iters, stream, only=None, flush=None, fused_input=True):
     """Times each op of the pipeline through its own C-ABI entry point (the
     kernels the fused call runs, plus the standalone count).  Each of `iters`
     passes runs the whole sequence with a HIP event recorded on the launching
@@ -105,9 +105,14 @@ def per_op_times(layer, d, on_input, iters, stream, only=None, flush=None):
     its real neighbours; with `flush`, the caches are flushed (untimed) before
     every op.  With `only`, the ops before it run once to fill its inputs and
     only it is launched repeatedly (so a profiler sees no other launch of the
-    same kernel).  Returns {op: [ms per pass]}."""
+    same kernel).  fused_input=False times the input quant and the permute as
+    the two separate calls (not the forward's path).  Returns {op: [ms per
+    pass]}."""
+    if only in ("input_quant", "permute"):
+        fused_input = False
     b = StepBuffers(layer, d["x"].shape[0], d["ids"].shape[1])
-    ops = step_ops(layer, d["x"], d["ids"], d["w"], on_input, b, fused=(only == "gemm_w13_act"))
+    ops = step_ops(layer, d["x"], d["ids"], d["w"], on_input, b, fused=(only == "gemm_w13_act"),
+                   fused_input=fused_input)
     names = list(ops)
     if only is not None:
         names = names[:names.index(only) + 1]
@@ -169,6 +174,8 @@ def algorithmic(cfg, counts: np.ndarray, R: int):
     by = {
         "count": 4 * M * T + 4 * cfg.El,
         "input_quant": 2 * M * K + M * K + 4 * M * K / 128,
+        # the input quant fused into the permute: bf16 x read once
+        "quant_permute": 2 * M * K + P * K + 4 * P * K / 128 + 8 * M * T + 4 * R,
         "permute": M * K + 4 * M * K / 128 + P * K + 4 * P * K / 128 + 8 * M * T + 4 * R,
         "gemm_w13": P * K + Ene * 2 * N * K + 4 * P * N + 4 * P * K / 128 + 4 * Ene * (2 * N // 128) * (K // 128),
         # fused with the SiLU-mul requant: h never reaches memory
@@ -255,7 +262,7 @@ def main():
                     help="also time short runs of the other layer configurations")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--profile-op", default=None,
-                    help="time only this op (input_quant, count, permute, gemm_w13, silu_mul_quant, "
+                    help="time only this op (count, quant_permute, input_quant, permute, gemm_w13, silu_mul_quant, "
                          "gemm_w2, unpermute, or gemm_w13_act: the fused variant) or 'copy'; for profiler runs")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -315,6 +322,7 @@ def main():
     ops, counts, R = per_op_times(layer, d, on_input, args.op_iters, stream)
     ops_cold, _, _ = per_op_times(layer, d, on_input, args.op_iters, stream, flush=flush)
     fused, _, _ = per_op_times(layer, d, on_input, args.op_iters, stream, only="gemm_w13_act")
+    unfused_in, _, _ = per_op_times(layer, d, on_input, args.op_iters, stream, fused_input=False)
     P, Ene, g1f, g2f, by = algorithmic(cfg, counts, R)
     ops_out = {}
     for name in ops:
@@ -334,6 +342,10 @@ def main():
     ops_out["gemm_w13_act (fused variant, not on the forward path)"] = {
         "ms": round(tf, 5), "GB/s": round(by["gemm_w13_act"] / (tf * 1e-3) / 1e9, 1),
         "TFLOP/s": round(g1f / (tf * 1e-3) / 1e12, 1)}
+    for name in ("input_quant", "permute"):
+        tu = stats(unfused_in[name])["median"]
+        ops_out[name + " (separate call, not on the forward path)"] = {
+            "ms": tu, "GB/s": round(by[name] / (tu * 1e-3) / 1e9, 1)}
     t_g1 = stats(ops["gemm_w13"])["median"]
     achieved = g1f / (t_g1 * 1e-3) / 1e12
     t_g2 = stats(ops["gemm_w2"])["median"]

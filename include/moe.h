@@ -120,6 +120,21 @@ int moe_permute(const uint8_t* a_q, const float* a_s, const int32_t* topk_ids,
                 int32_t* expert_offsets, int32_t* inv_perm, int32_t* row_src, void* workspace,
                 size_t workspace_bytes, void* stream);
 
+/* ep_scatter permute [P20903 Purpose item 2] with the per-token 1x128 fp8
+ * input quantisation [P20903 Optimizations] fused in, so the bf16 tokens are
+ * read once: x [Mc,K] bf16; every group of
+ * 128 values of a token is quantised as moe_act_quant in identity mode and
+ * its codes and scale are written straight to the token's expert rows, so
+ * a_perm, a_perm_s, counts, expert_offsets, inv_perm and row_src are exactly
+ * those of moe_act_quant (identity) followed by moe_permute, and no a_q/a_s
+ * buffer exists.  Other arguments, limits and errors as moe_permute; x must
+ * be 16-byte aligned. */
+int moe_quant_permute(const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
+                      int32_t apply_on_input, int64_t Mc, int32_t K, int32_t topk, const int32_t* expert_map,
+                      int32_t Eg, int32_t El, int32_t align, int64_t cap_rows, uint8_t* a_perm,
+                      float* a_perm_s, int32_t* counts, int32_t* expert_offsets, int32_t* inv_perm,
+                      int32_t* row_src, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Output-tile rows (128 or 256) the grouped GEMM uses for rows_hint routed
  * rows over El local experts: 256 once the experts average at least 256 rows,
  * else 128.  moe_grouped_gemm_fp8 passes cap_rows as the hint and

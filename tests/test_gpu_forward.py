@@ -28,7 +28,7 @@ import torch
 import oracle
 import unpermute_count_expert_amd as moe
 from unpermute_count_expert_amd import generators as gen
-from unpermute_count_expert_amd.pipeline import run_steps
+from unpermute_count_expert_amd.pipeline import StepBuffers, run_steps, step_ops
 from tests.gpu_helpers import (ATOL, RTOL, announce, assert_gemm_close, bf16_f64, dev, filled, host,
                                valid_rows)
 
@@ -74,7 +74,7 @@ def check_layer(cfg, on_input, n_sample_rows=64, n_sample_tokens=48):
     M, K, N, T, El = cfg.M, cfg.K, cfg.N, cfg.topk, cfg.El
     layer = _layer(inp)
     d = dict(x=dev(inp.x), ids=dev(inp.topk_ids), w=dev(inp.topk_weights))
-    b = run_steps(layer, d["x"], d["ids"], d["w"], on_input)
+    b = run_steps(layer, d["x"], d["ids"], d["w"], on_input, fused_input=False)
     g = {k: host(getattr(b, k)) for k in ("a_q", "a_s", "a_perm", "a_perm_s", "counts", "offsets", "inv_perm",
                                           "row_src", "act_q", "act_s", "count_only")}
     g["h"], g["y"], g["out"] = host(b.h, bf16=True), host(b.y, bf16=True), host(b.out, bf16=True)
@@ -94,6 +94,18 @@ def check_layer(cfg, on_input, n_sample_rows=64, n_sample_tokens=48):
     np.testing.assert_array_equal(g["a_perm"][rows], r["a_perm"][rows])
     np.testing.assert_array_equal(g["a_perm_s"][rows], r["a_perm_s"][rows])
     row_exp = np.repeat(np.arange(El), r["counts"]).astype(np.int32)   # expert of each valid row
+
+    # -- the input quant fused into the permute: the same bits as the chain
+    fb = StepBuffers(layer, M, T)
+    fb.a_perm.fill_(0x5A)
+    step_ops(layer, d["x"], d["ids"], d["w"], on_input, fb)["quant_permute"]()
+    for k in ("counts", "offsets", "inv_perm", "row_src"):
+        np.testing.assert_array_equal(host(getattr(fb, k)), g[k], err_msg="quant_permute " + k)
+    fa = host(fb.a_perm)
+    np.testing.assert_array_equal(fa[rows], g["a_perm"][rows])
+    np.testing.assert_array_equal(host(fb.a_perm_s)[rows], g["a_perm_s"][rows])
+    assert (fa[np.setdiff1d(np.arange(fa.shape[0]), rows)] == 0x5A).all(), "quant_permute wrote a padding row"
+    del fb
 
     # -- GEMM w13 on sampled valid rows
     pick = _sample(len(rows), rng, n_sample_rows)

@@ -187,6 +187,64 @@ def test_permute_parity(M, K, T, Eg, El, mapped, align, on_input, routing):
     _check_permute(g, r)
 
 
+def _gpu_quant_permute(x, ids, w, on_input, emap, Eg, El, align):
+    Mc, K = x.shape
+    T = ids.shape[1]
+    cap = moe.moe_max_rows(Mc, T, El, align)
+    ws = empty((moe.moe_permute_workspace_size(Mc, T, El),), torch.uint8)
+    a_perm = filled((cap, K), torch.uint8, 0xA5)
+    a_perm_s = filled((cap, K // 128), torch.float32, -7.0)
+    counts = empty((El,), torch.int32)
+    offs = empty((El + 1,), torch.int32)
+    inv = filled((Mc, T), torch.int32, -77)
+    rsrc = filled((cap,), torch.int32, -77)
+    xd = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to("cuda:0")
+    moe.moe_quant_permute(xd, dev(ids), dev(w), on_input, dev(emap) if emap is not None else None,
+                          Eg, El, align, cap, a_perm, a_perm_s, counts, offs, inv, rsrc, ws)
+    return dict(a_perm=host(a_perm), a_perm_s=host(a_perm_s), counts=host(counts),
+                expert_offsets=host(offs), inv_perm=host(inv), row_src=host(rsrc), cap_rows=cap)
+
+
+@pytest.mark.parametrize("M,K,T,Eg,El,mapped,align,on_input,routing,special", [
+    (77, 256, 4, 32, 12, True, 128, 0, "random", False),
+    (77, 384, 4, 32, 12, True, 16, 1, "random", True),       # 3 groups a token, NaN/Inf/zero rows
+    (300, 640, 3, 20, 20, False, 32, 1, "random", False),    # 5 groups a token
+    (64, 2048, 4, 128, 64, True, 128, 0, "uniform", False),  # profiling shape
+    (16384, 2048, 8, 128, 128, False, 128, 1, "uniform", False),
+    (3, 128, 256, 300, 300, False, 16, 0, "random", True),   # topk 256, one group a token
+])
+def test_quant_permute_parity(M, K, T, Eg, El, mapped, align, on_input, routing, special):
+    """The input quant fused into the permute: bit-exact with the oracle's
+    identity quant followed by its permute (codes, scales, offsets, inverse
+    and source indices); padding rows are not written."""
+    announce("quant permute", M, K, T, Eg, El, mapped, align, on_input, routing, special)
+    rng = np.random.default_rng(M * 5 + K)
+    xf = (rng.standard_normal((M, K)) * rng.uniform(1e-3, 3, (M, 1))).astype(np.float32)
+    if special:
+        xf[0, :] = 0.0
+        xf[-1, 5] = np.nan
+        xf[M // 2, 130 % K] = -np.inf
+        xf[M // 2, 7] = 1e30
+    x = gen.bf16_bits(xf)
+    if routing == "random":
+        ids = gen.random_ids(rng, M, T, Eg, 0.05, 0.02)
+    else:
+        cfg = gen.small_config(M=M, K=K, N=128, Eg=Eg, El=El, topk=T, routing="softmax", seed=M)
+        ids, _, _ = gen.routing(rng, cfg)
+    w = rng.uniform(0, 1, (M, T)).astype(np.float32)
+    emap = None
+    if mapped:
+        emap = np.full(Eg, -1, np.int32)
+        emap[Eg - El:] = np.arange(El, dtype=np.int32)
+    g = _gpu_quant_permute(x, ids, w, on_input, emap, Eg, El, align)
+    a_q, a_s = oracle.act_quant_identity(x)
+    r = oracle.permute(a_q, a_s, ids, w, on_input, emap, Eg, El, align)
+    _check_permute(g, r)
+    rows = valid_rows(r["expert_offsets"], r["counts"])
+    pad = np.setdiff1d(np.arange(g["cap_rows"]), rows)
+    assert (g["a_perm"][pad] == 0xA5).all() and (g["a_perm_s"][pad] == -7.0).all(), "padding row written"
+
+
 def test_permute_single_expert_takes_everything():
     announce("permute single expert")
     rng = np.random.default_rng(1)

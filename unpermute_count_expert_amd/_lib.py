@@ -38,7 +38,7 @@ class MoeProblem(C.Structure):
 EXPORTS = ["moe_status_string", "moe_last_error", "moe_max_rows", "moe_grouped_gemm_tile_rows",
            "moe_forward_workspace_size",
            "moe_permute_workspace_size", "moe_count", "moe_permute", "moe_grouped_gemm_fp8",
-           "moe_grouped_gemm_fp8_act_quant", "moe_act_quant", "moe_unpermute_weight_reduce",
+           "moe_grouped_gemm_fp8_act_quant", "moe_act_quant", "moe_quant_permute", "moe_unpermute_weight_reduce",
            "moe_forward_chunked"]
 
 _lib = None
@@ -61,6 +61,8 @@ def load() -> C.CDLL:
         L.moe_count.argtypes = [P, I64, P, I32, I32, P, P, P]
         L.moe_permute.argtypes = [P, P, P, P, I32, I64, I32, I32, P, I32, I32, I32, I64,
                                   P, P, P, P, P, P, P, SZ, P]
+        L.moe_quant_permute.argtypes = [P, P, P, I32, I64, I32, I32, P, I32, I32, I32, I64,
+                                        P, P, P, P, P, P, P, SZ, P]
         L.moe_grouped_gemm_fp8.argtypes = [P, P, P, P, P, P, I32, I64, I32, I32, P, P]
         L.moe_grouped_gemm_fp8_act_quant.argtypes = [P, P, P, P, P, P, I32, I64, I32, I32, P, P, P]
         L.moe_act_quant.argtypes = [P, I64, I32, I32, P, P, I32, P, P, P]
@@ -130,6 +132,17 @@ def moe_permute(a_q, a_s, topk_ids, topk_weights, apply_on_input, expert_map, Eg
                               _ptr(a_perm_s), _ptr(counts), _ptr(expert_offsets), _ptr(inv_perm),
                               _ptr(row_src), _ptr(workspace), workspace.numel() * workspace.element_size(),
                               _stream(stream)), "moe_permute")
+
+
+def moe_quant_permute(x, topk_ids, topk_weights, apply_on_input, expert_map, Eg, El, align, cap_rows,
+                      a_perm, a_perm_s, counts, expert_offsets, inv_perm, row_src, workspace, stream=None):
+    Mc, K = x.shape
+    topk = topk_ids.shape[1]
+    _check(load().moe_quant_permute(_ptr(x), _ptr(topk_ids), _ptr(topk_weights), apply_on_input,
+                                    Mc, K, topk, _ptr(expert_map), Eg, El, align, cap_rows, _ptr(a_perm),
+                                    _ptr(a_perm_s), _ptr(counts), _ptr(expert_offsets), _ptr(inv_perm),
+                                    _ptr(row_src), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(stream)), "moe_quant_permute")
 
 
 def moe_grouped_gemm_fp8(a, a_s, w, w_s, expert_offsets, counts, out, stream=None):

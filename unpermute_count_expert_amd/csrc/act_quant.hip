@@ -122,30 +122,8 @@ __global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restri
                 x.v[i + 1] = __uint_as_float(pk & 0xffff0000u);
             }
         }
-        // largest non-NaN magnitude: a compare-select skips quiet and
-        // signalling NaNs alike (v_max_f32 would turn a signalling NaN
-        // into NaN)
-        float amax = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float a = __builtin_fabsf(x.v[i]);
-            amax = a > amax ? a : amax;
-        }
-#pragma unroll
-        for (int d = kLanesPerGroup / 2; d >= 1; d >>= 1) {
-            const float o = __shfl_xor(amax, d, kWave);
-            amax = o > amax ? o : amax;
-        }
-        const float dd = __builtin_fmaxf(amax, 1e-10f);
-        const float scale = dd / 448.0f;
-        const float inv = 448.0f / dd;
-        float t[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) t[i] = x.v[i] * inv;
         uint2 codes;
-        // |t| <= 448 (1 + 2^-23) unless t is NaN: d >= every |x| of the group
-        codes.x = f32x4_to_e4m3_bounded(t[0], t[1], t[2], t[3]);
-        codes.y = f32x4_to_e4m3_bounded(t[4], t[5], t[6], t[7]);
+        const float scale = quant_group16(x.v, codes);
         if (valid) {
             *reinterpret_cast<uint2*>(q + r_this * n + gi_this * kGroup + sub * 8) = codes;
             if (sub == 0) q_s[r_this * ng + gi_this] = scale;

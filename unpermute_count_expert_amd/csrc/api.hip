@@ -92,7 +92,7 @@ size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
 // the unpermute reads bufB.  The output never aliases the workspace.
 struct Plan {
     int64_t cs, cap, nblk;
-    size_t bufA, bufAs, bufB, a_s_in_B, counts, offsets, inv, rsrc, hist, total;
+    size_t bufA, bufAs, bufB, counts, offsets, inv, rsrc, hist, total;
 };
 
 Plan make_plan(const moe_problem& p) {
@@ -107,12 +107,7 @@ Plan make_plan(const moe_problem& p) {
     size_t off = 0;
     pl.bufA = off;  off += up256((size_t)pl.cap * wA);
     pl.bufAs = off; off += up256((size_t)pl.cap * (wA / moe::kGroup) * 4);
-    pl.bufB = off;
-    pl.a_s_in_B = up256((size_t)pl.cs * K);
-    size_t bsz = (size_t)pl.cap * wB;
-    const size_t need_in = pl.a_s_in_B + (size_t)pl.cs * (K / moe::kGroup) * 4;
-    if (need_in > bsz) bsz = need_in;
-    off += up256(bsz);
+    pl.bufB = off;  off += up256((size_t)pl.cap * wB);
     pl.counts = off;  off += up256((size_t)El * 4);
     pl.offsets = off; off += up256((size_t)(El + 1) * 4);
     pl.inv = off;     off += up256((size_t)pl.cs * p.topk * 4);
@@ -202,12 +197,18 @@ int moe_count(const int32_t* topk_ids, int64_t num_pairs, const int32_t* expert_
     return MOE_OK;
 }
 
-int moe_permute(const uint8_t* a_q, const float* a_s, const int32_t* topk_ids,
-                const float* topk_weights, int32_t apply_on_input, int64_t Mc, int32_t K,
-                int32_t topk, const int32_t* expert_map, int32_t Eg, int32_t El, int32_t align,
-                int64_t cap_rows, uint8_t* a_perm, float* a_perm_s, int32_t* counts,
-                int32_t* expert_offsets, int32_t* inv_perm, int32_t* row_src, void* workspace,
-                size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// moe_permute (quant false: a_q / a_s given) and moe_quant_permute (quant
+// true: x given): the same checks, then the launch
+int permute_common(bool quant, const uint8_t* a_q, const float* a_s, const uint16_t* x, const int32_t* topk_ids,
+                   const float* topk_weights, int32_t apply_on_input, int64_t Mc, int32_t K, int32_t topk,
+                   const int32_t* expert_map, int32_t Eg, int32_t El, int32_t align, int64_t cap_rows,
+                   uint8_t* a_perm, float* a_perm_s, int32_t* counts, int32_t* expert_offsets,
+                   int32_t* inv_perm, int32_t* row_src, void* workspace, size_t workspace_bytes,
+                   void* stream) {
     REQUIRE(Mc >= 0, MOE_ERR_SHAPE, "Mc < 0");
     REQUIRE(K > 0 && K % moe::kGroup == 0, MOE_ERR_SHAPE, "K=%d is not a positive multiple of 128", K);
     REQUIRE(topk >= 1 && topk <= 256, MOE_ERR_SHAPE, "topk=%d outside [1,256]", topk);
@@ -228,8 +229,13 @@ int moe_permute(const uint8_t* a_q, const float* a_s, const int32_t* topk_ids,
     REQUIRE_PTR(expert_offsets);
     if (cap_rows > 0) REQUIRE_PTR(row_src);
     if (Mc > 0) {
-        REQUIRE_PTR(a_q);
-        REQUIRE_PTR(a_s);
+        if (quant) {
+            REQUIRE_PTR(x);
+            REQUIRE(aligned16(x), MOE_ERR_INVALID_ARG, "x is not 16-byte aligned");
+        } else {
+            REQUIRE_PTR(a_q);
+            REQUIRE_PTR(a_s);
+        }
         REQUIRE_PTR(topk_ids);
         REQUIRE_PTR(a_perm);
         REQUIRE_PTR(a_perm_s);
@@ -239,11 +245,47 @@ int moe_permute(const uint8_t* a_q, const float* a_s, const int32_t* topk_ids,
     REQUIRE(expert_map == nullptr || aligned16(expert_map), MOE_ERR_INVALID_ARG, "expert_map alignment");
     int st = check_device(nullptr);
     if (st) return st;
-    HIP_OK(moe::launch_permute(a_q, a_s, topk_ids, topk_weights, apply_on_input, Mc, K, topk, expert_map,
-                               Eg, El, align, cap_rows, a_perm, a_perm_s, counts, expert_offsets, inv_perm,
-                               row_src, static_cast<int32_t*>(workspace), nullptr,
-                               static_cast<hipStream_t>(stream)));
+    if (quant)
+        HIP_OK(moe::launch_quant_permute(x, topk_ids, topk_weights, apply_on_input, Mc, K, topk, expert_map, Eg,
+                                         El, align, cap_rows, a_perm, a_perm_s, counts, expert_offsets, inv_perm,
+                                         row_src, static_cast<int32_t*>(workspace), nullptr,
+                                         static_cast<hipStream_t>(stream)));
+    else
+        HIP_OK(moe::launch_permute(a_q, a_s, topk_ids, topk_weights, apply_on_input, Mc, K, topk, expert_map,
+                                   Eg, El, align, cap_rows, a_perm, a_perm_s, counts, expert_offsets, inv_perm,
+                                   row_src, static_cast<int32_t*>(workspace), nullptr,
+                                   static_cast<hipStream_t>(stream)));
     return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_permute(const uint8_t* a_q, const float* a_s, const int32_t* topk_ids,
+                const float* topk_weights, int32_t apply_on_input, int64_t Mc, int32_t K,
+                int32_t topk, const int32_t* expert_map, int32_t Eg, int32_t El, int32_t align,
+                int64_t cap_rows, uint8_t* a_perm, float* a_perm_s, int32_t* counts,
+                int32_t* expert_offsets, int32_t* inv_perm, int32_t* row_src, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    if (Mc > 0) {
+        REQUIRE_PTR(a_q);
+        REQUIRE_PTR(a_s);
+    }
+    return permute_common(false, a_q, a_s, nullptr, topk_ids, topk_weights, apply_on_input, Mc, K, topk, expert_map,
+                          Eg, El, align, cap_rows, a_perm, a_perm_s, counts, expert_offsets, inv_perm, row_src,
+                          workspace, workspace_bytes, stream);
+}
+
+int moe_quant_permute(const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
+                      int32_t apply_on_input, int64_t Mc, int32_t K, int32_t topk, const int32_t* expert_map,
+                      int32_t Eg, int32_t El, int32_t align, int64_t cap_rows, uint8_t* a_perm,
+                      float* a_perm_s, int32_t* counts, int32_t* expert_offsets, int32_t* inv_perm,
+                      int32_t* row_src, void* workspace, size_t workspace_bytes, void* stream) {
+    if (Mc > 0) REQUIRE_PTR(x);
+    return permute_common(true, nullptr, nullptr, x, topk_ids, topk_weights, apply_on_input, Mc, K, topk, expert_map,
+                          Eg, El, align, cap_rows, a_perm, a_perm_s, counts, expert_offsets, inv_perm, row_src,
+                          workspace, workspace_bytes, stream);
 }
 
 int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const uint8_t* w, const float* w_s,
@@ -381,10 +423,7 @@ int moe_forward_chunked(const moe_problem* p, const uint16_t* x, const int32_t* 
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     uint8_t* bufA = ws + pl.bufA;
     float* bufAs = reinterpret_cast<float*>(ws + pl.bufAs);
-    uint8_t* bufB = ws + pl.bufB;
-    uint8_t* a_q = bufB;
-    float* a_s = reinterpret_cast<float*>(bufB + pl.a_s_in_B);
-    uint16_t* hy = reinterpret_cast<uint16_t*>(bufB);
+    uint16_t* hy = reinterpret_cast<uint16_t*>(ws + pl.bufB);
     int32_t* counts = reinterpret_cast<int32_t*>(ws + pl.counts);
     int32_t* offsets = reinterpret_cast<int32_t*>(ws + pl.offsets);
     int32_t* inv = reinterpret_cast<int32_t*>(ws + pl.inv);
@@ -399,12 +438,11 @@ int moe_forward_chunked(const moe_problem* p, const uint16_t* x, const int32_t* 
         const int64_t Mc = (t0 + pl.cs <= P.M) ? pl.cs : (P.M - t0);
         const int32_t* ids_c = topk_ids + t0 * T;
         const float* w_c = topk_weights + t0 * T;
-        HIP_OK(moe::launch_act_quant(x + t0 * K, Mc, (int)K, moe::MOE_ACT_IDENTITY_K, nullptr, nullptr, 0,
-                                     a_q, a_s, s));
-        HIP_OK(moe::launch_permute(a_q, a_s, ids_c, w_c, on_in, Mc, (int)K, (int)T, expert_map,
-                                   P.num_global_experts, (int)El, P.align, pl.cap, bufA, bufAs, counts,
-                                   offsets, inv, rsrc, hist,
-                                   per_chunk_counts ? per_chunk_counts + c * El : nullptr, s));
+        // input quant fused into the permute's scatter
+        HIP_OK(moe::launch_quant_permute(x + t0 * K, ids_c, w_c, on_in, Mc, (int)K, (int)T, expert_map,
+                                         P.num_global_experts, (int)El, P.align, pl.cap, bufA, bufAs, counts,
+                                         offsets, inv, rsrc, hist,
+                                         per_chunk_counts ? per_chunk_counts + c * El : nullptr, s));
         HIP_OK(moe::launch_grouped_gemm(bufA, bufAs, w13, w13_s, offsets, counts, (int)El, pl.cap,
                                         (int)(2 * N), (int)K, hy, Mc * T, cus, s));
         HIP_OK(moe::launch_act_quant(hy, pl.cap, (int)N, moe::MOE_ACT_SILU_MUL_K, offsets, counts, (int)El,

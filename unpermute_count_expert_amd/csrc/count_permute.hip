@@ -151,8 +151,13 @@ __global__ __launch_bounds__(kScanThreads) void k_permute_colscan(int32_t* __res
 }
 
 // Stable rank of every local pair, inverse indices, then the row copies.
+// QUANT: the rows come from bf16 x [Mc, K] and are quantised here (per
+// 1x128 group, exactly as the identity act quant), so a_q / a_s are never
+// written or read; otherwise they are copied from a_q / a_s.
+template <bool QUANT>
 __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
-    const uint8_t* __restrict__ a_q, const float* __restrict__ a_s, const int32_t* __restrict__ ids,
+    const uint8_t* __restrict__ a_q, const float* __restrict__ a_s, const uint16_t* __restrict__ x,
+    const int32_t* __restrict__ ids,
     const float* __restrict__ topk_w, int apply_on_input, int64_t Mc, int K, int topk, int tpb,
     const int32_t* __restrict__ emap, int Eg, int El, int nbits, const int32_t* __restrict__ base,
     const int32_t* __restrict__ counts, int align, int64_t cap_rows, int32_t* __restrict__ offsets,
@@ -231,48 +236,94 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
     }
     __syncthreads();
 
-    // copies: each wave takes every fourth token of the block; a lane reads
-    // 16-byte chunks of the token rows, up to kBatch of them in flight at
-    // once, and writes each to the token's expert rows
-    constexpr int kBatch = 8;
     const int kg = K / kGroup;
-    const int nchunk = K / 16;
-    const int cpl = (nchunk + kWave - 1) / kWave;        // chunks per lane per token
     const int my_tokens = ntok > wave ? (ntok - wave + kWaves - 1) / kWaves : 0;
-    const int items = my_tokens * cpl;
-    for (int q0 = 0; q0 < items; q0 += kBatch) {
-        uint4 v[kBatch];
+    constexpr int kBatch = 8;
+    if constexpr (QUANT) {
+        // each wave takes every fourth token of the block; 16 lanes hold one
+        // 128-group (8 bf16 each), so a wave-wide load covers 4 groups of a
+        // token; up to kBatch such loads are in flight, then each group is
+        // quantised and its codes and scale written to the token's rows
+        const int sub = lane & 15;
+        const int gpi = (kg + 3) / 4;                 // 4-group slices per token
+        const int items = my_tokens * gpi;
+        for (int q0 = 0; q0 < items; q0 += kBatch) {
+            uint4 v[kBatch];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int q = q0 + u;
-            const int tl = wave + (q / cpl) * kWaves;
-            const int c = lane + (q % cpl) * kWave;
-            v[u] = uint4{0, 0, 0, 0};
-            if (q < items && c < nchunk)
-                v[u] = *reinterpret_cast<const uint4*>(a_q + (t0 + tl) * K + (int64_t)c * 16);
-        }
+            for (int u = 0; u < kBatch; ++u) {
+                const int q = q0 + u;
+                const int tl = wave + (q / gpi) * kWaves;
+                const int g = (q % gpi) * 4 + (lane >> 4);
+                v[u] = uint4{0, 0, 0, 0};
+                if (q < items && g < kg)
+                    v[u] = *reinterpret_cast<const uint4*>(x + (t0 + tl) * K + (int64_t)g * kGroup + sub * 8);
+            }
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int q = q0 + u;
-            const int tl = wave + (q / cpl) * kWaves;
-            const int c = lane + (q % cpl) * kWave;
-            if (q < items && c < nchunk) {
-                const int* rm = rowmap + tl * topk;
-                for (int k = 0; k < topk; ++k) {
-                    const int r = rm[k];
-                    if (r >= 0) *reinterpret_cast<uint4*>(a_perm + (int64_t)r * K + (int64_t)c * 16) = v[u];
+            for (int u = 0; u < kBatch; ++u) {
+                const int q = q0 + u;
+                const int tl = wave + (q / gpi) * kWaves;
+                const int g = (q % gpi) * 4 + (lane >> 4);
+                // every lane quantises (zeros past the end), so the group
+                // max shuffle always runs on whole 16-lane groups
+                float f[8];
+                bf16x8_to_f32(v[u], f);
+                uint2 codes;
+                const float scale = quant_group16(f, codes);
+                if (q < items && g < kg) {
+                    const int64_t t = t0 + tl;
+                    const int* rm = rowmap + tl * topk;
+                    for (int k = 0; k < topk; ++k) {
+                        const int r = rm[k];
+                        if (r >= 0) {
+                            *reinterpret_cast<uint2*>(a_perm + (int64_t)r * K + (int64_t)g * kGroup + sub * 8) = codes;
+                            if (sub == 0)
+                                a_perm_s[(int64_t)r * kg + g] = apply_on_input ? scale * topk_w[t * topk + k] : scale;
+                        }
+                    }
                 }
             }
         }
-    }
-    for (int tl = wave; tl < ntok; tl += kWaves) {
-        const int64_t t = t0 + tl;
-        const int* rm = rowmap + tl * topk;
-        for (int g = lane; g < kg; g += kWave) {
-            const float s = a_s[t * kg + g];
-            for (int k = 0; k < topk; ++k) {
-                const int r = rm[k];
-                if (r >= 0) a_perm_s[(int64_t)r * kg + g] = apply_on_input ? s * topk_w[t * topk + k] : s;
+    } else {
+        // copies: a lane reads 16-byte chunks of the token rows, up to
+        // kBatch of them in flight at once, and writes each to the token's
+        // expert rows
+        const int nchunk = K / 16;
+        const int cpl = (nchunk + kWave - 1) / kWave;        // chunks per lane per token
+        const int items = my_tokens * cpl;
+        for (int q0 = 0; q0 < items; q0 += kBatch) {
+            uint4 v[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int q = q0 + u;
+                const int tl = wave + (q / cpl) * kWaves;
+                const int c = lane + (q % cpl) * kWave;
+                v[u] = uint4{0, 0, 0, 0};
+                if (q < items && c < nchunk)
+                    v[u] = *reinterpret_cast<const uint4*>(a_q + (t0 + tl) * K + (int64_t)c * 16);
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int q = q0 + u;
+                const int tl = wave + (q / cpl) * kWaves;
+                const int c = lane + (q % cpl) * kWave;
+                if (q < items && c < nchunk) {
+                    const int* rm = rowmap + tl * topk;
+                    for (int k = 0; k < topk; ++k) {
+                        const int r = rm[k];
+                        if (r >= 0) *reinterpret_cast<uint4*>(a_perm + (int64_t)r * K + (int64_t)c * 16) = v[u];
+                    }
+                }
+            }
+        }
+        for (int tl = wave; tl < ntok; tl += kWaves) {
+            const int64_t t = t0 + tl;
+            const int* rm = rowmap + tl * topk;
+            for (int g = lane; g < kg; g += kWave) {
+                const float s = a_s[t * kg + g];
+                for (int k = 0; k < topk; ++k) {
+                    const int r = rm[k];
+                    if (r >= 0) a_perm_s[(int64_t)r * kg + g] = apply_on_input ? s * topk_w[t * topk + k] : s;
+                }
             }
         }
     }
@@ -313,9 +364,25 @@ hipError_t launch_permute(const uint8_t* a_q, const float* a_s, const int32_t* i
     k_permute_colscan<<<(unsigned)El, kScanThreads, 0, s>>>(hist, (int)nblk, El, counts, counts_copy);
     // at least one block, so that the offsets and padding marks are written
     // even for an empty chunk
-    k_permute_scatter<<<(unsigned)(nblk > 0 ? nblk : 1), kPermThreads, 0, s>>>(
-        a_q, a_s, ids, topk_w, apply_on_input, Mc, K, topk, tpb, emap, Eg, El, bits_for(El), hist, counts,
-        align, cap_rows, offsets, a_perm, a_perm_s, inv_perm, row_src);
+    k_permute_scatter<false><<<(unsigned)(nblk > 0 ? nblk : 1), kPermThreads, 0, s>>>(
+        a_q, a_s, nullptr, ids, topk_w, apply_on_input, Mc, K, topk, tpb, emap, Eg, El, bits_for(El), hist,
+        counts, align, cap_rows, offsets, a_perm, a_perm_s, inv_perm, row_src);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_permute(const uint16_t* x, const int32_t* ids, const float* topk_w, int apply_on_input,
+                                int64_t Mc, int K, int topk, const int32_t* emap, int Eg, int El, int align,
+                                int64_t cap_rows, uint8_t* a_perm, float* a_perm_s, int32_t* counts,
+                                int32_t* offsets, int32_t* inv_perm, int32_t* row_src, int32_t* hist,
+                                int32_t* counts_copy, hipStream_t s) {
+    const int tpb = permute_tokens_per_block(topk);
+    const int64_t nblk = permute_num_blocks(Mc, topk);
+    if (nblk > 0)
+        k_permute_hist<<<(unsigned)nblk, kPermThreads, 0, s>>>(ids, Mc, topk, tpb, emap, Eg, El, hist);
+    k_permute_colscan<<<(unsigned)El, kScanThreads, 0, s>>>(hist, (int)nblk, El, counts, counts_copy);
+    k_permute_scatter<true><<<(unsigned)(nblk > 0 ? nblk : 1), kPermThreads, 0, s>>>(
+        nullptr, nullptr, x, ids, topk_w, apply_on_input, Mc, K, topk, tpb, emap, Eg, El, bits_for(El), hist,
+        counts, align, cap_rows, offsets, a_perm, a_perm_s, inv_perm, row_src);
     return hipGetLastError();
 }
 

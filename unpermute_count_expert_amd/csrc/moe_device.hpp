@@ -72,6 +72,46 @@ __device__ __forceinline__ uint32_t f32x4_to_e4m3_bounded(float a, float b, floa
     return r;
 }
 
+// One 1x128 quantisation group held by 16 consecutive lanes, 8 values each
+// (lane l owns group elements 8*(l mod 16) .. +7): amax over the group (the
+// largest non-NaN magnitude, by compare-select, so quiet and signalling NaNs
+// are both skipped), d = max(amax, 1e-10), scale = d / 448, inv = 448 / d,
+// codes = e4m3(x * inv).  Every lane of the wave must call it (the group max
+// is an xor-shuffle inside each 16-lane group); returns the scale.
+__device__ __forceinline__ float quant_group16(const float (&x)[8], uint2& codes) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float a = __builtin_fabsf(x[i]);
+        amax = a > amax ? a : amax;
+    }
+#pragma unroll
+    for (int d = 8; d >= 1; d >>= 1) {
+        const float o = __shfl_xor(amax, d, kWave);
+        amax = o > amax ? o : amax;
+    }
+    const float dd = __builtin_fmaxf(amax, 1e-10f);
+    const float scale = dd / 448.0f;
+    const float inv = 448.0f / dd;
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = x[i] * inv;
+    // |t| <= 448 (1 + 2^-23) unless t is NaN: d >= every |x| of the group
+    codes.x = f32x4_to_e4m3_bounded(t[0], t[1], t[2], t[3]);
+    codes.y = f32x4_to_e4m3_bounded(t[4], t[5], t[6], t[7]);
+    return scale;
+}
+
+// eight bf16 values (one 16-byte load) as fp32
+__device__ __forceinline__ void bf16x8_to_f32(uint4 u, float (&v)[8]) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+
 // exp for SiLU, fixed operation by operation so that it is reproducible:
 // clamp to [-86, 88]; n = nearest-even(x / ln2); r = x - n*ln2 with ln2 in
 // two parts (Cody-Waite); Horner over the Taylor coefficients 1/k!, k<=7;

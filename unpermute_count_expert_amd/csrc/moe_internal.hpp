@@ -31,6 +31,14 @@ hipError_t launch_permute(const uint8_t* a_q, const float* a_s, const int32_t* i
                           uint8_t* a_perm, float* a_perm_s, int32_t* counts, int32_t* offsets,
                           int32_t* inv_perm, int32_t* row_src, int32_t* hist,
                           int32_t* counts_copy, hipStream_t s);
+// launch_permute with the input quantisation fused into the scatter: reads
+// bf16 x [Mc, K] and writes a_perm / a_perm_s exactly as launch_act_quant
+// (identity) followed by launch_permute would.
+hipError_t launch_quant_permute(const uint16_t* x, const int32_t* ids, const float* topk_w, int apply_on_input,
+                                int64_t Mc, int K, int topk, const int32_t* emap, int Eg, int El, int align,
+                                int64_t cap_rows, uint8_t* a_perm, float* a_perm_s, int32_t* counts,
+                                int32_t* offsets, int32_t* inv_perm, int32_t* row_src, int32_t* hist,
+                                int32_t* counts_copy, hipStream_t s);
 
 // ---- activation quantisation ------------------------------------------------
 hipError_t launch_act_quant(const uint16_t* in, int64_t rows, int n, int mode,

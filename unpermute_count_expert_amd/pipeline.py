@@ -1,10 +1,14 @@
 """The layer as a sequence of separate C-ABI calls, with every intermediate
 kept in its own buffer (for inspection, per-op timing and op-by-op checks).
 
-With fused=False the ops are exactly the kernels moe_forward_chunked runs,
-in its order (the gate/up GEMM writes h, a separate SiLU-mul requant
-follows); with fused=True the gate/up GEMM is the one fused with the SiLU-mul
-requant (moe_grouped_gemm_fp8_act_quant) and h never reaches memory.  The forward call runs on one reused workspace; this form trades
+With the defaults the ops are exactly the kernels moe_forward_chunked runs,
+in its order: the input quant fused into the permute (moe_quant_permute),
+the gate/up GEMM writing h, a separate SiLU-mul requant, the down GEMM and
+the unpermute (plus the standalone count, which the forward does inside the
+permute).  fused_input=False runs the input quant and the permute as two
+calls instead, keeping a_q / a_s; fused=True uses the gate/up GEMM fused with
+the SiLU-mul requant (moe_grouped_gemm_fp8_act_quant), so h never reaches
+memory.  The forward call runs on one reused workspace; this form trades
 memory for visibility.
 """
 from __future__ import annotations
@@ -36,16 +40,22 @@ class StepBuffers:
         self.count_only = e((El,), i32)
 
 
-def step_ops(layer, x, topk_ids, topk_weights, apply_on_input: int, b: StepBuffers, fused: bool = False):
+def step_ops(layer, x, topk_ids, topk_weights, apply_on_input: int, b: StepBuffers, fused: bool = False,
+             fused_input: bool = True):
     """Ordered {name: thunk}; running them in order computes the layer into b.out."""
     Eg, El, K, N, A = layer.Eg, layer.El, layer.K, layer.N, layer.align
     emap = layer.expert_map
     ops = OrderedDict()
-    ops["input_quant"] = lambda: _lib.moe_act_quant(x, K, _lib.MOE_ACT_IDENTITY, b.a_q, b.a_s)
     ops["count"] = lambda: _lib.moe_count(topk_ids, emap, Eg, El, b.count_only)
-    ops["permute"] = lambda: _lib.moe_permute(b.a_q, b.a_s, topk_ids, topk_weights, apply_on_input, emap, Eg,
-                                              El, A, b.cap, b.a_perm, b.a_perm_s, b.counts, b.offsets,
-                                              b.inv_perm, b.row_src, b.permute_ws)
+    if fused_input:
+        ops["quant_permute"] = lambda: _lib.moe_quant_permute(x, topk_ids, topk_weights, apply_on_input, emap, Eg,
+                                                              El, A, b.cap, b.a_perm, b.a_perm_s, b.counts,
+                                                              b.offsets, b.inv_perm, b.row_src, b.permute_ws)
+    else:
+        ops["input_quant"] = lambda: _lib.moe_act_quant(x, K, _lib.MOE_ACT_IDENTITY, b.a_q, b.a_s)
+        ops["permute"] = lambda: _lib.moe_permute(b.a_q, b.a_s, topk_ids, topk_weights, apply_on_input, emap, Eg,
+                                                  El, A, b.cap, b.a_perm, b.a_perm_s, b.counts, b.offsets,
+                                                  b.inv_perm, b.row_src, b.permute_ws)
     if fused:
         ops["gemm_w13_act"] = lambda: _lib.moe_grouped_gemm_fp8_act_quant(b.a_perm, b.a_perm_s, layer.w13,
                                                                           layer.w13_s, b.offsets, b.counts,
@@ -63,9 +73,9 @@ def step_ops(layer, x, topk_ids, topk_weights, apply_on_input: int, b: StepBuffe
 
 
 def run_steps(layer, x, topk_ids, topk_weights, apply_on_input: int = 0, b: StepBuffers = None,
-              fused: bool = False):
+              fused: bool = False, fused_input: bool = True):
     if b is None:
         b = StepBuffers(layer, x.shape[0], topk_ids.shape[1], x.device)
-    for fn in step_ops(layer, x, topk_ids, topk_weights, apply_on_input, b, fused).values():
+    for fn in step_ops(layer, x, topk_ids, topk_weights, apply_on_input, b, fused, fused_input).values():
         fn()
     return b
