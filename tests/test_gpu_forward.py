@@ -201,6 +201,9 @@ CASES = [
     ("C5u_on", gen.CONFIGS["C5u_on"], 1),
     ("C5h", gen.CONFIGS["C5h"], 0),
     ("C5h_on", gen.CONFIGS["C5h_on"], 1),
+    # the most local experts the library takes (1024), ~16 rows each
+    ("max_experts_1024", gen.small_config(M=2048, K=256, N=128, Eg=1024, El=1024, topk=8, chunk_size=0,
+                                          routing="softmax", seed=23), 0),
 ]
 
 

@@ -69,11 +69,10 @@ def test_identity_quant_parity(rows, n, scale):
     np.testing.assert_array_equal(q, qr)
 
 
-@pytest.mark.parametrize("masked", [False, True])
-def test_silu_mul_quant_parity(masked):
-    announce("silu quant masked" if masked else "silu quant")
+@pytest.mark.parametrize("masked,rows,n", [(False, 1000, 768), (True, 1000, 768), (False, 24, 32768)])
+def test_silu_mul_quant_parity(masked, rows, n):
+    announce("silu quant masked" if masked else "silu quant", rows, n)
     rng = np.random.default_rng(5)
-    rows, n = 1000, 768
     h = gen.bf16_bits((rng.standard_normal((rows, 2 * n)) * 4).astype(np.float32))
     # a few extreme gates: large positive / negative, exp clamp region, zeros
     h[0, :8] = gen.bf16_bits(np.array([100, -100, 88.5, -87, 0, -0.0, 1e-30, -3e4], np.float32))
@@ -357,6 +356,11 @@ def _spec_values():
     (3, 384, 768, [600, 1, 300], 128, 256),
     (2, 1536, 2048, [513, 256], 128, 256),
     (4, 640, 384, [0, 129, 767, 64], 64, 256),
+    # the largest k_in and n_out the library takes, and a long K loop on 256-row tiles
+    (1, 128, 65536, [33], 16, 128),
+    (1, 32768, 128, [70], 16, 128),
+    (1, 32768, 128, [600], 128, 256),
+    (2, 256, 16384, [300, 40], 128, 256),
 ])
 def test_gemm_random_parity(El, n_out, k_in, counts, align, tile):
     announce("gemm random", El, n_out, k_in, counts, align, tile)
