@@ -164,6 +164,7 @@ def _check_permute(g, r):
     (16384, 2048, 8, 128, 128, False, 128, 0, "uniform"),  # large batch
     (16384, 2048, 8, 128, 128, False, 128, 1, "hot"),
     (3, 256, 256, 300, 300, False, 16, 0, "random"),       # topk 256 (one token per block)
+    (2500, 2048, 8, 128, 128, False, 128, 1, "uniform"),   # 79 pair blocks x 6 uneven K slices
 ])
 def test_permute_parity(M, K, T, Eg, El, mapped, align, on_input, routing):
     announce("permute", M, K, T, Eg, El, mapped, align, on_input, routing)
@@ -211,6 +212,8 @@ def _gpu_quant_permute(x, ids, w, on_input, emap, Eg, El, align):
     (64, 2048, 4, 128, 64, True, 128, 0, "uniform", False),  # profiling shape
     (16384, 2048, 8, 128, 128, False, 128, 1, "uniform", False),
     (3, 128, 256, 300, 300, False, 16, 0, "random", True),   # topk 256, one group a token
+    (2500, 2048, 8, 128, 128, False, 128, 0, "uniform", False),  # 79 pair blocks x 6 uneven K slices
+    (130, 2048, 8, 128, 64, True, 128, 0, "uniform", True),  # 5 pair blocks x 16 K slices
 ])
 def test_quant_permute_parity(M, K, T, Eg, El, mapped, align, on_input, routing, special):
     """The input quant fused into the permute: bit-exact with the oracle's

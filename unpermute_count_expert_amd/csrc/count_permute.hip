@@ -7,11 +7,14 @@
 //   colscan one block per expert: exclusive scan of its column of the
 //           histogram (the block's first row within the expert's segment)
 //           and the expert's count
-//   scatter one block per 256 pairs: aligned offsets (every block scans the
-//           El counts itself; block 0 also publishes offsets and padding
-//           marks), wave-ballot ranks (stable in flat pair order), inverse
-//           indices, then each token row is read once and written to each of
-//           its expert rows with 16-byte lanes.
+//   scatter one block per 256 pairs and slice of the K groups: aligned
+//           offsets (every block scans the El counts itself; block (0, 0)
+//           also publishes offsets and padding marks), wave-ballot ranks
+//           (stable in flat pair order), inverse indices (written by the
+//           blocks of slice 0), then each token row slice is read once and
+//           written to each of its expert rows with 16-byte lanes.  Chunks
+//           of few tokens have few pair blocks, so their rows are split
+//           along K over up to 512 blocks in all.
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 
@@ -197,7 +200,7 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
         if (threadIdx.x == kPermThreads - 1) s_off[El] = run;
         __syncthreads();
     }
-    if (blockIdx.x == 0) {   // publish the offsets; mark padding rows and rows past the end
+    if (blockIdx.x == 0 && blockIdx.y == 0) {   // publish the offsets; mark padding rows and rows past the end
         for (int ex = threadIdx.x; ex <= El; ex += blockDim.x) offsets[ex] = s_off[ex];
         for (int ex = threadIdx.x; ex < El; ex += blockDim.x)
             for (int r = s_off[ex] + counts[ex]; r < s_off[ex + 1]; ++r) row_src[r] = -1;
@@ -230,46 +233,52 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
         row = s_off[e] + base[(int64_t)blockIdx.x * El + e] + pre + rank_w;
     }
     if (active) {
-        inv_perm[f] = row;
         rowmap[i] = row;
-        if (row >= 0) row_src[row] = (int32_t)(t0 + i / topk);
+        if (blockIdx.y == 0) {
+            inv_perm[f] = row;
+            if (row >= 0) row_src[row] = (int32_t)(t0 + i / topk);
+        }
     }
     __syncthreads();
 
+    // this block's slice of the K groups: [g_lo, g_lo + ng)
     const int kg = K / kGroup;
+    const int gps = (kg + (int)gridDim.y - 1) / (int)gridDim.y;
+    const int g_lo = min(kg, (int)blockIdx.y * gps);
+    const int ng = min(kg, g_lo + gps) - g_lo;
     const int my_tokens = ntok > wave ? (ntok - wave + kWaves - 1) / kWaves : 0;
     constexpr int kBatch = 8;
     if constexpr (QUANT) {
         // each wave takes every fourth token of the block; 16 lanes hold one
-        // 128-group (8 bf16 each), so a wave-wide load covers 4 groups of a
-        // token; up to kBatch such loads are in flight, then each group is
-        // quantised and its codes and scale written to the token's rows
+        // 128-group (8 bf16 each), so a wave-wide load covers 4 (token,
+        // group) items of the wave's tokens and the block's groups; up to
+        // kBatch such loads are in flight, then each group is quantised and
+        // its codes and scale written to the token's rows
         const int sub = lane & 15;
-        const int gpi = (kg + 3) / 4;                 // 4-group slices per token
-        const int items = my_tokens * gpi;
-        for (int q0 = 0; q0 < items; q0 += kBatch) {
+        const int items = my_tokens * ng;
+        for (int q0 = 0; q0 < items; q0 += 4 * kBatch) {
             uint4 v[kBatch];
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
-                const int q = q0 + u;
-                const int tl = wave + (q / gpi) * kWaves;
-                const int g = (q % gpi) * 4 + (lane >> 4);
+                const int q = q0 + 4 * u + (lane >> 4);
+                const int tl = wave + (q / ng) * kWaves;
+                const int g = g_lo + q % ng;
                 v[u] = uint4{0, 0, 0, 0};
-                if (q < items && g < kg)
+                if (q < items)
                     v[u] = *reinterpret_cast<const uint4*>(x + (t0 + tl) * K + (int64_t)g * kGroup + sub * 8);
             }
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
-                const int q = q0 + u;
-                const int tl = wave + (q / gpi) * kWaves;
-                const int g = (q % gpi) * 4 + (lane >> 4);
+                const int q = q0 + 4 * u + (lane >> 4);
+                const int tl = wave + (q / ng) * kWaves;
+                const int g = g_lo + q % ng;
                 // every lane quantises (zeros past the end), so the group
                 // max shuffle always runs on whole 16-lane groups
                 float f[8];
                 bf16x8_to_f32(v[u], f);
                 uint2 codes;
                 const float scale = quant_group16(f, codes);
-                if (q < items && g < kg) {
+                if (q < items) {
                     const int64_t t = t0 + tl;
                     const int* rm = rowmap + tl * topk;
                     for (int k = 0; k < topk; ++k) {
@@ -287,26 +296,28 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
         // copies: a lane reads 16-byte chunks of the token rows, up to
         // kBatch of them in flight at once, and writes each to the token's
         // expert rows
-        const int nchunk = K / 16;
-        const int cpl = (nchunk + kWave - 1) / kWave;        // chunks per lane per token
-        const int items = my_tokens * cpl;
-        for (int q0 = 0; q0 < items; q0 += kBatch) {
+        // (token, chunk) items over the wave's tokens and the block's 8 * ng
+        // chunks, one per lane
+        const int nch = ng * (kGroup / 16);
+        const int c_lo = g_lo * (kGroup / 16);
+        const int items = my_tokens * nch;
+        for (int q0 = 0; q0 < items; q0 += kWave * kBatch) {
             uint4 v[kBatch];
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
-                const int q = q0 + u;
-                const int tl = wave + (q / cpl) * kWaves;
-                const int c = lane + (q % cpl) * kWave;
+                const int q = q0 + u * kWave + lane;
+                const int tl = wave + (q / nch) * kWaves;
+                const int c = c_lo + q % nch;
                 v[u] = uint4{0, 0, 0, 0};
-                if (q < items && c < nchunk)
+                if (q < items)
                     v[u] = *reinterpret_cast<const uint4*>(a_q + (t0 + tl) * K + (int64_t)c * 16);
             }
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
-                const int q = q0 + u;
-                const int tl = wave + (q / cpl) * kWaves;
-                const int c = lane + (q % cpl) * kWave;
-                if (q < items && c < nchunk) {
+                const int q = q0 + u * kWave + lane;
+                const int tl = wave + (q / nch) * kWaves;
+                const int c = c_lo + q % nch;
+                if (q < items) {
                     const int* rm = rowmap + tl * topk;
                     for (int k = 0; k < topk; ++k) {
                         const int r = rm[k];
@@ -318,7 +329,7 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
         for (int tl = wave; tl < ntok; tl += kWaves) {
             const int64_t t = t0 + tl;
             const int* rm = rowmap + tl * topk;
-            for (int g = lane; g < kg; g += kWave) {
+            for (int g = g_lo + lane; g < g_lo + ng; g += kWave) {
                 const float s = a_s[t * kg + g];
                 for (int k = 0; k < topk; ++k) {
                     const int r = rm[k];
@@ -327,6 +338,18 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
             }
         }
     }
+}
+
+// (pair blocks, K slices): at least one block, so that the offsets and
+// padding marks are written even for an empty chunk; chunks of few pair
+// blocks split their rows along K so that up to 512 blocks share the copies
+dim3 scatter_grid(int64_t nblk, int K) {
+    const int64_t bx = nblk > 0 ? nblk : 1;
+    const int64_t kg = K / kGroup;
+    int64_t by = 512 / bx;
+    by = by < 1 ? 1 : (by > kg ? kg : by);
+    const int64_t gps = (kg + by - 1) / by;   // groups per slice; no slice left empty
+    return dim3((unsigned)bx, (unsigned)((kg + gps - 1) / gps), 1);
 }
 
 int bits_for(int El) {
@@ -364,7 +387,7 @@ hipError_t launch_permute(const uint8_t* a_q, const float* a_s, const int32_t* i
     k_permute_colscan<<<(unsigned)El, kScanThreads, 0, s>>>(hist, (int)nblk, El, counts, counts_copy);
     // at least one block, so that the offsets and padding marks are written
     // even for an empty chunk
-    k_permute_scatter<false><<<(unsigned)(nblk > 0 ? nblk : 1), kPermThreads, 0, s>>>(
+    k_permute_scatter<false><<<scatter_grid(nblk, K), kPermThreads, 0, s>>>(
         a_q, a_s, nullptr, ids, topk_w, apply_on_input, Mc, K, topk, tpb, emap, Eg, El, bits_for(El), hist,
         counts, align, cap_rows, offsets, a_perm, a_perm_s, inv_perm, row_src);
     return hipGetLastError();
@@ -380,7 +403,7 @@ hipError_t launch_quant_permute(const uint16_t* x, const int32_t* ids, const flo
     if (nblk > 0)
         k_permute_hist<<<(unsigned)nblk, kPermThreads, 0, s>>>(ids, Mc, topk, tpb, emap, Eg, El, hist);
     k_permute_colscan<<<(unsigned)El, kScanThreads, 0, s>>>(hist, (int)nblk, El, counts, counts_copy);
-    k_permute_scatter<true><<<(unsigned)(nblk > 0 ? nblk : 1), kPermThreads, 0, s>>>(
+    k_permute_scatter<true><<<scatter_grid(nblk, K), kPermThreads, 0, s>>>(
         nullptr, nullptr, x, ids, topk_w, apply_on_input, Mc, K, topk, tpb, emap, Eg, El, bits_for(El), hist,
         counts, align, cap_rows, offsets, a_perm, a_perm_s, inv_perm, row_src);
     return hipGetLastError();
