@@ -7,6 +7,8 @@
 //   colscan one block per expert: exclusive scan of its column of the
 //           histogram (the block's first row within the expert's segment)
 //           and the expert's count
+//   (chunks of at most 4096 pairs skip these two: each scatter block counts
+//   all the pairs itself)
 //   scatter one block per 256 pairs and slice of the K groups: aligned
 //           offsets (every block scans the El counts itself; block (0, 0)
 //           also publishes offsets and padding marks), wave-ballot ranks
@@ -163,7 +165,8 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
     const int32_t* __restrict__ ids,
     const float* __restrict__ topk_w, int apply_on_input, int64_t Mc, int K, int topk, int tpb,
     const int32_t* __restrict__ emap, int Eg, int El, int nbits, const int32_t* __restrict__ base,
-    const int32_t* __restrict__ counts, int align, int64_t cap_rows, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ counts, int32_t* __restrict__ counts_copy, int self_count, int align,
+    int64_t cap_rows, int32_t* __restrict__ offsets,
     uint8_t* __restrict__ a_perm, float* __restrict__ a_perm_s, int32_t* __restrict__ inv_perm,
     int32_t* __restrict__ row_src) {
     constexpr int kWaves = kPermThreads / kWave;
@@ -171,9 +174,34 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
     __shared__ int rowmap[kPermThreads];
     __shared__ int s_off[kMaxLocalExperts + 1];
     __shared__ int s_wsum[kWaves];
+    __shared__ int s_cnt[kMaxLocalExperts];    // self_count: the counts
+    __shared__ int s_base[kMaxLocalExperts];   // self_count: pairs of each expert before this block
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     for (int j = threadIdx.x; j < kWaves * El; j += blockDim.x) wcnt[j / El][j % El] = 0;
+    if (self_count) {
+        // few pairs: every block counts them all (no histogram launches)
+        for (int ex = threadIdx.x; ex < El; ex += blockDim.x) {
+            s_cnt[ex] = 0;
+            s_base[ex] = 0;
+        }
+        __syncthreads();
+        const int64_t np = Mc * topk;
+        const int64_t mine = (int64_t)blockIdx.x * tpb * topk;   // this block's first pair
+        for (int64_t f = threadIdx.x; f < np; f += blockDim.x) {
+            const int ex = local_expert(ids[f], emap, Eg, El);
+            if (ex >= 0) {
+                atomicAdd(&s_cnt[ex], 1);
+                if (f < mine) atomicAdd(&s_base[ex], 1);
+            }
+        }
+        __syncthreads();
+        if (blockIdx.x == 0 && blockIdx.y == 0)
+            for (int ex = threadIdx.x; ex < El; ex += blockDim.x) {
+                counts[ex] = s_cnt[ex];
+                if (counts_copy) counts_copy[ex] = s_cnt[ex];
+            }
+    }
 
     // aligned segment offsets: exclusive scan of align * ceil(counts / align)
     // over the experts, four experts per thread
@@ -182,7 +210,7 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int ex = threadIdx.x * 4 + j;
-            const int c = ex < El ? counts[ex] : 0;
+            const int c = ex < El ? (self_count ? s_cnt[ex] : counts[ex]) : 0;
             seg[j] = ((c + align - 1) / align) * align;
             tsum += seg[j];
         }
@@ -203,7 +231,7 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
     if (blockIdx.x == 0 && blockIdx.y == 0) {   // publish the offsets; mark padding rows and rows past the end
         for (int ex = threadIdx.x; ex <= El; ex += blockDim.x) offsets[ex] = s_off[ex];
         for (int ex = threadIdx.x; ex < El; ex += blockDim.x)
-            for (int r = s_off[ex] + counts[ex]; r < s_off[ex + 1]; ++r) row_src[r] = -1;
+            for (int r = s_off[ex] + (self_count ? s_cnt[ex] : counts[ex]); r < s_off[ex + 1]; ++r) row_src[r] = -1;
         for (int64_t r = s_off[El] + threadIdx.x; r < cap_rows; r += blockDim.x) row_src[r] = -1;
     }
 
@@ -230,7 +258,7 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
     if (e >= 0) {
         int pre = 0;
         for (int w = 0; w < wave; ++w) pre += wcnt[w][e];
-        row = s_off[e] + base[(int64_t)blockIdx.x * El + e] + pre + rank_w;
+        row = s_off[e] + (self_count ? s_base[e] : base[(int64_t)blockIdx.x * El + e]) + pre + rank_w;
     }
     if (active) {
         rowmap[i] = row;
@@ -340,6 +368,12 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
     }
 }
 
+// Up to 16 pair blocks (4096 pairs) every scatter block reads all the ids
+// itself for the counts and its per-expert row bases, which saves the
+// histogram and column-scan launches; beyond that the reads would grow with
+// the square of the pair count.
+int permute_self_count(int64_t nblk) { return nblk <= 16 ? 1 : 0; }
+
 // (pair blocks, K slices): at least one block, so that the offsets and
 // padding marks are written even for an empty chunk; chunks of few pair
 // blocks split their rows along K so that up to 512 blocks share the copies
@@ -382,14 +416,14 @@ hipError_t launch_permute(const uint8_t* a_q, const float* a_s, const int32_t* i
                           int32_t* counts_copy, hipStream_t s) {
     const int tpb = permute_tokens_per_block(topk);
     const int64_t nblk = permute_num_blocks(Mc, topk);
-    if (nblk > 0)
+    const int self = permute_self_count(nblk);
+    if (!self) {
         k_permute_hist<<<(unsigned)nblk, kPermThreads, 0, s>>>(ids, Mc, topk, tpb, emap, Eg, El, hist);
-    k_permute_colscan<<<(unsigned)El, kScanThreads, 0, s>>>(hist, (int)nblk, El, counts, counts_copy);
-    // at least one block, so that the offsets and padding marks are written
-    // even for an empty chunk
+        k_permute_colscan<<<(unsigned)El, kScanThreads, 0, s>>>(hist, (int)nblk, El, counts, counts_copy);
+    }
     k_permute_scatter<false><<<scatter_grid(nblk, K), kPermThreads, 0, s>>>(
         a_q, a_s, nullptr, ids, topk_w, apply_on_input, Mc, K, topk, tpb, emap, Eg, El, bits_for(El), hist,
-        counts, align, cap_rows, offsets, a_perm, a_perm_s, inv_perm, row_src);
+        counts, counts_copy, self, align, cap_rows, offsets, a_perm, a_perm_s, inv_perm, row_src);
     return hipGetLastError();
 }
 
@@ -400,12 +434,14 @@ hipError_t launch_quant_permute(const uint16_t* x, const int32_t* ids, const flo
                                 int32_t* counts_copy, hipStream_t s) {
     const int tpb = permute_tokens_per_block(topk);
     const int64_t nblk = permute_num_blocks(Mc, topk);
-    if (nblk > 0)
+    const int self = permute_self_count(nblk);
+    if (!self) {
         k_permute_hist<<<(unsigned)nblk, kPermThreads, 0, s>>>(ids, Mc, topk, tpb, emap, Eg, El, hist);
-    k_permute_colscan<<<(unsigned)El, kScanThreads, 0, s>>>(hist, (int)nblk, El, counts, counts_copy);
+        k_permute_colscan<<<(unsigned)El, kScanThreads, 0, s>>>(hist, (int)nblk, El, counts, counts_copy);
+    }
     k_permute_scatter<true><<<scatter_grid(nblk, K), kPermThreads, 0, s>>>(
         nullptr, nullptr, x, ids, topk_w, apply_on_input, Mc, K, topk, tpb, emap, Eg, El, bits_for(El), hist,
-        counts, align, cap_rows, offsets, a_perm, a_perm_s, inv_perm, row_src);
+        counts, counts_copy, self, align, cap_rows, offsets, a_perm, a_perm_s, inv_perm, row_src);
     return hipGetLastError();
 }
 
