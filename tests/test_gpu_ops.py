@@ -165,6 +165,9 @@ def _check_permute(g, r):
     (16384, 2048, 8, 128, 128, False, 128, 1, "hot"),
     (3, 256, 256, 300, 300, False, 16, 0, "random"),       # topk 256 (one token per block)
     (2500, 2048, 8, 128, 128, False, 128, 1, "uniform"),   # 79 pair blocks x 6 uneven K slices
+    (512, 256, 8, 64, 40, True, 32, 0, "random"),          # 16 pair blocks: counted in the scatter
+    (513, 256, 8, 64, 40, True, 32, 1, "random"),          # 17: histogram and column scan
+    (100, 256, 4, 5000, 64, True, 16, 0, "random"),        # expert map too large for LDS
 ])
 def test_permute_parity(M, K, T, Eg, El, mapped, align, on_input, routing):
     announce("permute", M, K, T, Eg, El, mapped, align, on_input, routing)
@@ -214,6 +217,8 @@ def _gpu_quant_permute(x, ids, w, on_input, emap, Eg, El, align):
     (3, 128, 256, 300, 300, False, 16, 0, "random", True),   # topk 256, one group a token
     (2500, 2048, 8, 128, 128, False, 128, 0, "uniform", False),  # 79 pair blocks x 6 uneven K slices
     (130, 2048, 8, 128, 64, True, 128, 0, "uniform", True),  # 5 pair blocks x 16 K slices
+    (512, 384, 8, 64, 40, True, 64, 1, "random", False),     # 16 pair blocks: counted in the scatter
+    (513, 384, 8, 64, 40, True, 64, 0, "random", False),     # 17: histogram and column scan
 ])
 def test_quant_permute_parity(M, K, T, Eg, El, mapped, align, on_input, routing, special):
     """The input quant fused into the permute: bit-exact with the oracle's

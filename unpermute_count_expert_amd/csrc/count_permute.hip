@@ -24,6 +24,7 @@ namespace moe {
 namespace {
 
 constexpr int kPermThreads = 256;
+constexpr int kMapLds = 2048;   // expert maps of up to this many global experts are staged in LDS
 constexpr int kScanThreads = 1024;
 constexpr int kScanWaves = kScanThreads / kWave;
 
@@ -170,29 +171,102 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
     uint8_t* __restrict__ a_perm, float* __restrict__ a_perm_s, int32_t* __restrict__ inv_perm,
     int32_t* __restrict__ row_src) {
     constexpr int kWaves = kPermThreads / kWave;
+    constexpr int kBatch = 8;
+    constexpr int kSelfLoads = 16;   // self_count: at most 16 * 256 pairs
     __shared__ int wcnt[kWaves][kMaxLocalExperts];
     __shared__ int rowmap[kPermThreads];
     __shared__ int s_off[kMaxLocalExperts + 1];
     __shared__ int s_wsum[kWaves];
     __shared__ int s_cnt[kMaxLocalExperts];    // self_count: the counts
     __shared__ int s_base[kMaxLocalExperts];   // self_count: pairs of each expert before this block
+    __shared__ int s_map[kMapLds];             // expert_map, when it fits
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    for (int j = threadIdx.x; j < kWaves * El; j += blockDim.x) wcnt[j / El][j % El] = 0;
+
+    // ---- everything read from global memory up front, so that the
+    // latencies overlap: this block's ids, the expert map, the pair ids of the
+    // whole chunk (self_count) and the first batch of token rows
+    const int64_t t0 = (int64_t)blockIdx.x * tpb;
+    const int ntok = (int)((Mc - t0) < tpb ? (Mc - t0) : tpb);
+    const int npairs = ntok * topk;
+    const int i = threadIdx.x;
+    const bool active = i < npairs;
+    const int64_t f = t0 * topk + i;
+    const int own_id = active ? ids[f] : -1;
+    const bool map_lds = emap != nullptr && Eg <= kMapLds;
+    if (map_lds)
+        for (int j = threadIdx.x; j < Eg; j += blockDim.x) s_map[j] = emap[j];
+    const int64_t np = Mc * topk;
+    int sid[kSelfLoads];
     if (self_count) {
-        // few pairs: every block counts them all (no histogram launches)
+#pragma unroll
+        for (int u = 0; u < kSelfLoads; ++u) {
+            const int64_t f2 = threadIdx.x + (int64_t)u * kPermThreads;
+            sid[u] = f2 < np ? ids[f2] : -1;
+        }
+    }
+    // this block's slice of the K groups: [g_lo, g_lo + ng)
+    const int kg = K / kGroup;
+    const int gps = (kg + (int)gridDim.y - 1) / (int)gridDim.y;
+    const int g_lo = min(kg, (int)blockIdx.y * gps);
+    const int ng = min(kg, g_lo + gps) - g_lo;
+    const int my_tokens = ntok > wave ? (ntok - wave + kWaves - 1) / kWaves : 0;
+    // QUANT: each wave takes every fourth token of the block; 16 lanes hold
+    // one 128-group (8 bf16 each), so a wave-wide load covers 4 (token,
+    // group) items of the wave's tokens and the block's groups.  Copies:
+    // (token, 16-byte chunk) items over the wave's tokens and the block's
+    // 8 * ng chunks, one per lane.  Up to kBatch loads per lane are in flight.
+    const int sub = lane & 15;
+    const int nch = ng * (kGroup / 16);
+    const int c_lo = g_lo * (kGroup / 16);
+    const int items = QUANT ? my_tokens * ng : my_tokens * nch;
+    const int istep = QUANT ? 4 * kBatch : kWave * kBatch;
+    auto item = [&](int q0, int u, int& tl, int& gc) __attribute__((always_inline)) {
+        const int q = QUANT ? q0 + 4 * u + (lane >> 4) : q0 + u * kWave + lane;
+        const int per = QUANT ? ng : nch;
+        tl = wave + (q / per) * kWaves;
+        gc = (QUANT ? g_lo : c_lo) + q % per;
+        return q;
+    };
+    auto load_batch = [&](int q0, uint4 (&v)[kBatch]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            int tl, gc;
+            const int q = item(q0, u, tl, gc);
+            v[u] = uint4{0, 0, 0, 0};
+            if (q < items) {
+                if constexpr (QUANT)
+                    v[u] = *reinterpret_cast<const uint4*>(x + (t0 + tl) * K + (int64_t)gc * kGroup + sub * 8);
+                else
+                    v[u] = *reinterpret_cast<const uint4*>(a_q + (t0 + tl) * K + (int64_t)gc * 16);
+            }
+        }
+    };
+    uint4 v[kBatch];
+    load_batch(0, v);
+
+    auto loc = [&](int id) __attribute__((always_inline)) {
+        if (id < 0 || id >= Eg) return -1;
+        const int ex = map_lds ? s_map[id] : (emap ? emap[id] : id);
+        return (ex >= 0 && ex < El) ? ex : -1;
+    };
+    for (int j = threadIdx.x; j < kWaves * El; j += blockDim.x) wcnt[j / El][j % El] = 0;
+    if (self_count)
         for (int ex = threadIdx.x; ex < El; ex += blockDim.x) {
             s_cnt[ex] = 0;
             s_base[ex] = 0;
         }
-        __syncthreads();
-        const int64_t np = Mc * topk;
+    __syncthreads();   // s_map, wcnt, s_cnt, s_base ready
+    if (self_count) {
+        // few pairs: every block counts them all (no histogram launches)
         const int64_t mine = (int64_t)blockIdx.x * tpb * topk;   // this block's first pair
-        for (int64_t f = threadIdx.x; f < np; f += blockDim.x) {
-            const int ex = local_expert(ids[f], emap, Eg, El);
+#pragma unroll
+        for (int u = 0; u < kSelfLoads; ++u) {
+            const int64_t f2 = threadIdx.x + (int64_t)u * kPermThreads;
+            const int ex = loc(sid[u]);
             if (ex >= 0) {
                 atomicAdd(&s_cnt[ex], 1);
-                if (f < mine) atomicAdd(&s_base[ex], 1);
+                if (f2 < mine) atomicAdd(&s_base[ex], 1);
             }
         }
         __syncthreads();
@@ -230,19 +304,15 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
     }
     if (blockIdx.x == 0 && blockIdx.y == 0) {   // publish the offsets; mark padding rows and rows past the end
         for (int ex = threadIdx.x; ex <= El; ex += blockDim.x) offsets[ex] = s_off[ex];
-        for (int ex = threadIdx.x; ex < El; ex += blockDim.x)
-            for (int r = s_off[ex] + (self_count ? s_cnt[ex] : counts[ex]); r < s_off[ex + 1]; ++r) row_src[r] = -1;
+        // one wave per expert, its lanes on consecutive padding rows
+        for (int ex = wave; ex < El; ex += kWaves) {
+            const int pad_lo = s_off[ex] + (self_count ? s_cnt[ex] : counts[ex]);
+            for (int r = pad_lo + lane; r < s_off[ex + 1]; r += kWave) row_src[r] = -1;
+        }
         for (int64_t r = s_off[El] + threadIdx.x; r < cap_rows; r += blockDim.x) row_src[r] = -1;
     }
 
-    const int64_t t0 = (int64_t)blockIdx.x * tpb;
-    const int ntok = (int)((Mc - t0) < tpb ? (Mc - t0) : tpb);
-    const int npairs = ntok * topk;
-    const int i = threadIdx.x;
-    const bool active = i < npairs;
-    const int64_t f = t0 * topk + i;
-    const int e = active ? local_expert(ids[f], emap, Eg, El) : -1;
-
+    const int e = active ? loc(own_id) : -1;
     // lanes of this wave with the same expert (multisplit over the id bits)
     uint64_t peers = ballot(e >= 0);
     for (int bit = 0; bit < nbits; ++bit) {
@@ -251,7 +321,6 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
         peers &= b ? m : ~m;
     }
     const int rank_w = __popcll(peers & lanemask_lt());
-    __syncthreads();  // wcnt zeroed
     if (e >= 0 && rank_w == 0) wcnt[wave][e] = __popcll(peers);
     __syncthreads();
     int row = -1;
@@ -269,43 +338,20 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
     }
     __syncthreads();
 
-    // this block's slice of the K groups: [g_lo, g_lo + ng)
-    const int kg = K / kGroup;
-    const int gps = (kg + (int)gridDim.y - 1) / (int)gridDim.y;
-    const int g_lo = min(kg, (int)blockIdx.y * gps);
-    const int ng = min(kg, g_lo + gps) - g_lo;
-    const int my_tokens = ntok > wave ? (ntok - wave + kWaves - 1) / kWaves : 0;
-    constexpr int kBatch = 8;
-    if constexpr (QUANT) {
-        // each wave takes every fourth token of the block; 16 lanes hold one
-        // 128-group (8 bf16 each), so a wave-wide load covers 4 (token,
-        // group) items of the wave's tokens and the block's groups; up to
-        // kBatch such loads are in flight, then each group is quantised and
-        // its codes and scale written to the token's rows
-        const int sub = lane & 15;
-        const int items = my_tokens * ng;
-        for (int q0 = 0; q0 < items; q0 += 4 * kBatch) {
-            uint4 v[kBatch];
+    // ---- the row copies, batch 0 already loaded
+    for (int q0 = 0; q0 < items; q0 += istep) {
+        if (q0 > 0) load_batch(q0, v);
+        if constexpr (QUANT) {
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
-                const int q = q0 + 4 * u + (lane >> 4);
-                const int tl = wave + (q / ng) * kWaves;
-                const int g = g_lo + q % ng;
-                v[u] = uint4{0, 0, 0, 0};
-                if (q < items)
-                    v[u] = *reinterpret_cast<const uint4*>(x + (t0 + tl) * K + (int64_t)g * kGroup + sub * 8);
-            }
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int q = q0 + 4 * u + (lane >> 4);
-                const int tl = wave + (q / ng) * kWaves;
-                const int g = g_lo + q % ng;
+                int tl, g;
+                const int q = item(q0, u, tl, g);
                 // every lane quantises (zeros past the end), so the group
                 // max shuffle always runs on whole 16-lane groups
-                float f[8];
-                bf16x8_to_f32(v[u], f);
+                float fv[8];
+                bf16x8_to_f32(v[u], fv);
                 uint2 codes;
-                const float scale = quant_group16(f, codes);
+                const float scale = quant_group16(fv, codes);
                 if (q < items) {
                     const int64_t t = t0 + tl;
                     const int* rm = rowmap + tl * topk;
@@ -319,32 +365,11 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
                     }
                 }
             }
-        }
-    } else {
-        // copies: a lane reads 16-byte chunks of the token rows, up to
-        // kBatch of them in flight at once, and writes each to the token's
-        // expert rows
-        // (token, chunk) items over the wave's tokens and the block's 8 * ng
-        // chunks, one per lane
-        const int nch = ng * (kGroup / 16);
-        const int c_lo = g_lo * (kGroup / 16);
-        const int items = my_tokens * nch;
-        for (int q0 = 0; q0 < items; q0 += kWave * kBatch) {
-            uint4 v[kBatch];
+        } else {
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
-                const int q = q0 + u * kWave + lane;
-                const int tl = wave + (q / nch) * kWaves;
-                const int c = c_lo + q % nch;
-                v[u] = uint4{0, 0, 0, 0};
-                if (q < items)
-                    v[u] = *reinterpret_cast<const uint4*>(a_q + (t0 + tl) * K + (int64_t)c * 16);
-            }
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int q = q0 + u * kWave + lane;
-                const int tl = wave + (q / nch) * kWaves;
-                const int c = c_lo + q % nch;
+                int tl, c;
+                const int q = item(q0, u, tl, c);
                 if (q < items) {
                     const int* rm = rowmap + tl * topk;
                     for (int k = 0; k < topk; ++k) {
@@ -354,6 +379,8 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
                 }
             }
         }
+    }
+    if constexpr (!QUANT) {
         for (int tl = wave; tl < ntok; tl += kWaves) {
             const int64_t t = t0 + tl;
             const int* rm = rowmap + tl * topk;
