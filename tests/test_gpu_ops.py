@@ -97,6 +97,30 @@ def test_silu_mul_quant_parity(masked, rows, n):
         assert np.all(qg[other] == 0xAB) and np.all(sg[other] == -7.0)
 
 
+@pytest.mark.parametrize("up", ["one", "random"])
+def test_silu_mul_quant_every_bf16_gate(up):
+    """Every one of the 65536 bf16 gate patterns (zeros, subnormals, the
+    tabulated range, huge values, infinities, NaNs), sorted and shuffled into
+    groups, with up = 1 or random: codes and scales bit-exact with the
+    oracle's SiLU formula."""
+    announce("silu quant all bf16 gates", up)
+    rng = np.random.default_rng(11)
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    gates = np.concatenate([pats, rng.permutation(pats)]).reshape(-1, 128)
+    if up == "one":
+        ups = np.full(gates.shape, 0x3F80, np.uint16)
+    else:
+        ups = gen.bf16_bits(rng.standard_normal(gates.shape).astype(np.float32))
+    h = np.concatenate([gates, ups], axis=1)
+    rows, n = gates.shape
+    q = filled((rows, n), torch.uint8, 0xAB)
+    sc = filled((rows, n // 128), torch.float32, -7.0)
+    moe.moe_act_quant(dev(h), n, moe.MOE_ACT_SILU_MUL, q, sc)
+    qr, sr = oracle.silu_mul_quant(h, None, None, 0)
+    np.testing.assert_array_equal(host(sc), sr)
+    np.testing.assert_array_equal(host(q), qr)
+
+
 # ---------------------------------------------------------------- count
 @pytest.mark.parametrize("M,T,Eg,El,mapped,p_neg,p_bad", [
     (64, 4, 128, 64, True, 0.0, 0.0),

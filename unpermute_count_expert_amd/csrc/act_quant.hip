@@ -7,6 +7,14 @@
 // group amax is a 4-step xor-shuffle inside the 16 lanes; codes leave as one
 // 8-byte store per lane.  Compiled without FMA contraction so each operation
 // below is the IEEE operation written.
+//
+// SiLU of a bf16 gate value is a function of 16 bits, so each block first
+// tabulates silu(g) = g / (1 + exp(-g)) in LDS, with the same pinned exp and
+// IEEE division, for every g with 2^-12 <= |g| < 2^8 (5120 values, 20 KB),
+// and then looks the gate values up; the few others (zeros, tiny and huge
+// values, infinities, NaN) take the formula itself.  The table holds the
+// formula's own results, so the codes are the same bit for bit, and the
+// kernel no longer spends ~40 VALU instructions per element on it.
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 
@@ -16,6 +24,27 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kLanesPerGroup = 16;
 constexpr int kGroupsPerBlock = kThreads / kLanesPerGroup;
+
+// SiLU table: bf16 gate values with biased exponent in [kSiluExpLo,
+// kSiluExpLo + kSiluExps), both signs; entry (sign * kSiluExps + exp -
+// kSiluExpLo) * 128 + mantissa.
+constexpr int kSiluExpLo = 127 - 12;
+constexpr int kSiluExps = 20;
+constexpr int kSiluHalf = kSiluExps * 128;
+constexpr int kSiluEntries = 2 * kSiluHalf;
+
+__device__ __forceinline__ float silu_pinned(float g) {
+    const float e = exp_pinned(-g);
+    return g / (1.0f + e);
+}
+
+// silu of the bf16 value with bits hb (as fp32: hb << 16), from the table
+// when it covers hb
+__device__ __forceinline__ float silu_bf16(const float* __restrict__ tab, uint32_t hb) {
+    const uint32_t t = (hb & 0x7fffu) - (uint32_t)(kSiluExpLo << 7);
+    if (__builtin_expect(t < (uint32_t)kSiluHalf, 1)) return tab[t + (hb >> 15) * kSiluHalf];
+    return silu_pinned(__uint_as_float(hb << 16));
+}
 
 struct Vals8 {
     float v[8];
@@ -40,11 +69,18 @@ __global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restri
                                                         float* __restrict__ q_s) {
     __shared__ int s_off[kMaxLocalExperts + 1];
     __shared__ int s_end[kMaxLocalExperts];
+    __shared__ float s_silu[MODE == MOE_ACT_SILU_MUL_K ? kSiluEntries : 1];
     const bool masked = offsets != nullptr;
     if (masked) {
         for (int e = threadIdx.x; e <= El; e += blockDim.x) s_off[e] = offsets[e];
         for (int e = threadIdx.x; e < El; e += blockDim.x) s_end[e] = offsets[e] + counts[e];
     }
+    if (MODE == MOE_ACT_SILU_MUL_K)
+        for (int j = threadIdx.x; j < kSiluEntries; j += blockDim.x) {
+            const uint32_t hb = ((uint32_t)(j >= kSiluHalf) << 15) |
+                                (uint32_t)((kSiluExpLo << 7) + (j >= kSiluHalf ? j - kSiluHalf : j));
+            s_silu[j] = silu_pinned(__uint_as_float(hb << 16));
+        }
     __syncthreads();
     const int ng = n / kGroup;
     const int64_t total = rows * ng;
@@ -105,14 +141,14 @@ __global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restri
             x = unpack_bf16x8(u);
         } else {
             const uint16_t* base = in + r_this * 2 * (int64_t)n + gi_this * kGroup + sub * 8;
-            const Vals8 g = unpack_bf16x8(*reinterpret_cast<const uint4*>(base));
+            const uint4 gw = *reinterpret_cast<const uint4*>(base);
             const Vals8 u = unpack_bf16x8(*reinterpret_cast<const uint4*>(base + n));
+            const uint32_t gbits[4] = {gw.x, gw.y, gw.z, gw.w};
             float prod[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float e = exp_pinned(-g.v[i]);
-                const float s = g.v[i] / (1.0f + e);
-                prod[i] = s * u.v[i];
+            for (int i = 0; i < 4; ++i) {
+                prod[2 * i] = silu_bf16(s_silu, gbits[i] & 0xffffu) * u.v[2 * i];
+                prod[2 * i + 1] = silu_bf16(s_silu, gbits[i] >> 16) * u.v[2 * i + 1];
             }
             // the activation is rounded to bf16 before it is quantised
 #pragma unroll
@@ -139,7 +175,10 @@ hipError_t launch_act_quant(const uint16_t* in, int64_t rows, int n, int mode,
     const int64_t groups = rows * (n / kGroup);
     if (groups <= 0) return hipSuccess;
     int64_t blocks = (groups + kGroupsPerBlock - 1) / kGroupsPerBlock;
-    if (blocks > 8192) blocks = 8192;
+    // SiLU-mul: each block builds the 5120-entry SiLU table, so fewer, longer
+    // blocks (the table costs a block as much as ~90 groups)
+    const int64_t cap = mode == MOE_ACT_IDENTITY_K ? 8192 : 1024;
+    if (blocks > cap) blocks = cap;
     if (mode == MOE_ACT_IDENTITY_K)
         k_act_quant<MOE_ACT_IDENTITY_K><<<(unsigned)blocks, kThreads, 0, s>>>(in, rows, n, offsets, counts,
                                                                              El, q, q_s);
