@@ -25,26 +25,6 @@ constexpr int kThreads = 256;
 constexpr int kLanesPerGroup = 16;
 constexpr int kGroupsPerBlock = kThreads / kLanesPerGroup;
 
-// SiLU table: bf16 gate values with biased exponent in [kSiluExpLo,
-// kSiluExpLo + kSiluExps), both signs; entry (sign * kSiluExps + exp -
-// kSiluExpLo) * 128 + mantissa.
-constexpr int kSiluExpLo = 127 - 12;
-constexpr int kSiluExps = 20;
-constexpr int kSiluHalf = kSiluExps * 128;
-constexpr int kSiluEntries = 2 * kSiluHalf;
-
-__device__ __forceinline__ float silu_pinned(float g) {
-    const float e = exp_pinned(-g);
-    return g / (1.0f + e);
-}
-
-// silu of the bf16 value with bits hb (as fp32: hb << 16), from the table
-// when it covers hb
-__device__ __forceinline__ float silu_bf16(const float* __restrict__ tab, uint32_t hb) {
-    const uint32_t t = (hb & 0x7fffu) - (uint32_t)(kSiluExpLo << 7);
-    if (__builtin_expect(t < (uint32_t)kSiluHalf, 1)) return tab[t + (hb >> 15) * kSiluHalf];
-    return silu_pinned(__uint_as_float(hb << 16));
-}
 
 struct Vals8 {
     float v[8];
@@ -75,12 +55,7 @@ __global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restri
         for (int e = threadIdx.x; e <= El; e += blockDim.x) s_off[e] = offsets[e];
         for (int e = threadIdx.x; e < El; e += blockDim.x) s_end[e] = offsets[e] + counts[e];
     }
-    if (MODE == MOE_ACT_SILU_MUL_K)
-        for (int j = threadIdx.x; j < kSiluEntries; j += blockDim.x) {
-            const uint32_t hb = ((uint32_t)(j >= kSiluHalf) << 15) |
-                                (uint32_t)((kSiluExpLo << 7) + (j >= kSiluHalf ? j - kSiluHalf : j));
-            s_silu[j] = silu_pinned(__uint_as_float(hb << 16));
-        }
+    if (MODE == MOE_ACT_SILU_MUL_K) silu_table_build(s_silu);
     __syncthreads();
     const int ng = n / kGroup;
     const int64_t total = rows * ng;

@@ -337,7 +337,7 @@ int moe_grouped_gemm_fp8_act_quant(const uint8_t* a, const float* a_s, const uin
     int st = check_device(&cus);
     if (st) return st;
     HIP_OK(moe::launch_grouped_gemm_act(a, a_s, w13, w13_s, expert_offsets, counts, El, cap_rows, N, k_in, q,
-                                        q_s, cus, static_cast<hipStream_t>(stream)));
+                                        q_s, cap_rows, cus, static_cast<hipStream_t>(stream)));
     return MOE_OK;
 }
 

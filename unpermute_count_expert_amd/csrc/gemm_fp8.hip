@@ -248,8 +248,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
     using Sh = Shape<MI>;
     constexpr int BM = Sh::BM, kStageA = Sh::kStageA, kStage = Sh::kStage, kStages = Sh::kStages;
     constexpr int kADma = Sh::kADma, kDmaPerStep = Sh::kDmaPerStep, kScaleRows = Sh::kScaleRows;
-    static_assert(!KACT || MI == 4, "the fused epilogue is laid out for 128-row tiles");
+    // the 256-row fused kernel has room for the SiLU table next to its two
+    // 64 KB stages; the 128-row one, with three 48 KB stages, computes SiLU
+    constexpr bool kSiluLds = KACT && MI == 8;
     __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStage];
+    __shared__ float s_silu[kSiluLds ? kSiluEntries : 1];
     __shared__ __attribute__((aligned(16))) float sAs[kStages][BM];   // [stage][row]
     __shared__ int s_tpre[kMaxLocalExperts + 1];
     __shared__ int s_wsum[kWaves];
@@ -259,6 +262,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    if constexpr (kSiluLds) silu_table_build(s_silu);   // published by the barriers below
 
     // ---- m-tile prefix over the experts' valid row counts ------------------
     int ntl[2];
@@ -496,23 +500,31 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
             }
         } else {
             // ---- epilogue: SiLU-and-mul and per-128 requant ----------------
-            // This lane holds, for 16 rows, act columns 2fr and 2fr+1 of the
-            // wave's 32-column slice (gate in blocks 0/1, up in 2/3).  The
-            // group of a row is the tile's 128 act columns, spread over the
-            // 16 lanes of a row quad and the 4 waves of the same wm.
+            // This lane holds, for 4 * MI rows, act columns 2fr and 2fr+1 of
+            // the wave's 32-column slice (gate in blocks 0/1, up in 2/3).
+            // The group of a row is the tile's 128 act columns, spread over
+            // the 16 lanes of a row quad and the 4 waves of the same wm.
             const int j = cur.n0 >> 8;   // act column block
-            float act[4][4][2];
-            float amax[4][4];
+            float act[MI][4][2];
+            float amax[MI][4];
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
+            for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const uint32_t hg = f32x2_to_bf16x2(acc[mi][0][v], acc[mi][1][v]);
                     const uint32_t hu = f32x2_to_bf16x2(acc[mi][2][v], acc[mi][3][v]);
                     const float g0 = __uint_as_float(hg << 16), g1 = __uint_as_float(hg & 0xffff0000u);
                     const float u0 = __uint_as_float(hu << 16), u1 = __uint_as_float(hu & 0xffff0000u);
-                    const float p0 = (g0 / (1.0f + exp_pinned(-g0))) * u0;
-                    const float p1 = (g1 / (1.0f + exp_pinned(-g1))) * u1;
+                    float s0, s1;
+                    if constexpr (kSiluLds) {
+                        s0 = silu_bf16(s_silu, hg & 0xffffu);
+                        s1 = silu_bf16(s_silu, hg >> 16);
+                    } else {
+                        s0 = silu_pinned(g0);
+                        s1 = silu_pinned(g1);
+                    }
+                    const float p0 = s0 * u0;
+                    const float p1 = s1 * u1;
                     const uint32_t pk = f32x2_to_bf16x2(p0, p1);   // act is rounded to bf16
                     act[mi][v][0] = __uint_as_float(pk << 16);
                     act[mi][v][1] = __uint_as_float(pk & 0xffff0000u);
@@ -530,19 +542,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
                 }
             if (fr == 0) {
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
+                for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) s_amax[wn][wm * 64 + mi * 16 + (lane >> 4) * 4 + v] = amax[mi][v];
+                    for (int v = 0; v < 4; ++v)
+                        s_amax[wn][wm * 16 * MI + mi * 16 + (lane >> 4) * 4 + v] = amax[mi][v];
             }
             // publish the partial maxima (LDS only: the DMAs in flight for
             // the next steps are not waited for)
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             const int ng = n_half / 128;
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
+            for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const int rl = wm * 64 + mi * 16 + (lane >> 4) * 4 + v;
+                    const int rl = wm * 16 * MI + mi * 16 + (lane >> 4) * 4 + v;
                     float m = s_amax[0][rl];
 #pragma unroll
                     for (int ww = 1; ww < 4; ++ww) {
@@ -611,10 +624,16 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_s, const uint8_t
 hipError_t launch_grouped_gemm_act(const uint8_t* a, const float* a_s, const uint8_t* w13,
                                    const float* w13_s, const int32_t* offsets, const int32_t* counts,
                                    int El, int64_t cap_rows, int N, int k_in, uint8_t* q, float* q_s,
-                                   int num_cus, hipStream_t s) {
-    const int64_t grid = gemm_grid(cap_rows, El, 2 * N, Shape<4>::BM, num_cus);
-    k_grouped_gemm<true, 4><<<(unsigned)grid, kThreads, 0, s>>>(a, a_s, w13, w13_s, offsets, counts, El,
-                                                                 cap_rows, 2 * N, k_in, nullptr, q, q_s);
+                                   int64_t rows_hint, int num_cus, hipStream_t s) {
+    if (gemm_tile_rows(rows_hint, El) == 256) {
+        const int64_t grid = gemm_grid(cap_rows, El, 2 * N, Shape<8>::BM, num_cus);
+        k_grouped_gemm<true, 8><<<(unsigned)grid, kThreads, 0, s>>>(a, a_s, w13, w13_s, offsets, counts, El,
+                                                                     cap_rows, 2 * N, k_in, nullptr, q, q_s);
+    } else {
+        const int64_t grid = gemm_grid(cap_rows, El, 2 * N, Shape<4>::BM, num_cus);
+        k_grouped_gemm<true, 4><<<(unsigned)grid, kThreads, 0, s>>>(a, a_s, w13, w13_s, offsets, counts, El,
+                                                                     cap_rows, 2 * N, k_in, nullptr, q, q_s);
+    }
     return hipGetLastError();
 }
 

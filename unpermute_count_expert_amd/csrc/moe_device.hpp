@@ -135,6 +135,39 @@ __device__ __forceinline__ float exp_pinned(float x) {
     return __builtin_amdgcn_ldexpf(p, static_cast<int>(n));
 }
 
+// SiLU as the SiLU-mul requant defines it: g / (1 + exp(-g)) with the
+// pinned exp and an IEEE division.
+__device__ __forceinline__ float silu_pinned(float g) {
+    const float e = exp_pinned(-g);
+    return g / (1.0f + e);
+}
+
+// SiLU of a bf16 value is a function of its 16 bits: a table of the formula's
+// own results for every bf16 g with 2^-12 <= |g| < 2^8 (both signs, 5120
+// entries, 20 KB of LDS; entry (sign * kSiluExps + exponent - kSiluExpLo) *
+// 128 + mantissa), built by the whole block; other g (zeros, tiny and huge
+// values, infinities, NaN) take the formula itself, so a lookup returns the
+// formula's bits for every g.
+constexpr int kSiluExpLo = 127 - 12;
+constexpr int kSiluExps = 20;
+constexpr int kSiluHalf = kSiluExps * 128;
+constexpr int kSiluEntries = 2 * kSiluHalf;
+
+__device__ __forceinline__ void silu_table_build(float* tab) {
+    for (int j = threadIdx.x; j < kSiluEntries; j += blockDim.x) {
+        const bool neg = j >= kSiluHalf;
+        const uint32_t hb = ((uint32_t)neg << 15) | (uint32_t)((kSiluExpLo << 7) + (neg ? j - kSiluHalf : j));
+        tab[j] = silu_pinned(__uint_as_float(hb << 16));
+    }
+}
+
+// silu of the bf16 value with bits hb
+__device__ __forceinline__ float silu_bf16(const float* __restrict__ tab, uint32_t hb) {
+    const uint32_t t = (hb & 0x7fffu) - (uint32_t)(kSiluExpLo << 7);
+    if (__builtin_expect(t < (uint32_t)kSiluHalf, 1)) return tab[t + (hb >> 15) * kSiluHalf];
+    return silu_pinned(__uint_as_float(hb << 16));
+}
+
 __device__ __forceinline__ int local_expert(int id, const int32_t* __restrict__ emap, int Eg, int El) {
     if (id < 0 || id >= Eg) return -1;
     int e = emap ? emap[id] : id;

@@ -59,7 +59,7 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_s, const uint8_t
 hipError_t launch_grouped_gemm_act(const uint8_t* a, const float* a_s, const uint8_t* w13,
                                    const float* w13_s, const int32_t* offsets, const int32_t* counts,
                                    int El, int64_t cap_rows, int N, int k_in, uint8_t* q, float* q_s,
-                                   int num_cus, hipStream_t s);
+                                   int64_t rows_hint, int num_cus, hipStream_t s);
 
 // ---- unpermute ----------------------------------------------------------------
 hipError_t launch_unpermute(const uint16_t* y, int64_t y_rows, const int32_t* inv_perm,
