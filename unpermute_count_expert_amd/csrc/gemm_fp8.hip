@@ -257,6 +257,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
     __shared__ int s_tpre[kMaxLocalExperts + 1];
     __shared__ int s_wsum[kWaves];
     __shared__ float s_amax[KACT ? 4 : 1][KACT ? BM : 1];   // per-wave-column partial group maxima
+    __shared__ __attribute__((aligned(16))) float s_inv[KACT ? BM : 1];   // 448 / d of each row
     const int n_half = n_out / 2;                 // N when KACT
 
     const int tid = threadIdx.x;
@@ -507,38 +508,66 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
             const int j = cur.n0 >> 8;   // act column block
             float act[MI][4][2];
             float amax[MI][4];
+            if constexpr (kSiluLds) {
+                // SiLU of the bf16 gates from the table, without branches;
+                // gates outside it (rare) are redone below with the formula
+                bool outside = false;
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const uint32_t hg = f32x2_to_bf16x2(acc[mi][0][v], acc[mi][1][v]);
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const uint32_t hb = h ? hg >> 16 : hg & 0xffffu;
+                            const uint32_t t = (hb & 0x7fffu) - (uint32_t)(kSiluExpLo << 7);
+                            const bool in = t < (uint32_t)kSiluHalf;
+                            act[mi][v][h] = s_silu[in ? t + (hb >> 15) * kSiluHalf : 0u];
+                            outside |= !in;
+                        }
+                    }
+                if (__builtin_expect(__ballot(outside) != 0, 0)) {
+#pragma unroll
+                    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const uint32_t hg = f32x2_to_bf16x2(acc[mi][0][v], acc[mi][1][v]);
+#pragma unroll
+                            for (int h = 0; h < 2; ++h) {
+                                const uint32_t hb = h ? hg >> 16 : hg & 0xffffu;
+                                const uint32_t t = (hb & 0x7fffu) - (uint32_t)(kSiluExpLo << 7);
+                                if (t >= (uint32_t)kSiluHalf) act[mi][v][h] = silu_pinned(__uint_as_float(hb << 16));
+                            }
+                        }
+                }
+            }
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const uint32_t hg = f32x2_to_bf16x2(acc[mi][0][v], acc[mi][1][v]);
                     const uint32_t hu = f32x2_to_bf16x2(acc[mi][2][v], acc[mi][3][v]);
-                    const float g0 = __uint_as_float(hg << 16), g1 = __uint_as_float(hg & 0xffff0000u);
                     const float u0 = __uint_as_float(hu << 16), u1 = __uint_as_float(hu & 0xffff0000u);
                     float s0, s1;
                     if constexpr (kSiluLds) {
-                        s0 = silu_bf16(s_silu, hg & 0xffffu);
-                        s1 = silu_bf16(s_silu, hg >> 16);
+                        s0 = act[mi][v][0];
+                        s1 = act[mi][v][1];
                     } else {
-                        s0 = silu_pinned(g0);
-                        s1 = silu_pinned(g1);
+                        const uint32_t hg = f32x2_to_bf16x2(acc[mi][0][v], acc[mi][1][v]);
+                        s0 = silu_pinned(__uint_as_float(hg << 16));
+                        s1 = silu_pinned(__uint_as_float(hg & 0xffff0000u));
                     }
                     const float p0 = s0 * u0;
                     const float p1 = s1 * u1;
                     const uint32_t pk = f32x2_to_bf16x2(p0, p1);   // act is rounded to bf16
                     act[mi][v][0] = __uint_as_float(pk << 16);
                     act[mi][v][1] = __uint_as_float(pk & 0xffff0000u);
-                    // largest non-NaN magnitude, by compare-select
+                    // largest non-NaN magnitude (compare-select, so m is never
+                    // NaN), then over the 16 lanes of the row quad
                     float m = 0.0f;
                     const float a0 = __builtin_fabsf(act[mi][v][0]), a1 = __builtin_fabsf(act[mi][v][1]);
                     m = a0 > m ? a0 : m;
                     m = a1 > m ? a1 : m;
-#pragma unroll
-                    for (int d = 1; d < 16; d <<= 1) {
-                        const float o = __shfl_xor(m, d, kWave);
-                        m = o > m ? o : m;
-                    }
-                    amax[mi][v] = m;
+                    amax[mi][v] = row16_max_nonnan(m);
                 }
             if (fr == 0) {
 #pragma unroll
@@ -551,29 +580,38 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
             // the next steps are not waited for)
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             const int ng = n_half / 128;
+            // each row's d, scale and 448 / d once: the 4 waves of a wave row
+            // take 4 * MI of its 16 * MI rows each, one per lane
+            if (lane < 4 * MI) {
+                const int rl = wm * 16 * MI + wn * 4 * MI + lane;
+                float m = s_amax[0][rl];
 #pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
+                for (int ww = 1; ww < 4; ++ww) {
+                    const float o = s_amax[ww][rl];
+                    m = o > m ? o : m;
+                }
+                const float dd = __builtin_fmaxf(m, 1e-10f);
+                s_inv[rl] = 448.0f / dd;
+                const int row = cur.m0 + rl;
+                if (row < cur.row_end) q_s[(int64_t)row * ng + j] = dd / 448.0f;
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi) {
+                const v4f inv4 = *reinterpret_cast<const v4f*>(&s_inv[wm * 16 * MI + mi * 16 + (lane >> 4) * 4]);
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int rl = wm * 16 * MI + mi * 16 + (lane >> 4) * 4 + v;
-                    float m = s_amax[0][rl];
-#pragma unroll
-                    for (int ww = 1; ww < 4; ++ww) {
-                        const float o = s_amax[ww][rl];
-                        m = o > m ? o : m;
-                    }
-                    const float dd = __builtin_fmaxf(m, 1e-10f);
-                    const float inv = 448.0f / dd;
-                    // |act * inv| <= 448 (1 + 2^-23) unless NaN: dd >= every |act| of the group
+                    const float inv = inv4[v];
+                    // |act * inv| <= 448 (1 + 2^-23) unless NaN: d >= every |act| of the group
                     const uint32_t codes =
                         f32x4_to_e4m3_bounded(act[mi][v][0] * inv, act[mi][v][1] * inv, 0.0f, 0.0f);
                     const int row = cur.m0 + rl;
-                    if (wave_has_rows && row < cur.row_end) {
+                    if (wave_has_rows && row < cur.row_end)
                         *reinterpret_cast<uint16_t*>(q + (int64_t)row * n_half + j * 128 + wn * 32 + 2 * fr) =
                             (uint16_t)codes;
-                        if (wn == 0 && fr == 0) q_s[(int64_t)row * ng + j] = dd / 448.0f;
-                    }
                 }
+            }
         }
         walk.next(cur);
     }

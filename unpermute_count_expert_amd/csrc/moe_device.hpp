@@ -135,6 +135,29 @@ __device__ __forceinline__ float exp_pinned(float x) {
     return __builtin_amdgcn_ldexpf(p, static_cast<int>(n));
 }
 
+// Largest value among the 16 lanes of this lane's DPP row, returned to all
+// 16, for values that are never NaN (so the hardware maximum is the plain
+// larger value, as compare-select would give): lane pairs xor 1, xor 2
+// (quad permutes), then the two quads of each half and the two halves (the
+// half-row and row mirrors), one v_max_f32 with a DPP operand each.  The
+// s_nop before each step covers the wait a DPP read of a VGPR written by the
+// previous VALU instruction needs.
+__device__ __forceinline__ float row16_max_nonnan(float m) {
+    float r;
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_max_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf"
+        : "=&v"(r)
+        : "v"(m));
+    return r;
+}
+
 // SiLU as the SiLU-mul requant defines it: g / (1 + exp(-g)) with the
 // pinned exp and an IEEE division.
 __device__ __forceinline__ float silu_pinned(float g) {
