@@ -253,8 +253,10 @@ def copy_calibration(iters):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the GPU's clock settles only after ~0.1 s of continuous load, so the
+    # default warm-up runs 100 layer calls (~0.1 s) before the 100 timed ones
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="C5u", choices=sorted(gen.CONFIGS))
     ap.add_argument("--op-iters", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
