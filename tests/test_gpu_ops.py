@@ -97,16 +97,18 @@ def test_silu_mul_quant_parity(masked, rows, n):
         assert np.all(qg[other] == 0xAB) and np.all(sg[other] == -7.0)
 
 
-@pytest.mark.parametrize("up", ["one", "random"])
-def test_silu_mul_quant_every_bf16_gate(up):
+@pytest.mark.parametrize("up,n", [("one", 128), ("random", 128), ("one", 8192), ("random", 8192)])
+def test_silu_mul_quant_every_bf16_gate(up, n):
     """Every one of the 65536 bf16 gate patterns (zeros, subnormals, the
     tabulated range, huge values, infinities, NaNs), sorted and shuffled into
     groups, with up = 1 or random: codes and scales bit-exact with the
-    oracle's SiLU formula."""
-    announce("silu quant all bf16 gates", up)
+    oracle's SiLU formula.  n = 128 gives 1024 groups (SiLU by the formula);
+    n = 8192 gives 65536 groups, enough rows for the kernel's SiLU table."""
+    announce("silu quant all bf16 gates", up, n)
     rng = np.random.default_rng(11)
     pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
-    gates = np.concatenate([pats, rng.permutation(pats)]).reshape(-1, 128)
+    reps = 2 if n == 128 else 128
+    gates = np.concatenate([pats] + [rng.permutation(pats) for _ in range(reps - 1)]).reshape(-1, n)
     if up == "one":
         ups = np.full(gates.shape, 0x3F80, np.uint16)
     else:

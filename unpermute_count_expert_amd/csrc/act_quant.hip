@@ -41,7 +41,8 @@ __device__ __forceinline__ Vals8 unpack_bf16x8(uint4 u) {
     return r;
 }
 
-template <int MODE>
+// MODE: identity or SiLU-mul; TABLE (SiLU-mul only): SiLU from the LDS table
+template <int MODE, bool TABLE>
 __global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restrict__ in, int64_t rows,
                                                         int n, const int32_t* __restrict__ offsets,
                                                         const int32_t* __restrict__ counts, int El,
@@ -49,13 +50,13 @@ __global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restri
                                                         float* __restrict__ q_s) {
     __shared__ int s_off[kMaxLocalExperts + 1];
     __shared__ int s_end[kMaxLocalExperts];
-    __shared__ float s_silu[MODE == MOE_ACT_SILU_MUL_K ? kSiluEntries : 1];
+    __shared__ float s_silu[TABLE ? kSiluEntries : 1];
     const bool masked = offsets != nullptr;
     if (masked) {
         for (int e = threadIdx.x; e <= El; e += blockDim.x) s_off[e] = offsets[e];
         for (int e = threadIdx.x; e < El; e += blockDim.x) s_end[e] = offsets[e] + counts[e];
     }
-    if (MODE == MOE_ACT_SILU_MUL_K) silu_table_build(s_silu);
+    if (TABLE) silu_table_build(s_silu);
     __syncthreads();
     const int ng = n / kGroup;
     const int64_t total = rows * ng;
@@ -122,8 +123,13 @@ __global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restri
             float prod[8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                prod[2 * i] = silu_bf16(s_silu, gbits[i] & 0xffffu) * u.v[2 * i];
-                prod[2 * i + 1] = silu_bf16(s_silu, gbits[i] >> 16) * u.v[2 * i + 1];
+                if constexpr (TABLE) {
+                    prod[2 * i] = silu_bf16(s_silu, gbits[i] & 0xffffu) * u.v[2 * i];
+                    prod[2 * i + 1] = silu_bf16(s_silu, gbits[i] >> 16) * u.v[2 * i + 1];
+                } else {
+                    prod[2 * i] = silu_pinned(__uint_as_float(gbits[i] << 16)) * u.v[2 * i];
+                    prod[2 * i + 1] = silu_pinned(__uint_as_float(gbits[i] & 0xffff0000u)) * u.v[2 * i + 1];
+                }
             }
             // the activation is rounded to bf16 before it is quantised
 #pragma unroll
@@ -146,20 +152,25 @@ __global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restri
 
 hipError_t launch_act_quant(const uint16_t* in, int64_t rows, int n, int mode,
                             const int32_t* offsets, const int32_t* counts, int El, uint8_t* q,
-                            float* q_s, hipStream_t s) {
+                            float* q_s, int64_t rows_hint, hipStream_t s) {
     const int64_t groups = rows * (n / kGroup);
     if (groups <= 0) return hipSuccess;
     int64_t blocks = (groups + kGroupsPerBlock - 1) / kGroupsPerBlock;
-    // SiLU-mul: each block builds the 5120-entry SiLU table, so fewer, longer
-    // blocks (the table costs a block as much as ~90 groups)
-    const int64_t cap = mode == MOE_ACT_IDENTITY_K ? 8192 : 1024;
-    if (blocks > cap) blocks = cap;
-    if (mode == MOE_ACT_IDENTITY_K)
-        k_act_quant<MOE_ACT_IDENTITY_K><<<(unsigned)blocks, kThreads, 0, s>>>(in, rows, n, offsets, counts,
-                                                                             El, q, q_s);
-    else
-        k_act_quant<MOE_ACT_SILU_MUL_K><<<(unsigned)blocks, kThreads, 0, s>>>(in, rows, n, offsets, counts,
-                                                                             El, q, q_s);
+    if (mode == MOE_ACT_IDENTITY_K) {
+        if (blocks > 8192) blocks = 8192;
+        k_act_quant<MOE_ACT_IDENTITY_K, false><<<(unsigned)blocks, kThreads, 0, s>>>(in, rows, n, offsets, counts,
+                                                                                    El, q, q_s);
+    } else if ((rows_hint < rows ? rows_hint : rows) * (n / kGroup) >= (int64_t)1024 * 64) {
+        // enough valid rows for 1024 blocks of >= 64 groups each: every block
+        // builds the SiLU table (as costly as ~90 groups) and then looks up
+        if (blocks > 1024) blocks = 1024;
+        k_act_quant<MOE_ACT_SILU_MUL_K, true><<<(unsigned)blocks, kThreads, 0, s>>>(in, rows, n, offsets, counts,
+                                                                                   El, q, q_s);
+    } else {
+        if (blocks > 8192) blocks = 8192;
+        k_act_quant<MOE_ACT_SILU_MUL_K, false><<<(unsigned)blocks, kThreads, 0, s>>>(in, rows, n, offsets, counts,
+                                                                                    El, q, q_s);
+    }
     return hipGetLastError();
 }
 

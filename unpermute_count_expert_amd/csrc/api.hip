@@ -360,7 +360,7 @@ int moe_act_quant(const uint16_t* in, int64_t rows, int32_t n, int32_t mode,
     REQUIRE_PTR(q_s);
     int st = check_device(nullptr);
     if (st) return st;
-    HIP_OK(moe::launch_act_quant(in, rows, n, mode, expert_offsets, counts, El, q, q_s,
+    HIP_OK(moe::launch_act_quant(in, rows, n, mode, expert_offsets, counts, El, q, q_s, rows,
                                  static_cast<hipStream_t>(stream)));
     return MOE_OK;
 }
@@ -446,7 +446,7 @@ int moe_forward_chunked(const moe_problem* p, const uint16_t* x, const int32_t* 
         HIP_OK(moe::launch_grouped_gemm(bufA, bufAs, w13, w13_s, offsets, counts, (int)El, pl.cap,
                                         (int)(2 * N), (int)K, hy, Mc * T, cus, s));
         HIP_OK(moe::launch_act_quant(hy, pl.cap, (int)N, moe::MOE_ACT_SILU_MUL_K, offsets, counts, (int)El,
-                                     bufA, bufAs, s));
+                                     bufA, bufAs, Mc * T, s));
         HIP_OK(moe::launch_grouped_gemm(bufA, bufAs, w2, w2_s, offsets, counts, (int)El, pl.cap, (int)K,
                                         (int)N, hy, Mc * T, cus, s));
         HIP_OK(moe::launch_unpermute(hy, pl.cap, inv, w_c, Mc, (int)K, (int)T, on_in, out + t0 * K, s));
