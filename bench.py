@@ -211,11 +211,13 @@ def cpu_baseline(inp, on_input, target_s=15.0):
                       f"{ts:.1f} s"}
 
 
-def other_layers(names, warmup=3, steps=5):
+def other_layers(names, warm_s=0.15, timed_s=0.1):
     """Step time of the fused forward on the other layer configurations (hot
     routing, router weight on input, the 4096-token prefill chunk, the
     8192-token layer in chunks of 64 with 64 of 128 experts local, and the
-    64-token profiling shape), each on its own seeded inputs."""
+    64-token profiling shape), each on its own seeded inputs: warm-up for
+    about warm_s seconds (the clock settles after ~0.1 s of load), then about
+    timed_s seconds of steps timed, at least 3 of each."""
     res = {}
     stream = torch.cuda.current_stream()
     for name in names:
@@ -227,10 +229,11 @@ def other_layers(names, warmup=3, steps=5):
         out = torch.empty((c.M, c.K), dtype=torch.int16, device="cuda:0")
         fn = lambda: layer.forward(x, ids, w, chunk_size=c.chunk_size, apply_on_input=c.apply_router_weight_on_input,
                                    out=out)
-        for _ in range(warmup):
+        probe = timed(fn, 1, stream)   # one step, to size the loops
+        for _ in range(max(3, int(warm_s / (probe * 1e-3)))):
             fn()
         torch.cuda.synchronize()
-        ms = timed(fn, steps, stream)
+        ms = timed(fn, max(3, int(timed_s / (probe * 1e-3))), stream)
         res[name] = {"workload": f"M={c.M} chunk={c.chunk_size} K={c.K} N={c.N} E={c.El}/{c.Eg} topk={c.topk} "
                                  f"routing={c.routing} on_input={c.apply_router_weight_on_input}",
                      "ms_per_step": round(ms, 5), "tokens/s": round(c.M / (ms * 1e-3), 1)}
