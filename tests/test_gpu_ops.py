@@ -417,7 +417,10 @@ def test_gemm_random_parity(El, n_out, k_in, counts, align, tile):
 
 # ---------------------------------------------------------------- unpermute
 @pytest.mark.parametrize("M,K,T,on_input", [(1, 128, 1, 0), (513, 2048, 8, 0), (100, 384, 3, 1),
-                                            (16384, 2048, 8, 0)])
+                                            (16384, 2048, 8, 0),
+                                            (77, 2176, 8, 1),     # a second, partial pass of slabs
+                                            (37, 640, 12, 0),     # more than eight rows a token
+                                            (20, 2176, 20, 1)])
 def test_unpermute_parity(M, K, T, on_input):
     announce("unpermute", M, K, T, on_input)
     rng = np.random.default_rng(M + K)
@@ -425,9 +428,13 @@ def test_unpermute_parity(M, K, T, on_input):
     y = gen.bf16_bits(rng.standard_normal((R, K)).astype(np.float32))
     inv = rng.permutation(R)[:M * T].reshape(M, T).astype(np.int32)
     inv[rng.random((M, T)) < 0.1] = -1
+    # indices past the rows of y are never read; they count as dropped pairs
+    oob = rng.random((M, T)) < 0.05
+    inv_gpu = np.where(oob, R + 7, inv).astype(np.int32)
+    inv_ref = np.where(oob, -1, inv).astype(np.int32)
     w = rng.uniform(0, 1, (M, T)).astype(np.float32)
     out = filled((M, K), "bf16", 0x7FC1)
-    moe.moe_unpermute_weight_reduce(dev(y), dev(inv), dev(w), on_input, out)
+    moe.moe_unpermute_weight_reduce(dev(y), dev(inv_gpu), dev(w), on_input, out)
     got = host(out, bf16=True)
-    ref = oracle.unpermute(y, inv, w, on_input)
+    ref = oracle.unpermute(y, inv_ref, w, on_input)
     np.testing.assert_array_equal(got, ref)   # same fmaf order on both sides
