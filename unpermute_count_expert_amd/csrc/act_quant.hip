@@ -15,6 +15,9 @@
 // values, infinities, NaN) take the formula itself.  The table holds the
 // formula's own results, so the codes are the same bit for bit, and the
 // kernel no longer spends ~40 VALU instructions per element on it.
+//
+// The input rows are read once and the codes written once, with
+// non-temporal loads and stores.
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 
@@ -113,12 +116,12 @@ __global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restri
         }
         Vals8 x;
         if (MODE == MOE_ACT_IDENTITY_K) {
-            const uint4 u = *reinterpret_cast<const uint4*>(in + r_this * n + gi_this * kGroup + sub * 8);
+            const uint4 u = load_once16(in + r_this * n + gi_this * kGroup + sub * 8);
             x = unpack_bf16x8(u);
         } else {
             const uint16_t* base = in + r_this * 2 * (int64_t)n + gi_this * kGroup + sub * 8;
-            const uint4 gw = *reinterpret_cast<const uint4*>(base);
-            const Vals8 u = unpack_bf16x8(*reinterpret_cast<const uint4*>(base + n));
+            const uint4 gw = load_once16(base);
+            const Vals8 u = unpack_bf16x8(load_once16(base + n));
             const uint32_t gbits[4] = {gw.x, gw.y, gw.z, gw.w};
             float prod[8];
 #pragma unroll
@@ -142,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restri
         uint2 codes;
         const float scale = quant_group16(x.v, codes);
         if (valid) {
-            *reinterpret_cast<uint2*>(q + r_this * n + gi_this * kGroup + sub * 8) = codes;
+            store_once8(q + r_this * n + gi_this * kGroup + sub * 8, codes);
             if (sub == 0) q_s[r_this * ng + gi_this] = scale;
         }
     }

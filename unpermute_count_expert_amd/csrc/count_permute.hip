@@ -16,7 +16,10 @@
 //           blocks of slice 0), then each token row slice is read once and
 //           written to each of its expert rows with 16-byte lanes.  The
 //           rows are split along K so that about 1024 blocks share them
-//           (chunks of few tokens have few pair blocks).
+//           (chunks of few tokens have few pair blocks).  The token rows
+//           are read with non-temporal loads; the stores of a_perm stay
+//           ordinary (non-temporal ones move their cost into the GEMM
+//           that reads a_perm next: both ways the step takes as long).
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 
@@ -236,9 +239,9 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
             v[u] = uint4{0, 0, 0, 0};
             if (q < items) {
                 if constexpr (QUANT)
-                    v[u] = *reinterpret_cast<const uint4*>(x + (t0 + tl) * K + (int64_t)gc * kGroup + sub * 8);
+                    v[u] = load_once16(x + (t0 + tl) * K + (int64_t)gc * kGroup + sub * 8);
                 else
-                    v[u] = *reinterpret_cast<const uint4*>(a_q + (t0 + tl) * K + (int64_t)gc * 16);
+                    v[u] = load_once16(a_q + (t0 + tl) * K + (int64_t)gc * 16);
             }
         }
     };

@@ -112,6 +112,22 @@ __device__ __forceinline__ void bf16x8_to_f32(uint4 u, float (&v)[8]) {
     }
 }
 
+// Loads and stores of data that one kernel touches exactly once (rows read
+// once, outputs written once): non-temporal, so the lines are not kept in
+// the caches at the expense of data that is reused.
+typedef int moe_i4 __attribute__((ext_vector_type(4)));
+typedef int moe_i2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 load_once16(const void* p) {
+    const moe_i4 q = __builtin_nontemporal_load(reinterpret_cast<const moe_i4*>(p));
+    return uint4{(unsigned)q.x, (unsigned)q.y, (unsigned)q.z, (unsigned)q.w};
+}
+__device__ __forceinline__ void store_once16(void* p, const uint4& v) {
+    __builtin_nontemporal_store(moe_i4{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, reinterpret_cast<moe_i4*>(p));
+}
+__device__ __forceinline__ void store_once8(void* p, const uint2& v) {
+    __builtin_nontemporal_store(moe_i2{(int)v.x, (int)v.y}, reinterpret_cast<moe_i2*>(p));
+}
+
 // exp for SiLU, fixed operation by operation so that it is reproducible:
 // clamp to [-86, 88]; n = nearest-even(x / ln2); r = x - n*ln2 with ln2 in
 // two parts (Cody-Waite); Horner over the Taylor coefficients 1/k!, k<=7;

@@ -22,17 +22,6 @@ constexpr int kThreads = 256;
 constexpr int kTokensPerBlock = kThreads / kWave;
 constexpr int kSlabs = 4;   // 512-column slabs per pass
 
-typedef int v4n __attribute__((ext_vector_type(4)));
-
-// 16 bytes of a row that is read once
-__device__ __forceinline__ uint4 load_once(const uint16_t* p) {
-    const v4n q = __builtin_nontemporal_load(reinterpret_cast<const v4n*>(p));
-    return uint4{(unsigned)q.x, (unsigned)q.y, (unsigned)q.z, (unsigned)q.w};
-}
-__device__ __forceinline__ void store_once(uint16_t* p, const uint4& o) {
-    __builtin_nontemporal_store(v4n{(int)o.x, (int)o.y, (int)o.z, (int)o.w}, reinterpret_cast<v4n*>(p));
-}
-
 // acc[0..7] = fmaf(w, each bf16 of v, acc) in column order
 __device__ __forceinline__ void fold8(float (&acc)[8], float w, const uint4& v) {
     const uint32_t u[4] = {v.x, v.y, v.z, v.w};
@@ -114,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void k_unpermute(const uint16_t* __restri
                 const int c0 = p0 + sb * kWave * 8;
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
-                    v[sb][j] = load_once(y + (int64_t)(ok[j] ? rr[j] : 0) * K + (c0 < K ? c0 : 0));
+                    v[sb][j] = load_once16(y + (int64_t)(ok[j] ? rr[j] : 0) * K + (c0 < K ? c0 : 0));
             }
 #pragma unroll
             for (int sb = 0; sb < kSlabs; ++sb) {
@@ -125,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void k_unpermute(const uint16_t* __restri
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
                     if (ok[j]) fold8(acc, ww[j], v[sb][j]);
-                if (c0 < K) store_once(out + t * K + c0, to_bf16x8(acc));
+                if (c0 < K) store_once16(out + t * K + c0, to_bf16x8(acc));
             }
         }
         return;
@@ -144,13 +133,13 @@ __global__ __launch_bounds__(kThreads) void k_unpermute(const uint16_t* __restri
                 const int r = k0 + j < topk ? rows[k0 + j] : -1;
                 wk[j] = apply_on_input ? 1.0f : (k0 + j < topk ? wts[k0 + j] : 0.0f);
                 ok[j] = r >= 0 && r < y_rows;
-                v[j] = load_once(y + (int64_t)(ok[j] ? r : 0) * K + c0);
+                v[j] = load_once16(y + (int64_t)(ok[j] ? r : 0) * K + c0);
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 if (ok[j]) fold8(acc, wk[j], v[j]);
         }
-        store_once(out + t * K + c0, to_bf16x8(acc));
+        store_once16(out + t * K + c0, to_bf16x8(acc));
     }
 }
 
