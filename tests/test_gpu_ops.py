@@ -415,6 +415,49 @@ def test_gemm_random_parity(El, n_out, k_in, counts, align, tile):
     assert np.all(out[untouched] == 0x7FC1)
 
 
+@pytest.mark.parametrize("El,max_tokens,n_out,k_in,tile", [
+    (16, 16, 768, 2048, 128),     # decode-sized slots: 0..16 rows per expert
+    (6, 300, 384, 768, 256),      # slots longer than a 256-row tile
+    (4, 512, 256, 512, 256),
+])
+def test_gemm_masked_batched_layout(El, max_tokens, n_out, k_in, tile):
+    """The batched, masked layout [E, max_tokens, K] with a valid-row count
+    per expert (low-latency dispatch, vLLM PR #20903 Purpose) is the grouped
+    GEMM with expert_offsets[e] = e * max_tokens: slots need not be packed or
+    aligned.  Counts include an empty and a full slot; the SiLU-mul requant
+    is checked on the same layout."""
+    announce("gemm masked batched", El, max_tokens, n_out, k_in, tile)
+    rng = np.random.default_rng(El * max_tokens)
+    cnt = rng.integers(0, max_tokens + 1, El).astype(np.int32)
+    cnt[0], cnt[-1] = 0, max_tokens
+    offs = (np.arange(El + 1) * max_tokens).astype(np.int32)
+    cap = El * max_tokens
+    assert moe.moe_grouped_gemm_tile_rows(cap, El) == tile
+    a = gen.random_codes(rng, (cap, k_in))
+    w = gen.random_codes(rng, (El, n_out, k_in))
+    a_s = rng.uniform(1e-3, 1, (cap, k_in // 128)).astype(np.float32)
+    w_s = rng.uniform(1e-3, 1, (El, n_out // 128, k_in // 128)).astype(np.float32)
+    out = _gpu_gemm(a, a_s, w, w_s, offs, cnt)
+    ref = oracle.grouped_gemm(a, a_s, w, w_s, offs, cnt)
+    absterm = oracle.grouped_gemm(a & 0x7F, a_s, w & 0x7F, w_s, offs, cnt)
+    rows = valid_rows(offs, cnt)
+    assert_gemm_close(out[rows], ref[rows], absterm[rows], "gemm masked")
+    assert np.all(out[np.setdiff1d(np.arange(cap), rows)] == 0x7FC1)
+    # SiLU-mul requant over the same slots, on the oracle's own GEMM output
+    # (the act width is n_out / 2 rounded down to whole groups)
+    n = (n_out // 2) // 128 * 128
+    h = np.ascontiguousarray(ref[:, :2 * n])
+    q = filled((cap, n), torch.uint8, 0xAB)
+    s = filled((cap, n // 128), torch.float32, -7.0)
+    moe.moe_act_quant(dev(h), n, moe.MOE_ACT_SILU_MUL, q, s, dev(offs), dev(cnt), El)
+    qr, sr = oracle.silu_mul_quant(h, offs, cnt, El)
+    qg, sg = host(q), host(s)
+    np.testing.assert_array_equal(sg[rows], sr[rows])
+    np.testing.assert_array_equal(qg[rows], qr[rows])
+    other = np.setdiff1d(np.arange(cap), rows)
+    assert np.all(qg[other] == 0xAB) and np.all(sg[other] == -7.0)
+
+
 # ---------------------------------------------------------------- unpermute
 @pytest.mark.parametrize("M,K,T,on_input", [(1, 128, 1, 0), (513, 2048, 8, 0), (100, 384, 3, 1),
                                             (16384, 2048, 8, 0),
