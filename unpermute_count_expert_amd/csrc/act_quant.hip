@@ -44,35 +44,70 @@ __device__ __forceinline__ Vals8 unpack_bf16x8(uint4 u) {
     return r;
 }
 
-// MODE: identity or SiLU-mul; TABLE (SiLU-mul only): SiLU from the LDS table
+// MODE: identity or SiLU-mul; TABLE (SiLU-mul only): SiLU from the LDS table.
+// With offsets (masked), the rows are expert slots: the valid rows of expert
+// e are [offsets[e], offsets[e] + counts[e]), cut at the next slot and at
+// rows; only those are read and written.  The work is the sequence of the
+// valid rows' groups, so padding rows cost nothing.
 template <int MODE, bool TABLE>
 __global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restrict__ in, int64_t rows,
                                                         int n, const int32_t* __restrict__ offsets,
                                                         const int32_t* __restrict__ counts, int El,
                                                         uint8_t* __restrict__ q,
                                                         float* __restrict__ q_s) {
-    __shared__ int s_off[kMaxLocalExperts + 1];
-    __shared__ int s_end[kMaxLocalExperts];
+    __shared__ int s_off[kMaxLocalExperts];        // first row of each expert's slot
+    __shared__ int s_vpre[kMaxLocalExperts + 1];   // valid rows of the experts before e
+    __shared__ int s_wsum[kThreads / kWave];
     __shared__ float s_silu[TABLE ? kSiluEntries : 1];
     const bool masked = offsets != nullptr;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
     if (masked) {
-        for (int e = threadIdx.x; e <= El; e += blockDim.x) s_off[e] = offsets[e];
-        for (int e = threadIdx.x; e < El; e += blockDim.x) s_end[e] = offsets[e] + counts[e];
+        // valid rows per expert (clamped to the slot and to [0, rows)), then
+        // their exclusive scan; four experts per thread covers El <= 1024
+        int v[4], tsum = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = threadIdx.x * 4 + j;
+            v[j] = 0;
+            if (e < El) {
+                const int64_t lo = min((int64_t)max(offsets[e], 0), rows);
+                int64_t hi = min(lo + (int64_t)max(counts[e], 0), rows);
+                hi = min(hi, max((int64_t)offsets[e + 1], lo));   // offsets has El + 1 entries
+                s_off[e] = (int)lo;
+                v[j] = (int)(hi - lo);
+            }
+            tsum += v[j];
+        }
+        const int incl = wave_inclusive_scan(tsum);
+        if (lane == kWave - 1) s_wsum[wave] = incl;
+        __syncthreads();
+        int run = incl - tsum;
+        for (int w = 0; w < wave; ++w) run += s_wsum[w];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = threadIdx.x * 4 + j;
+            if (e < El) s_vpre[e] = run;
+            run += v[j];
+        }
+        if (threadIdx.x == kThreads - 1) s_vpre[El] = run;
     }
     if (TABLE) silu_table_build(s_silu);
     __syncthreads();
     const int ng = n / kGroup;
-    const int64_t total = rows * ng;
+    const int64_t nrows = masked ? (int64_t)s_vpre[El] : rows;   // rows of the work sequence
+    const int64_t total = nrows * ng;
     const int sub = threadIdx.x & (kLanesPerGroup - 1);
     // each block takes a contiguous range of groups, 16 at a time, so a
-    // thread's rows advance slowly and the expert segment found for one row
-    // is reused for the next ones
+    // thread's rows advance slowly and the expert found for one row is
+    // reused for the next ones
     const int64_t per_block = ((total + gridDim.x - 1) / gridDim.x + kGroupsPerBlock - 1) / kGroupsPerBlock *
                               kGroupsPerBlock;
     const int64_t g_lo = (int64_t)blockIdx.x * per_block;
     const int64_t g_hi = g_lo + per_block < total ? g_lo + per_block : total;
-    int64_t seg_lo = 0, seg_hi = -1;   // rows [seg_lo, seg_hi) share one validity, seg_valid
-    bool seg_valid = true;
+    // masked: valid rows [seg_lo, seg_hi) of the sequence belong to one
+    // expert, whose slot starts at row seg_lo + seg_shift
+    int64_t seg_lo = 0, seg_hi = -1, seg_shift = 0;
     // (row, group in row) of this thread's group, advanced by 16 groups per
     // iteration without a division
     int64_t grp = g_lo + threadIdx.x / kLanesPerGroup;
@@ -80,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restri
     int gi = (int)(grp - r * ng);
     const int adv_r = kGroupsPerBlock / ng, adv_g = kGroupsPerBlock % ng;
     for (; grp < g_hi; grp += kGroupsPerBlock) {
-        const int64_t r_this = r;
+        int64_t r_this = r;
         const int gi_this = gi;
         gi += adv_g;
         r += adv_r;
@@ -88,31 +123,19 @@ __global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restri
             gi -= ng;
             ++r;
         }
-        bool valid = true;
         if (masked) {
             if (r_this < seg_lo || r_this >= seg_hi) {
-                // the expert segment holding row r_this: largest e with s_off[e] <= r_this
-                int lo = 0, hi = El;  // answer in [0, El]
+                // the expert of valid row r_this: largest e < El with s_vpre[e] <= r_this
+                int lo = 0, hi = El - 1;
                 while (lo < hi) {
-                    int mid = (lo + hi + 1) >> 1;
-                    if (s_off[mid] <= r_this) lo = mid; else hi = mid - 1;
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (s_vpre[mid] <= r_this) lo = mid; else hi = mid - 1;
                 }
-                if (lo < El && r_this < s_end[lo]) {   // valid rows of expert lo
-                    seg_lo = s_off[lo];
-                    seg_hi = s_end[lo];
-                    seg_valid = true;
-                } else if (lo < El) {             // its padding rows
-                    seg_lo = s_end[lo];
-                    seg_hi = s_off[lo + 1];
-                    seg_valid = false;
-                } else {                          // past the last segment
-                    seg_lo = s_off[El];
-                    seg_hi = INT64_MAX;
-                    seg_valid = false;
-                }
+                seg_lo = s_vpre[lo];
+                seg_hi = s_vpre[lo + 1];
+                seg_shift = (int64_t)s_off[lo] - seg_lo;
             }
-            valid = seg_valid;
-            if (!valid) continue;   // padding rows are neither read nor written
+            r_this += seg_shift;
         }
         Vals8 x;
         if (MODE == MOE_ACT_IDENTITY_K) {
@@ -144,10 +167,8 @@ __global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restri
         }
         uint2 codes;
         const float scale = quant_group16(x.v, codes);
-        if (valid) {
-            store_once8(q + r_this * n + gi_this * kGroup + sub * 8, codes);
-            if (sub == 0) q_s[r_this * ng + gi_this] = scale;
-        }
+        store_once8(q + r_this * n + gi_this * kGroup + sub * 8, codes);
+        if (sub == 0) q_s[r_this * ng + gi_this] = scale;
     }
 }
 
@@ -158,7 +179,10 @@ hipError_t launch_act_quant(const uint16_t* in, int64_t rows, int n, int mode,
                             float* q_s, int64_t rows_hint, hipStream_t s) {
     const int64_t groups = rows * (n / kGroup);
     if (groups <= 0) return hipSuccess;
-    int64_t blocks = (groups + kGroupsPerBlock - 1) / kGroupsPerBlock;
+    // masked, the kernel walks the valid rows only, of which there are at
+    // most rows_hint
+    const int64_t work_rows = offsets && rows_hint < rows ? (rows_hint > 1 ? rows_hint : 1) : rows;
+    int64_t blocks = (work_rows * (n / kGroup) + kGroupsPerBlock - 1) / kGroupsPerBlock;
     if (mode == MOE_ACT_IDENTITY_K) {
         if (blocks > 8192) blocks = 8192;
         k_act_quant<MOE_ACT_IDENTITY_K, false><<<(unsigned)blocks, kThreads, 0, s>>>(in, rows, n, offsets, counts,

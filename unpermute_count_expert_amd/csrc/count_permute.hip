@@ -11,7 +11,8 @@
 //   all the pairs itself)
 //   scatter one block per 256 pairs and slice of the K groups: aligned
 //           offsets (every block scans the El counts itself; block (0, 0)
-//           also publishes offsets and padding marks), wave-ballot ranks
+//           publishes them and all blocks share the padding marks),
+//           wave-ballot ranks
 //           (stable in flat pair order), inverse indices (written by the
 //           blocks of slice 0), then each token row slice is read once and
 //           written to each of its expert rows with 16-byte lanes.  The
@@ -111,16 +112,6 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_hist(const int32_t* __
     __syncthreads();
     int32_t* row = hist + (int64_t)blockIdx.x * El;
     for (int e = threadIdx.x; e < El; e += blockDim.x) row[e] = h[e];
-}
-
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        int u = __shfl_up(v, d, kWave);
-        if (lane >= d) v += u;
-    }
-    return v;
 }
 
 __device__ __forceinline__ int wave_exclusive_scan(int v) { return wave_inclusive_scan(v) - v; }
@@ -305,14 +296,20 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
         if (threadIdx.x == kPermThreads - 1) s_off[El] = run;
         __syncthreads();
     }
-    if (blockIdx.x == 0 && blockIdx.y == 0) {   // publish the offsets; mark padding rows and rows past the end
-        for (int ex = threadIdx.x; ex <= El; ex += blockDim.x) offsets[ex] = s_off[ex];
-        // one wave per expert, its lanes on consecutive padding rows
-        for (int ex = wave; ex < El; ex += kWaves) {
+    {   // block (0, 0) publishes the offsets; all blocks share the padding
+        // marks (one wave per expert, its lanes on consecutive padding rows)
+        // and the rows past the last segment
+        const int nblocks = (int)(gridDim.x * gridDim.y);
+        const int bid = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+        if (bid == 0)
+            for (int ex = threadIdx.x; ex <= El; ex += blockDim.x) offsets[ex] = s_off[ex];
+        for (int ex = bid * kWaves + wave; ex < El; ex += nblocks * kWaves) {
             const int pad_lo = s_off[ex] + (self_count ? s_cnt[ex] : counts[ex]);
             for (int r = pad_lo + lane; r < s_off[ex + 1]; r += kWave) row_src[r] = -1;
         }
-        for (int64_t r = s_off[El] + threadIdx.x; r < cap_rows; r += blockDim.x) row_src[r] = -1;
+        for (int64_t r = s_off[El] + (int64_t)bid * blockDim.x + threadIdx.x; r < cap_rows;
+             r += (int64_t)nblocks * blockDim.x)
+            row_src[r] = -1;
     }
 
     const int e = active ? loc(own_id) : -1;
@@ -347,6 +344,7 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
         if constexpr (QUANT) {
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
+                if (q0 + 4 * u >= items) break;   // no item of this wave left (wave-uniform)
                 int tl, g;
                 const int q = item(q0, u, tl, g);
                 // every lane quantises (zeros past the end), so the group
@@ -371,6 +369,7 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
         } else {
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
+                if (q0 + u * kWave >= items) break;   // no item of this wave left (wave-uniform)
                 int tl, c;
                 const int q = item(q0, u, tl, c);
                 if (q < items) {

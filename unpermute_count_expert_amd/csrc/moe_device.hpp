@@ -213,6 +213,17 @@ __device__ __forceinline__ int local_expert(int id, const int32_t* __restrict__ 
     return (e >= 0 && e < El) ? e : -1;
 }
 
+// inclusive prefix sum over the 64 lanes of the wave
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        int u = __shfl_up(v, d, kWave);
+        if (lane >= d) v += u;
+    }
+    return v;
+}
+
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
 __device__ __forceinline__ uint64_t lanemask_lt() {

@@ -2,9 +2,10 @@
 // (vLLM PR #20903 Purpose item 2 and bot Highlights; the weight-and-reduce
 // inside the experts of vLLM PR #20725 Purpose), producing (M, K) directly.
 //
-// One wave per token.  Each lane owns 8 consecutive columns (16 bytes) of a
-// 512-column slab; for each slab the token's expert rows are gathered in k
-// order and folded with one fmaf per element, exactly in the order
+// One wave per token (for few tokens, per token and slice of its columns).
+// Each lane owns 8 consecutive columns (16 bytes) of a 512-column slab; for
+// each slab the token's expert rows are gathered in k order and folded with
+// one fmaf per element, exactly in the order
 // acc = fmaf(w_k, y_k, acc), k = 0..topk-1, then rounded once to bf16.
 // The row index of the token is wave-uniform, so indices and weights come
 // through the scalar cache.  With topk <= 8 all the rows of a pass of four
@@ -53,8 +54,13 @@ __global__ __launch_bounds__(kThreads) void k_unpermute(const uint16_t* __restri
     if (t >= Mc) return;
     const int32_t* rows = inv_perm + t * topk;
     const float* wts = topk_w + t * topk;
+    // this wave's columns: slice blockIdx.y of the token's 512-column slabs
+    const int nslab = (K + kWave * 8 - 1) / (kWave * 8);
+    const int spw = (nslab + (int)gridDim.y - 1) / (int)gridDim.y;
+    const int c_beg = min(K, (int)blockIdx.y * spw * kWave * 8);
+    const int c_end = min(K, c_beg + spw * kWave * 8);
     if (y_rows <= 0) {   // nothing to gather: the token's output is +0
-        for (int c0 = lane * 8; c0 < K; c0 += kWave * 8)
+        for (int c0 = c_beg + lane * 8; c0 < c_end; c0 += kWave * 8)
             *reinterpret_cast<uint4*>(out + t * K + c0) = uint4{0, 0, 0, 0};
         return;
     }
@@ -94,16 +100,21 @@ __global__ __launch_bounds__(kThreads) void k_unpermute(const uint16_t* __restri
         bool ok[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) ok[j] = rr[j] >= 0 && rr[j] < y_rows;
-        for (int p0 = lane * 8; p0 < K; p0 += kSlabs * kWave * 8) {
+        for (int p0 = c_beg + lane * 8; p0 < c_end; p0 += kSlabs * kWave * 8) {
             // every row load of the pass first (rows outside y read row 0,
             // columns past K column 0, and are not folded)
             uint4 v[kSlabs][8];
 #pragma unroll
             for (int sb = 0; sb < kSlabs; ++sb) {
                 const int c0 = p0 + sb * kWave * 8;
+                if (p0 - lane * 8 + sb * kWave * 8 < c_end) {   // the slab starts in the slice (wave-uniform)
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    v[sb][j] = load_once16(y + (int64_t)(ok[j] ? rr[j] : 0) * K + (c0 < K ? c0 : 0));
+                    for (int j = 0; j < 8; ++j)
+                        v[sb][j] = load_once16(y + (int64_t)(ok[j] ? rr[j] : 0) * K + (c0 < c_end ? c0 : 0));
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) v[sb][j] = uint4{0, 0, 0, 0};
+                }
             }
 #pragma unroll
             for (int sb = 0; sb < kSlabs; ++sb) {
@@ -114,13 +125,13 @@ __global__ __launch_bounds__(kThreads) void k_unpermute(const uint16_t* __restri
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
                     if (ok[j]) fold8(acc, ww[j], v[sb][j]);
-                if (c0 < K) store_once16(out + t * K + c0, to_bf16x8(acc));
+                if (c0 < c_end) store_once16(out + t * K + c0, to_bf16x8(acc));
             }
         }
         return;
     }
     // topk > 8: per slab, the rows eight at a time
-    for (int c0 = lane * 8; c0 < K; c0 += kWave * 8) {
+    for (int c0 = c_beg + lane * 8; c0 < c_end; c0 += kWave * 8) {
         float acc[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
@@ -150,8 +161,16 @@ hipError_t launch_unpermute(const uint16_t* y, int64_t y_rows, const int32_t* in
                             hipStream_t s) {
     if (Mc <= 0) return hipSuccess;
     const int64_t blocks = (Mc + kTokensPerBlock - 1) / kTokensPerBlock;
-    k_unpermute<<<(unsigned)blocks, kThreads, 0, s>>>(y, inv_perm, topk_w, y_rows, Mc, K, topk, apply_on_input,
-                                                      out);
+    // few tokens: each token's 512-column slabs are split over up to four
+    // waves (slices of grid.y), so that at least ~256 blocks take part
+    const int64_t nslab = (K + kWave * 8 - 1) / (kWave * 8);
+    int64_t ys = (256 + blocks - 1) / blocks;
+    ys = ys < 1 ? 1 : (ys > 4 ? 4 : ys);
+    ys = ys < nslab ? ys : nslab;
+    const int64_t spw = (nslab + ys - 1) / ys;
+    ys = (nslab + spw - 1) / spw;   // no empty slice
+    k_unpermute<<<dim3((unsigned)blocks, (unsigned)ys), kThreads, 0, s>>>(y, inv_perm, topk_w, y_rows, Mc, K, topk,
+                                                                        apply_on_input, out);
     return hipGetLastError();
 }
 
