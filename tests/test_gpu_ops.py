@@ -97,25 +97,34 @@ def test_silu_mul_quant_parity(masked, rows, n):
         assert np.all(qg[other] == 0xAB) and np.all(sg[other] == -7.0)
 
 
-def test_silu_mul_quant_counts_cut_at_the_slot():
+@pytest.mark.parametrize("offs,cnt", [
+    # all but expert 1 run past their slots; the last slot ends past the rows
+    ([0, 128, 256, 256, 512, 750], [200, 5, 40, 300, 250]),
+    # inconsistent offsets: slots that go backwards and overlap
+    ([0, 400, 100, 650, 50, 700], [500, 300, 600, 100, 900]),
+])
+def test_silu_mul_quant_counts_cut_at_the_slot(offs, cnt):
     """Counts that run past their expert's slot (into the next slot or past
-    the array) are cut there: exactly the rows the oracle writes for the cut
-    counts are written, and nothing else."""
-    announce("silu quant cut counts")
+    the array) are cut there, and inconsistent offsets stay in bounds: the
+    rows written are exactly those of the cut slots, each with the oracle's
+    codes for that row, and nothing else is touched."""
+    announce("silu quant cut counts", offs, cnt)
     rng = np.random.default_rng(11)
     rows, n = 700, 256
     h = gen.bf16_bits((rng.standard_normal((rows, 2 * n)) * 4).astype(np.float32))
-    offs = np.array([0, 128, 256, 256, 512, 750], np.int32)       # 5 experts; the last slot ends past rows
-    cnt = np.array([200, 5, 40, 300, 250], np.int32)                # all but expert 1 run past their slots
+    offs = np.asarray(offs, np.int32)
+    cnt = np.asarray(cnt, np.int32)
     El = len(cnt)
-    cut = np.minimum(cnt, np.minimum(offs[1:], rows) - offs[:-1]).astype(np.int32)
+    lo = np.minimum(offs[:-1], rows)
+    hi = np.minimum(np.minimum(lo + cnt, rows), np.maximum(offs[1:], lo))
+    cut = (hi - lo).astype(np.int32)
     q = filled((rows, n), torch.uint8, 0xAB)
     s = filled((rows, n // 128), torch.float32, -7.0)
     moe.moe_act_quant(dev(h), n, moe.MOE_ACT_SILU_MUL, q, s, dev(offs), dev(cnt), El)
     qg, sg = host(q), host(s)
-    cap_offs = np.concatenate([offs[:-1], [rows]]).astype(np.int32)   # the oracle's slots, last one cut at rows
-    qr, sr = oracle.silu_mul_quant(h, cap_offs, cut, El)
-    rows_v = valid_rows(offs, cut)
+    # every row's codes depend on that row only: the oracle on all rows
+    qr, sr = oracle.silu_mul_quant(h)
+    rows_v = np.unique(valid_rows(lo, cut))
     np.testing.assert_array_equal(sg[rows_v], sr[rows_v])
     np.testing.assert_array_equal(qg[rows_v], qr[rows_v])
     other = np.setdiff1d(np.arange(rows), rows_v)

@@ -56,8 +56,10 @@ __global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restri
                                                         uint8_t* __restrict__ q,
                                                         float* __restrict__ q_s) {
     __shared__ int s_off[kMaxLocalExperts];        // first row of each expert's slot
-    __shared__ int s_vpre[kMaxLocalExperts + 1];   // valid rows of the experts before e
-    __shared__ int s_wsum[kThreads / kWave];
+    // valid rows of the experts before e, in 64 bits: slots that overlap
+    // (inconsistent offsets) may add up to more than 2^31 rows
+    __shared__ int64_t s_vpre[kMaxLocalExperts + 1];
+    __shared__ int64_t s_wsum[kThreads / kWave];
     __shared__ float s_silu[TABLE ? kSiluEntries : 1];
     const bool masked = offsets != nullptr;
     const int lane = threadIdx.x & (kWave - 1);
@@ -65,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restri
     if (masked) {
         // valid rows per expert (clamped to the slot and to [0, rows)), then
         // their exclusive scan; four experts per thread covers El <= 1024
-        int v[4], tsum = 0;
+        int64_t v[4], tsum = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = threadIdx.x * 4 + j;
@@ -75,14 +77,14 @@ __global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restri
                 int64_t hi = min(lo + (int64_t)max(counts[e], 0), rows);
                 hi = min(hi, max((int64_t)offsets[e + 1], lo));   // offsets has El + 1 entries
                 s_off[e] = (int)lo;
-                v[j] = (int)(hi - lo);
+                v[j] = hi - lo;
             }
             tsum += v[j];
         }
-        const int incl = wave_inclusive_scan(tsum);
+        const int64_t incl = wave_inclusive_scan(tsum);
         if (lane == kWave - 1) s_wsum[wave] = incl;
         __syncthreads();
-        int run = incl - tsum;
+        int64_t run = incl - tsum;
         for (int w = 0; w < wave; ++w) run += s_wsum[w];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -95,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void k_act_quant(const uint16_t* __restri
     if (TABLE) silu_table_build(s_silu);
     __syncthreads();
     const int ng = n / kGroup;
-    const int64_t nrows = masked ? (int64_t)s_vpre[El] : rows;   // rows of the work sequence
+    const int64_t nrows = masked ? s_vpre[El] : rows;   // rows of the work sequence
     const int64_t total = nrows * ng;
     const int sub = threadIdx.x & (kLanesPerGroup - 1);
     // each block takes a contiguous range of groups, 16 at a time, so a

@@ -214,11 +214,12 @@ __device__ __forceinline__ int local_expert(int id, const int32_t* __restrict__ 
 }
 
 // inclusive prefix sum over the 64 lanes of the wave
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
+template <typename T>
+__device__ __forceinline__ T wave_inclusive_scan(T v) {
     const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
-        int u = __shfl_up(v, d, kWave);
+        const T u = __shfl_up(v, d, kWave);
         if (lane >= d) v += u;
     }
     return v;
