@@ -41,8 +41,9 @@ hipError_t launch_quant_permute(const uint16_t* x, const int32_t* ids, const flo
                                 int32_t* counts_copy, hipStream_t s);
 
 // ---- activation quantisation ------------------------------------------------
-// rows_hint: the rows expected to be valid (the chunk's routed pairs in the
-// forward; rows otherwise), which decides whether the SiLU table pays
+// rows_hint: at most this many rows are valid (the chunk's routed pairs in
+// the forward; rows otherwise).  It sizes the grid of a masked launch, which
+// walks the valid rows only, and decides whether the SiLU table pays.
 hipError_t launch_act_quant(const uint16_t* in, int64_t rows, int n, int mode,
                             const int32_t* offsets, const int32_t* counts, int El, uint8_t* q,
                             float* q_s, int64_t rows_hint, hipStream_t s);
