@@ -183,7 +183,10 @@ int moe_grouped_gemm_fp8_act_quant(const uint8_t* a, const float* a_s, const uin
  * then per group of 128: d = max(amax|v|, 1e-10), q_s = d/448,
  * q = e4m3(v * (448/d)) (saturating, nearest-even).
  * expert_offsets / counts: NULL = every row valid; otherwise only valid rows
- * (as in moe_grouped_gemm_fp8) are written.  q [rows,n], q_s [rows,n/128]. */
+ * (as in moe_grouped_gemm_fp8) are read and written: the rows of expert e are
+ * [expert_offsets[e], expert_offsets[e] + counts[e]), cut at
+ * expert_offsets[e+1] and at rows, so inconsistent offsets or counts never
+ * move an access outside [0, rows).  q [rows,n], q_s [rows,n/128]. */
 int moe_act_quant(const uint16_t* in, int64_t rows, int32_t n, int32_t mode,
                   const int32_t* expert_offsets, const int32_t* counts, int32_t El, uint8_t* q,
                   float* q_s, void* stream);
