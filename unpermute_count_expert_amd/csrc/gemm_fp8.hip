@@ -482,22 +482,31 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
 
         if constexpr (!KACT) {
             // ---- epilogue: each lane owns 4 adjacent columns of 16 rows ----
+            // Streaming stores: the output is read back from HBM by the next
+            // kernel, so it need not take L2 lines from the operands.  Rows
+            // are addressed from the lane's first row by 32-bit offsets; a
+            // wave whose 16 * MI rows are all valid stores without row tests.
             if (wave_has_rows) {
-                const int col = cur.n0 + wn * 64 + 4 * fr;
+                const int row0 = cur.m0 + wm * 16 * MI + (lane >> 4) * 4;
+                uint16_t* const base = out + (int64_t)row0 * n_out + (cur.n0 + wn * 64 + 4 * fr);
+                auto store_row = [&](int mi, int v) __attribute__((always_inline)) {
+                    v2i qv;
+                    qv.x = (int)f32x2_to_bf16x2(acc[mi][0][v], acc[mi][1][v]);
+                    qv.y = (int)f32x2_to_bf16x2(acc[mi][2][v], acc[mi][3][v]);
+                    __builtin_nontemporal_store(qv, reinterpret_cast<v2i*>(base + (mi * 16 + v) * n_out));
+                };
+                if (cur.m0 + wm * 16 * MI + 16 * MI <= cur.row_end) {
 #pragma unroll
-                for (int mi = 0; mi < MI; ++mi)
+                    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int row = cur.m0 + wm * 16 * MI + mi * 16 + (lane >> 4) * 4 + v;
-                        if (row < cur.row_end) {
-                            v2i qv;
-                            qv.x = (int)f32x2_to_bf16x2(acc[mi][0][v], acc[mi][1][v]);
-                            qv.y = (int)f32x2_to_bf16x2(acc[mi][2][v], acc[mi][3][v]);
-                            // streaming store: the output is read back from HBM by the
-                            // next kernel, so it need not take L2 lines from the operands
-                            __builtin_nontemporal_store(qv, reinterpret_cast<v2i*>(out + (int64_t)row * n_out + col));
-                        }
-                    }
+                        for (int v = 0; v < 4; ++v) store_row(mi, v);
+                } else {
+#pragma unroll
+                    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            if (row0 + mi * 16 + v < cur.row_end) store_row(mi, v);
+                }
             }
         } else {
             // ---- epilogue: SiLU-and-mul and per-128 requant ----------------
