@@ -125,25 +125,16 @@ __device__ __forceinline__ void dma4(uint32_t m0, uint32_t voff, const void* sba
                  : "memory", "m0");
 }
 
-// Wait until at most n of this wave's vector-memory loads issued after the
+// Wait until at most N of this wave's vector-memory loads issued after the
 // one waited for are outstanding, then the workgroup barrier.  Loads retire
 // in issue order, so a younger load can never be the reason the count is
 // low; stores may retire in any order, which only makes the wait longer.
-#define MOE_WAIT_CASE(n)                                                              \
-    case n:                                                                           \
-        asm volatile("s_waitcnt vmcnt(" #n ") lgkmcnt(0)\n\ts_barrier" ::: "memory"); \
-        break;
-__device__ __forceinline__ void wait_loads_barrier(int n) {
-    switch (n) {
-        MOE_WAIT_CASE(1) MOE_WAIT_CASE(2) MOE_WAIT_CASE(3) MOE_WAIT_CASE(4) MOE_WAIT_CASE(5)
-        MOE_WAIT_CASE(6) MOE_WAIT_CASE(7) MOE_WAIT_CASE(8) MOE_WAIT_CASE(9) MOE_WAIT_CASE(10)
-        MOE_WAIT_CASE(11) MOE_WAIT_CASE(12) MOE_WAIT_CASE(13) MOE_WAIT_CASE(14) MOE_WAIT_CASE(15)
-        MOE_WAIT_CASE(16) MOE_WAIT_CASE(17) MOE_WAIT_CASE(18) MOE_WAIT_CASE(19) MOE_WAIT_CASE(20)
-        default:
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    }
+// N is a compile-time count: a count chosen at run time would need a
+// dispatch over literal vmcnt values, which costs ~5% of the GEMM's time.
+template <int N>
+__device__ __forceinline__ void wait_loads_barrier_c() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
-#undef MOE_WAIT_CASE
 
 // rows [lo, hi) of expert e, clamped to [0, cap_rows)
 __device__ __forceinline__ void rows_of(const int32_t* __restrict__ offsets, const int32_t* __restrict__ counts,
@@ -431,9 +422,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
             for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
         for (int g = 0; g < kg; ++g, ++i) {
-            // step i's DMAs complete, in every wave
-            wait_loads_barrier(__builtin_amdgcn_readfirstlane(
-                loads - (slot == 0 ? d_end0 : (slot == 1 ? d_end1 : d_end2))));
+            // step i's DMAs complete, in every wave.  The loads issued after
+            // them are the next kStages - 2 steps' DMAs: none with two
+            // stages, where vmcnt(0) is exact; with three, one step's or (at
+            // the end of the stream) none.  Waiting for fewer outstanding
+            // loads than issued after them is always safe, so two fixed
+            // counts cover every case without a dispatch.
+            if constexpr (kStages == 2) {
+                wait_loads_barrier_c<0>();
+            } else {
+                const int n_after = __builtin_amdgcn_readfirstlane(
+                    loads - (slot == 0 ? d_end0 : (slot == 1 ? d_end1 : d_end2)));
+                if (n_after >= kDmaPerStep) wait_loads_barrier_c<kDmaPerStep>();
+                else wait_loads_barrier_c<0>();
+            }
             if (i + kStages - 1 < S) MOE_DMA_NEXT();   // into the slot step i-1 has released
             if (wave_has_rows) {
                 const uint32_t sb = (uint32_t)slot * kStage;
