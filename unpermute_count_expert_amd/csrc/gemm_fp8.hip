@@ -403,7 +403,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
     if (S > 0) MOE_DMA_NEXT();
     if (kStages > 2 && S > 1) MOE_DMA_NEXT();
 
-    int64_t i = 0;   // compute step
+    // DMA steps still to issue after the prologue's (a 32-bit scalar
+    // countdown: a block runs at most a few thousand steps)
+    int dma_left = (int)(S > kStages - 1 ? S - (kStages - 1) : 0);
     int slot = 0;    // its ring slot
     TileCursor cur;
     walk.start(cur, t_lo);
@@ -421,7 +423,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-        for (int g = 0; g < kg; ++g, ++i) {
+        for (int g = 0; g < kg; ++g) {
             // step i's DMAs complete, in every wave.  The loads issued after
             // them are the next kStages - 2 steps' DMAs: none with two
             // stages, where vmcnt(0) is exact; with three, one step's or (at
@@ -436,7 +438,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
                 if (n_after >= kDmaPerStep) wait_loads_barrier_c<kDmaPerStep>();
                 else wait_loads_barrier_c<0>();
             }
-            if (i + kStages - 1 < S) MOE_DMA_NEXT();   // into the slot step i-1 has released
+            if (dma_left > 0) {   // into the slot step i-1 has released
+                MOE_DMA_NEXT();
+                --dma_left;
+            }
             if (wave_has_rows) {
                 const uint32_t sb = (uint32_t)slot * kStage;
                 const uint8_t* alo = smem + (sb + fA_lo);
