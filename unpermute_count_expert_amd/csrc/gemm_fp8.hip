@@ -406,7 +406,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
     // DMA steps still to issue after the prologue's (a 32-bit scalar
     // countdown: a block runs at most a few thousand steps)
     int dma_left = (int)(S > kStages - 1 ? S - (kStages - 1) : 0);
-    int slot = 0;    // its ring slot
+    int slot = 0;    // ring slot of the step being computed
     TileCursor cur;
     walk.start(cur, t_lo);
     while (cur.valid) {
@@ -424,7 +424,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
             for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
         for (int g = 0; g < kg; ++g) {
-            // step i's DMAs complete, in every wave.  The loads issued after
+            // this step's DMAs complete, in every wave.  The loads issued after
             // them are the next kStages - 2 steps' DMAs: none with two
             // stages, where vmcnt(0) is exact; with three, one step's or (at
             // the end of the stream) none.  Waiting for fewer outstanding
@@ -438,7 +438,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
                 if (n_after >= kDmaPerStep) wait_loads_barrier_c<kDmaPerStep>();
                 else wait_loads_barrier_c<0>();
             }
-            if (dma_left > 0) {   // into the slot step i-1 has released
+            if (dma_left > 0) {   // into the slot the previous step has released
                 MOE_DMA_NEXT();
                 --dma_left;
             }
