@@ -201,6 +201,13 @@ CASES = [
     ("C5u_on", gen.CONFIGS["C5u_on"], 1),
     ("C5h", gen.CONFIGS["C5h"], 0),
     ("C5h_on", gen.CONFIGS["C5h_on"], 1),
+    # more than eight experts a token (the unpermute's second path), K past
+    # whole 512-column slabs, 32-row alignment, uneven chunks, on-input weights
+    ("topk12_K2176_align32", gen.small_config(M=200, K=2176, N=256, Eg=48, El=24, topk=12, chunk_size=96,
+                                              routing="zipf", seed=24, ep_rank_of_2=1, align=32), 1),
+    # hot routing in chunks that do not divide M, 64-row alignment
+    ("hot_align64_chunked", gen.small_config(M=1000, K=1024, N=512, Eg=64, El=64, topk=6, chunk_size=300,
+                                             routing="hot", seed=25, align=64), 0),
     # the most local experts the library takes (1024), ~16 rows each
     ("max_experts_1024", gen.small_config(M=2048, K=256, N=128, Eg=1024, El=1024, topk=8, chunk_size=0,
                                           routing="softmax", seed=23), 0),
