@@ -294,8 +294,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
     const int nslots = gridDim.x >> 3;
     const int64_t t_lo = total * xcd / 8 + (blockIdx.x >> 3);
     const int64_t t_hi = total * (xcd + 1) / 8;
-    const int64_t ntiles = t_lo < t_hi ? (t_hi - t_lo + nslots - 1) / nslots : 0;
-    const int64_t S = ntiles * kg;   // this block's K steps, over all its tiles
 
     TileWalk walk;
     walk.offsets = offsets;
@@ -400,12 +398,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
     } while (0)
     if (dT.valid) MOE_DMA_OFFSETS();
     // the DMA stream runs kStages - 1 steps ahead
-    if (S > 0) MOE_DMA_NEXT();
-    if (kStages > 2 && S > 1) MOE_DMA_NEXT();
+    if (dT.valid) MOE_DMA_NEXT();
+    if (kStages > 2 && dT.valid) MOE_DMA_NEXT();
 
-    // DMA steps still to issue after the prologue's (a 32-bit scalar
-    // countdown: a block runs at most a few thousand steps)
-    int dma_left = (int)(S > kStages - 1 ? S - (kStages - 1) : 0);
     int slot = 0;    // ring slot of the step being computed
     TileCursor cur;
     walk.start(cur, t_lo);
@@ -438,10 +433,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
                 if (n_after >= kDmaPerStep) wait_loads_barrier_c<kDmaPerStep>();
                 else wait_loads_barrier_c<0>();
             }
-            if (dma_left > 0) {   // into the slot the previous step has released
-                MOE_DMA_NEXT();
-                --dma_left;
-            }
+            // into the slot the previous step has released, while the DMA
+            // cursor (kStages - 1 steps ahead) has steps left: a flag of the
+            // tile walk, so no step count is compared
+            if (dT.valid) MOE_DMA_NEXT();
             if (wave_has_rows) {
                 const uint32_t sb = (uint32_t)slot * kStage;
                 const uint8_t* alo = smem + (sb + fA_lo);
