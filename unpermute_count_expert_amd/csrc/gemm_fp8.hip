@@ -356,6 +356,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
     uint32_t voA[kADma], voB0 = 0, voB1 = 0, voB2 = 0, voB3 = 0, voS = 0;
 #pragma unroll
     for (int j = 0; j < kADma; ++j) voA[j] = 0;
+    // the DMA cursor's tile: its A rows, weight rows and A scales at its
+    // current K step, set per tile and advanced by one step per DMA step
+    const uint8_t* dA = a;
+    const uint8_t* dB = w;
+    const float* dS = a_s;
 #define MOE_DMA_OFFSETS()                                                             \
     do {                                                                              \
         const int last_ = max(dT.row_end - 1 - dT.m0, 0);                             \
@@ -367,15 +372,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
         voB2 = (uint32_t)(min(nB[2], nlast_) * k_in + cB[2] * 16);                    \
         voB3 = (uint32_t)(min(nB[3], nlast_) * k_in + cB[3] * 16);                    \
         voS = (uint32_t)(min(rS, last_) * kg * 4);                                    \
+        const int64_t brow0_ = KACT ? (int64_t)((wave & 1) ? n_half : 0) + (dT.n0 >> 1) \
+                                    : (int64_t)dT.n0;                                 \
+        dA = a + (int64_t)dT.m0 * k_in;                                               \
+        dB = w + ((int64_t)dT.e * n_out + brow0_) * k_in;                             \
+        dS = a_s + (int64_t)dT.m0 * kg;                                               \
     } while (0)
     // one step of DMAs into ring slot d_slot, then advance the cursor
 #define MOE_DMA_NEXT()                                                                \
     do {                                                                              \
-        const uint8_t* sa_ = a + ((int64_t)dT.m0 * k_in + d_g * BK);                  \
-        const int64_t brow_ = KACT ? (int64_t)((wave & 1) ? n_half : 0) + (dT.n0 >> 1)  \
-                                   : (int64_t)dT.n0;                                  \
-        const uint8_t* sb_ = w + (((int64_t)dT.e * n_out + brow_) * k_in + d_g * BK); \
-        const float* ss_ = a_s + ((int64_t)dT.m0 * kg + d_g);                         \
+        const uint8_t* sa_ = dA;                                                      \
+        const uint8_t* sb_ = dB;                                                      \
+        const float* ss_ = dS;                                                        \
+        dA += BK;                                                                     \
+        dB += BK;                                                                     \
+        dS += 1;                                                                      \
         const uint32_t base_ = lds_smem + d_slot * kStage;                            \
         _Pragma("unroll") for (int j_ = 0; j_ < kADma; ++j_)                          \
             dma16(base_ + (wave * kADma + j_) * 1024, voA[j_], sa_);                  \
