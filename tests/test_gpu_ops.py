@@ -493,6 +493,23 @@ def test_gemm_masked_batched_layout(El, max_tokens, n_out, k_in, tile):
 
 
 # ---------------------------------------------------------------- unpermute
+def test_unpermute_empty_y_gives_zero():
+    """With no rows in y every pair is dropped, so every token's output is +0,
+    also where each token's columns are split over several waves (few tokens,
+    K past whole 512-column slabs)."""
+    announce("unpermute empty y")
+    rng = np.random.default_rng(31)
+    M, K, T = 37, 2176, 8
+    y = np.zeros((0, K), np.uint16)
+    inv = rng.integers(0, 500, (M, T)).astype(np.int32)
+    w = rng.uniform(0, 1, (M, T)).astype(np.float32)
+    out = filled((M, K), "bf16", 0x7FC1)
+    moe.moe_unpermute_weight_reduce(dev(y), dev(inv), dev(w), 0, out)
+    got = host(out, bf16=True)
+    assert np.all(got == 0)
+    np.testing.assert_array_equal(got, oracle.unpermute(y, np.full((M, T), -1, np.int32), w, 0))
+
+
 @pytest.mark.parametrize("M,K,T,on_input", [(1, 128, 1, 0), (513, 2048, 8, 0), (100, 384, 3, 1),
                                             (16384, 2048, 8, 0),
                                             (77, 2176, 8, 1),     # a second, partial pass of slabs
