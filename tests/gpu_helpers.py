@@ -1,4 +1,6 @@
 """Helpers shared by the GPU parity tests: device transfer and comparisons."""
+import json
+import os
 import sys
 
 import numpy as np
@@ -6,6 +8,31 @@ import torch
 
 DEV = "cuda:0"
 RTOL, ATOL = 1e-2, 1e-3   # bf16 outputs: |gpu - ref| <= ATOL + RTOL*|ref|
+
+
+# Parity statistics of the layer tests (outputs beyond the tolerance, code
+# flips), printed in pytest's terminal summary and, when MOE_PARITY_RECORD
+# names a file, written there as JSON lines.
+PARITY_RECORD = []
+
+
+def record(**stats):
+    PARITY_RECORD.append(stats)
+    path = os.environ.get("MOE_PARITY_RECORD")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(stats) + "\n")
+
+
+def tight_excess(got_bits, ref_bits):
+    """(number of outputs beyond ATOL + RTOL|ref|, number compared, largest
+    |gpu - ref| / (ATOL + RTOL|ref|)); NaN pairs count as equal."""
+    g, r = bf16_f64(got_bits), bf16_f64(ref_bits)
+    tol = ATOL + RTOL * np.abs(r)
+    ratio = np.abs(g - r) / tol
+    ratio[np.isnan(g) & np.isnan(r)] = 0.0
+    ratio[np.isnan(ratio)] = np.inf
+    return int((ratio > 1.0).sum()), int(ratio.size), float(ratio.max()) if ratio.size else 0.0
 
 
 def announce(*what):

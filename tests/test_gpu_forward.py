@@ -5,18 +5,26 @@ moe_forward_chunked runs, in the same order), so every intermediate can be
 checked against the oracle fed with the GPU's own input to that op:
 
 * count, offsets, inv_perm, row_src, permuted rows/scales: bit-exact;
-* h = GEMM(w13): within the GEMM bound of the oracle on the same a_perm;
+* h = GEMM(w13): within 1e-3 + 1e-2|ref| of the oracle's exact GEMM of the
+  same a_perm rows, on every output;
 * act_q/act_s: bit-exact against the oracle's SiLU-mul requant of the GPU h
   (the quantisation decision is taken on the identical bf16 h);
-* y = GEMM(w2): within the GEMM bound of the oracle on the GPU act_q;
+* the fused GEMM w13 + SiLU-mul requant: bit-exact with that chain, and
+  against the oracle's own h bit-exact on every act group whose h the GPU
+  rounds alike;
+* y = GEMM(w2): within 1e-3 + 1e-2|ref| of the oracle on the GPU act_q;
 * out: bit-exact against the oracle's unpermute of the GPU y;
 * moe_forward_chunked: bit-exact against the chain, chunked == unchunked;
-* end to end against the all-oracle layer: within 1e-3 + 1e-2|ref| for every
-  token whose act codes the GPU and the oracle decide alike; a token whose
-  h differs from the exact sum by one bf16 rounding can land a group amax or
-  a code on the other side of a rounding boundary, and only such tokens may
-  exceed it (they must stay within 1e-2 + 5e-2|ref|); at most 1% of the act
-  codes may be decided differently.
+* end to end, hybrid: the GPU's y rows of the sampled tokens within
+  1e-3 + 1e-2|ref| of the oracle's GEMM w2 of the GPU's act codes, and the
+  output within that tolerance propagated through the exact weighted reduce
+  (sum_k |w'_k| tol(y_k) plus one bf16 rounding; where the topk rows cancel,
+  that can exceed 1e-3 + 1e-2|out|, and such outputs are counted);
+* end to end against the all-oracle layer: the same tolerance, except on
+  outputs reached by act codes decided differently (a bf16 rounding of h one
+  ulp from the oracle's landing on the other side of an e4m3 rounding
+  boundary, on rows whose h is checked): at most 1% of the codes and 0.5% of
+  the outputs, both counted and recorded.
 
 Full-size layers (4096 and 16384 tokens) are checked on sampled rows/tokens,
 which the oracle computes on their own (rows are independent).
@@ -29,8 +37,8 @@ import oracle
 import unpermute_count_expert_amd as moe
 from unpermute_count_expert_amd import generators as gen
 from unpermute_count_expert_amd.pipeline import StepBuffers, run_steps, step_ops
-from tests.gpu_helpers import (ATOL, RTOL, announce, assert_gemm_close, bf16_f64, dev, filled, host,
-                               valid_rows)
+from tests.gpu_helpers import (ATOL, RTOL, announce, bf16_f64, bf16_ulp, dev, filled, host, record,
+                               tight_excess, valid_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -69,7 +77,59 @@ def _sample(M, rng, n):
     return np.unique(np.concatenate([[0, 1, M // 2, M - 2, M - 1], rng.choice(M, n, replace=False)]))
 
 
-def check_layer(cfg, on_input, n_sample_rows=64, n_sample_tokens=48):
+def _sample_rows(offsets, counts, rng, n):
+    """All valid rows when there are at most n; otherwise every non-empty
+    expert's first and last row (tile and expert boundaries) plus n random
+    ones."""
+    rows = valid_rows(offsets, counts)
+    if len(rows) <= n:
+        return np.arange(len(rows))
+    firsts = np.concatenate([[0], np.cumsum(counts)[:-1]])[counts > 0]
+    lasts = np.cumsum(counts)[counts > 0] - 1
+    return np.unique(np.concatenate([firsts, lasts, rng.choice(len(rows), n, replace=False)]))
+
+
+def _tight(name, what, got_bits, ref_bits):
+    """Asserts the tolerance 1e-3 + 1e-2|ref| on every output; returns the
+    largest |gpu - ref| / tolerance."""
+    n_bad, n, worst = tight_excess(got_bits, ref_bits)
+    assert n_bad == 0, f"{name} {what}: {n_bad} of {n} outputs beyond 1e-3 + 1e-2|ref| (worst {worst:.3g}x)"
+    return worst
+
+
+# At most this fraction of the end-to-end outputs may differ from the
+# all-oracle layer by more than 1e-3 + 1e-2|ref| (measured: 0 to 0.12%).
+# Each such output is explained, because every step is checked on the GPU's
+# own intermediates: h is within the tolerance of the exact GEMM (on the
+# sampled tokens' own rows too), so its bf16 rounding may sit one ulp from
+# the oracle's; an act group then quantised from a different h can land a
+# code on the other side of an e4m3 rounding boundary (a flip, at most 1% of
+# codes); and from the GPU's act codes on, the GPU output is within the
+# propagated tolerance of the oracle's GEMM w2 and unpermute (the hybrid
+# check).  A flipped code moves one act value by one e4m3 step, which reaches
+# every output of its token through w2.
+MAX_E2E_EXCESS_FRAC = 5e-3
+
+
+def reduce_bound(y_ref_bits, inv_small, w_prime, out_ref_bits):
+    """Allowed |gpu - ref| of the unpermute's output when each of its y rows
+    may be off by the tolerance 1e-3 + 1e-2|y|: the reduce is exact given y
+    (bit-exact with the oracle), so the y errors reach out[t] weighted by
+    |w'_k|, plus one bf16 rounding of out; never below the tolerance itself."""
+    y = bf16_f64(y_ref_bits)
+    tol_y = ATOL + RTOL * np.abs(y)
+    M, T = inv_small.shape
+    prop = np.zeros((M, y.shape[1]))
+    for k in range(T):
+        r = inv_small[:, k]
+        ok = r >= 0
+        prop[ok] += np.abs(w_prime[ok, k])[:, None] * tol_y[r[ok]]
+    o = bf16_f64(out_ref_bits)
+    tol = ATOL + RTOL * np.abs(o)
+    return np.maximum(tol, prop + bf16_ulp(np.abs(o) + prop))
+
+
+def check_layer(cfg, on_input, n_sample_rows=512, n_sample_tokens=48):
     inp = _inputs(cfg)
     M, K, N, T, El = cfg.M, cfg.K, cfg.N, cfg.topk, cfg.El
     layer = _layer(inp)
@@ -79,6 +139,7 @@ def check_layer(cfg, on_input, n_sample_rows=64, n_sample_tokens=48):
                                           "row_src", "act_q", "act_s", "count_only")}
     g["h"], g["y"], g["out"] = host(b.h, bf16=True), host(b.y, bf16=True), host(b.out, bf16=True)
     rng = np.random.default_rng(cfg.seed + 1000 * on_input)
+    name = f"{cfg.name}{'_on' if on_input else ''}"
 
     # -- input quant and routing bookkeeping: bit-exact on everything
     a_q, a_s = oracle.act_quant_identity(inp.x)
@@ -107,12 +168,13 @@ def check_layer(cfg, on_input, n_sample_rows=64, n_sample_tokens=48):
     assert (fa[np.setdiff1d(np.arange(fa.shape[0]), rows)] == 0x5A).all(), "quant_permute wrote a padding row"
     del fb
 
-    # -- GEMM w13 on sampled valid rows
-    pick = _sample(len(rows), rng, n_sample_rows)
+    # -- GEMM w13 against the oracle's exact GEMM of the same rows: within
+    #    1e-3 + 1e-2|ref| on every output (all rows of the small layers; each
+    #    expert's first and last row plus 512 others on the large ones)
+    pick = _sample_rows(r["expert_offsets"], r["counts"], rng, n_sample_rows)
     sr, se = rows[pick], row_exp[pick]
     h_ref = oracle.gemm_rows(g["a_perm"][sr], g["a_perm_s"][sr], se, inp.w13, inp.w13_s)
-    h_abs = oracle.gemm_rows(g["a_perm"][sr] & 0x7F, g["a_perm_s"][sr], se, inp.w13 & 0x7F, inp.w13_s)
-    assert_gemm_close(g["h"][sr], h_ref, h_abs, f"{cfg.name} h")
+    worst_h = _tight(name, "h", g["h"][sr], h_ref)
 
     # -- SiLU-mul requant of the GPU's own h: bit-exact on every valid row
     q, s = oracle.silu_mul_quant(g["h"][rows])
@@ -130,11 +192,23 @@ def check_layer(cfg, on_input, n_sample_rows=64, n_sample_tokens=48):
     np.testing.assert_array_equal(fs[rows], g["act_s"][rows])
     pad = np.setdiff1d(np.arange(fq.shape[0]), rows)
     assert (fq[pad] == 0xA5).all() and (fs[pad] == -7.0).all(), "fused GEMM wrote a padding row"
+    # ... and directly against the oracle (its exact GEMM, then its SiLU-mul
+    # requant): an act group is a function of its 128 gate and 128 up values
+    # of h, so every group whose h the GPU rounds exactly as the oracle does
+    # must have the oracle's codes and scale bit for bit; the other groups may
+    # differ in a few codes (flips), at most 1% of codes overall
+    q_or, s_or = oracle.silu_mul_quant(h_ref)
+    ng = N // 128
+    hg = (g["h"][sr] == h_ref).reshape(len(sr), 2, ng, 128).all(axis=(1, 3))   # [rows, groups]: h alike
+    q_f = fq[sr].reshape(len(sr), ng, 128)
+    np.testing.assert_array_equal(q_f[hg], q_or.reshape(len(sr), ng, 128)[hg])
+    np.testing.assert_array_equal(fs[sr][hg], s_or[hg])
+    fused_flip = float((fq[sr] != q_or).mean())
+    assert fused_flip <= 1e-2, f"{name}: fused GEMM codes differ from the oracle's on {fused_flip:.2%}"
 
-    # -- GEMM w2 on the GPU's act_q, sampled rows
+    # -- GEMM w2 on the GPU's act_q: within 1e-3 + 1e-2|ref| on every output
     y_ref = oracle.gemm_rows(g["act_q"][sr], g["act_s"][sr], se, inp.w2, inp.w2_s)
-    y_abs = oracle.gemm_rows(g["act_q"][sr] & 0x7F, g["act_s"][sr], se, inp.w2 & 0x7F, inp.w2_s)
-    assert_gemm_close(g["y"][sr], y_ref, y_abs, f"{cfg.name} y")
+    worst_y = _tight(name, "y", g["y"][sr], y_ref)
 
     # -- unpermute of the GPU's y: bit-exact
     np.testing.assert_array_equal(g["out"], oracle.unpermute(g["y"], g["inv_perm"], inp.topk_weights, on_input))
@@ -151,39 +225,64 @@ def check_layer(cfg, on_input, n_sample_rows=64, n_sample_tokens=48):
             np.testing.assert_array_equal(
                 pcc[c], oracle.count(inp.topk_ids[c * cs:(c + 1) * cs], inp.expert_map, cfg.Eg, El)[0])
 
-    # -- end to end against the all-oracle layer on sampled tokens
+    # -- end to end on sampled tokens.  Hybrid: from the GPU's act codes (the
+    #    oracle's SiLU-mul requant of the GPU's h, asserted equal above) the
+    #    oracle's GEMM w2 and unpermute.  The GPU's y rows of these tokens
+    #    must be within 1e-3 + 1e-2|ref| of the oracle's, and its output
+    #    within that tolerance propagated through the (exact) weighted reduce.
     toks = _sample(M, rng, n_sample_tokens)
-    ref = bf16_f64(oracle.forward_chunked(inp.x[toks], inp.topk_ids[toks], inp.topk_weights[toks],
-                                          inp.expert_map, inp.w13, inp.w13_s, inp.w2, inp.w2_s, cfg.Eg,
-                                          apply_on_input=on_input, align=cfg.align))
-    got = bf16_f64(g["out"][toks])
-    # tokens where the oracle's own h leads to different act codes than the GPU's h
-    flipped = np.zeros(len(toks), bool)
+    inv_t = g["inv_perm"][toks]
+    urows = np.unique(inv_t[inv_t >= 0]).astype(np.int64)
+    ex_u = (np.searchsorted(r["expert_offsets"], urows, side="right") - 1).astype(np.int32)
+    y_hyb = (oracle.gemm_rows(g["act_q"][urows], g["act_s"][urows], ex_u, inp.w2, inp.w2_s) if len(urows)
+             else np.zeros((0, K), np.uint16))
+    _tight(name, "y of the sampled tokens", g["y"][urows], y_hyb)
+    inv_small = np.where(inv_t >= 0, np.searchsorted(urows, np.maximum(inv_t, 0)), -1).astype(np.int32)
+    w_t = inp.topk_weights[toks]
+    out_hyb = oracle.unpermute(y_hyb, inv_small, w_t, on_input)
+    w_prime = np.ones_like(w_t) if on_input else w_t
+    bound = reduce_bound(y_hyb, inv_small, w_prime, out_hyb)
+    err_h = np.abs(bf16_f64(g["out"][toks]) - bf16_f64(out_hyb))
+    assert (err_h <= bound).all(), (f"{name}: {int((err_h > bound).sum())} outputs beyond the propagated "
+                                    f"tolerance of the hybrid layer (worst {float((err_h / bound).max()):.3g}x)")
+    n_hyb_bad, _, worst_hyb = tight_excess(g["out"][toks], out_hyb)
+
+    # -- against the all-oracle layer: the same tolerance, except on outputs
+    #    reached by act-code flips, which are counted, capped and recorded;
+    #    every flip sits on a row whose h is within the tolerance
+    ref = oracle.forward_chunked(inp.x[toks], inp.topk_ids[toks], inp.topk_weights[toks], inp.expert_map,
+                                 inp.w13, inp.w13_s, inp.w2, inp.w2_s, cfg.Eg, apply_on_input=on_input,
+                                 align=cfg.align)
     n_codes = n_code_diff = 0
+    flipped = np.zeros(len(toks), bool)
     for i, t in enumerate(toks):
-        trows = g["inv_perm"][t][g["inv_perm"][t] >= 0].astype(np.int64)
+        trows = inv_t[i][inv_t[i] >= 0].astype(np.int64)
         if len(trows) == 0:
             continue
-        ex = np.searchsorted(r["expert_offsets"], trows, side="right").astype(np.int32) - 1
+        ex = (np.searchsorted(r["expert_offsets"], trows, side="right") - 1).astype(np.int32)
         h_or = oracle.gemm_rows(g["a_perm"][trows], g["a_perm_s"][trows], ex, inp.w13, inp.w13_s)
-        q_or, s_or = oracle.silu_mul_quant(h_or)
-        flipped[i] = not (np.array_equal(q_or, g["act_q"][trows]) and np.array_equal(s_or, g["act_s"][trows]))
-        n_codes += q_or.size
-        n_code_diff += int((q_or != g["act_q"][trows]).sum())
-    err = np.abs(got - ref)
-    tight = err <= ATOL + RTOL * np.abs(ref)
-    loose = err <= 1e-2 + 5e-2 * np.abs(ref)
-    bad_tight = ~tight.all(axis=1) & ~flipped
-    assert not bad_tight.any(), (f"{cfg.name}: tokens {toks[bad_tight][:5].tolist()} exceed 1e-3 + 1e-2|ref| "
-                                 f"without an act-code flip; max err {err[bad_tight].max()}")
-    assert loose.all(), f"{cfg.name}: max err {err.max()} beyond 1e-2 + 5e-2|ref|"
+        worst_h = max(worst_h, _tight(name, "h of a sampled token", g["h"][trows], h_or))
+        q_t, s_t = oracle.silu_mul_quant(h_or)
+        diff = int((q_t != g["act_q"][trows]).sum())
+        flipped[i] = diff > 0 or not np.array_equal(s_t, g["act_s"][trows])
+        n_codes += q_t.size
+        n_code_diff += diff
+    n_bad, n_out, worst_e2e = tight_excess(g["out"][toks], ref)
+    bad_tok = ~(np.abs(bf16_f64(g["out"][toks]) - bf16_f64(ref)) <= ATOL + RTOL * np.abs(bf16_f64(ref))).all(1)
     frac = n_code_diff / max(n_codes, 1)
-    print(f"{cfg.name} on_input={on_input}: {flipped.sum()} of {len(toks)} sampled tokens have an act-code "
-          f"flip ({n_code_diff} of {n_codes} codes, {frac:.2e}); max end-to-end err {err.max():.3g}",
-          flush=True)
+    record(case=name, h_worst=round(worst_h, 3), y_worst=round(worst_y, 3),
+           out_vs_hybrid_beyond_tol=f"{n_hyb_bad}/{n_out}", out_vs_hybrid_worst=round(worst_hyb, 3),
+           code_flip_frac=f"{frac:.2e}", fused_code_flip_frac=f"{fused_flip:.2e}",
+           tokens_with_flip=f"{int(flipped.sum())}/{len(toks)}", tokens_beyond_tol=int(bad_tok.sum()),
+           e2e_outputs_beyond_tol=f"{n_bad}/{n_out}", e2e_worst=round(worst_e2e, 3))
+    assert not (bad_tok & ~flipped).any(), (
+        f"{name}: tokens {toks[bad_tok & ~flipped][:5].tolist()} exceed 1e-3 + 1e-2|ref| without an act-code flip")
     # the oracle's exact h and the GPU's fp32-accumulated h decide alike on
     # almost every code; a wrong GEMM would disagree on most of them
-    assert frac <= 1e-2
+    assert frac <= 1e-2, f"{name}: {frac:.2%} of act codes flipped"
+    assert n_bad <= MAX_E2E_EXCESS_FRAC * n_out, (
+        f"{name}: {n_bad} of {n_out} outputs beyond 1e-3 + 1e-2|ref| of the all-oracle layer "
+        f"(worst {worst_e2e:.3g}x)")
 
 
 CASES = [
@@ -248,9 +347,39 @@ def test_forward_m1_and_empty():
     got, _ = _forward(layer, d, 1, 1, 0)
     ref = oracle.forward_chunked(inp.x, inp.topk_ids, inp.topk_weights, None, inp.w13, inp.w13_s, inp.w2,
                                  inp.w2_s, cfg.Eg)
-    assert np.all(np.abs(bf16_f64(got) - bf16_f64(ref)) <= 1e-2 + 5e-2 * np.abs(bf16_f64(ref)))
+    _tight("M=1", "out", got, ref)
     out = layer.forward(dev(inp.x[:0]), dev(inp.topk_ids[:0]), dev(inp.topk_weights[:0]))
     assert out.shape == (0, 128)
+
+
+@pytest.mark.parametrize("name,cfg", [("small_chunked_zipf", CASES[2][1]), ("C4b", gen.CONFIGS["C4b"]),
+                                      ("topk12", CASES[12][1])])
+def test_forward_workspace_guard_bands(name, cfg):
+    """Every slice of the forward's workspace is followed by a guard band:
+    filled with a pattern before the call, the bands (and the bytes after
+    the last slice) still hold it afterwards, so no kernel wrote past the
+    end of its slice."""
+    announce("workspace guard bands", name)
+    inp = gen.make_inputs(cfg)
+    layer = _layer(inp)
+    p = layer.problem(cfg.M, cfg.topk, cfg.chunk_size, 0)
+    total = moe.moe_forward_workspace_size(p)
+    ws = filled((total + 4096,), torch.uint8, 0xC3)   # and a band past the end
+    out = filled((cfg.M, cfg.K), "bf16", 0)
+    emap = layer.expert_map
+    moe._lib.moe_forward_chunked(p, dev(inp.x), dev(inp.topk_ids), dev(inp.topk_weights), emap, layer.w13,
+                                 layer.w13_s, layer.w2, layer.w2_s, out, ws)
+    w = host(ws)
+    sl = moe.moe_forward_workspace_slices(p)
+    ends = [o + n for o, n in sl]
+    nxt = [o for o, _ in sl[1:]] + [len(w)]
+    for i, (e, q) in enumerate(zip(ends, nxt)):
+        assert (w[e:q] == 0xC3).all(), f"guard band after slice {i} was written"
+    # the call did write inside the slices it uses
+    assert not (w[sl[0][0]:ends[0]] == 0xC3).all()
+    ref, _ = _forward(layer, dict(x=dev(inp.x), ids=dev(inp.topk_ids), w=dev(inp.topk_weights)), cfg.M,
+                      cfg.chunk_size, 0)
+    np.testing.assert_array_equal(host(out, bf16=True), ref)
 
 
 def test_forward_is_deterministic():

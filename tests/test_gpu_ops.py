@@ -2,8 +2,11 @@
 
 Same seeded inputs on both sides.  Bit-exact: counts, offsets, inv_perm,
 row_src, permuted rows and scales, act-quant codes and scales, unpermute.
-GEMM: within |d| <= 1e-3 + 1e-2|ref| of the oracle, and bit-exact against an
-int64 matmul in the integer special case.
+GEMM: on layer-like data (N(0,1) tokens in 1x128 groups, N(0, 0.02) weights
+in 128x128 blocks) within 1e-3 + 1e-2|ref| of the oracle; on uniform random
+full-range codes within the bound the fp8 MFMA's block-aligned summation
+allows (2^-12 of the absolute-term sum, see gpu_helpers.gemm_tolerance); and
+bit-exact against an int64 matmul in the integer special case.
 """
 import numpy as np
 import pytest
@@ -12,7 +15,8 @@ import torch
 import oracle
 import unpermute_count_expert_amd as moe
 from unpermute_count_expert_amd import generators as gen
-from tests.gpu_helpers import (announce, assert_gemm_close, dev, empty, filled, host, valid_rows)
+from tests.gpu_helpers import (announce, assert_bf16_close, assert_gemm_close, dev, empty, filled, host,
+                               valid_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -447,6 +451,51 @@ def test_gemm_random_parity(El, n_out, k_in, counts, align, tile):
     assert_gemm_close(out[rows], ref[rows], absterm[rows], "gemm")
     untouched = np.setdiff1d(np.arange(cap), rows)
     assert np.all(out[untouched] == 0x7FC1)
+
+
+@pytest.mark.parametrize("El,hi,n_out,k_in,tile,data", [
+    (64, 300, 2048, 512, 128, "codes"),    # ~900 128-row tiles (3 LDS stages)
+    (48, 700, 2048, 512, 256, "codes"),    # ~620 256-row tiles (2 LDS stages)
+    (64, 300, 2048, 512, 128, "layer"),
+    (48, 700, 2048, 512, 256, "layer"),
+])
+def test_gemm_full_grid_every_row(El, hi, n_out, k_in, tile, data):
+    """Several times more tiles than the persistent grid has blocks, over
+    many experts of uneven size (some empty, some exact tile multiples), with
+    a K loop of four steps: every block walks many tiles, its DMA stream runs
+    ahead across tile and expert boundaries, and every valid row is compared
+    with the oracle.  "codes": uniform random e4m3 codes and scales, within
+    the GEMM bound for full-range codes; "layer": activations and weights
+    drawn and quantised like the layer's (N(0,1) tokens in 1x128 groups,
+    N(0, 0.02) weights in 128x128 blocks), within 1e-3 + 1e-2|ref|."""
+    announce("gemm full grid", El, hi, n_out, k_in, tile, data)
+    rng = np.random.default_rng(El * 1000 + hi + (data == "layer"))
+    cnt = rng.integers(0, hi + 1, El).astype(np.int32)
+    cnt[::9] = 0
+    cnt[1::11] = tile
+    cnt[2::13] = 2 * tile
+    offs, cnt = _segments(cnt, 128)
+    cap = int(offs[-1]) + 5
+    assert moe.moe_grouped_gemm_tile_rows(cap, El) == tile
+    mt = int(((cnt + tile - 1) // tile).sum())
+    assert mt * (n_out // 256) >= 2 * 256, "not enough tiles to exercise the persistent walk"
+    if data == "codes":
+        a = gen.random_codes(rng, (cap, k_in))
+        w = gen.random_codes(rng, (El, n_out, k_in))
+        a_s = rng.uniform(1e-3, 1, (cap, k_in // 128)).astype(np.float32)
+        w_s = rng.uniform(1e-3, 1, (El, n_out // 128, k_in // 128)).astype(np.float32)
+    else:
+        a, a_s = oracle.act_quant_identity(gen.bf16_bits(rng.standard_normal((cap, k_in), dtype=np.float32)))
+        w, w_s = gen.block_weights(rng, El, n_out, k_in)
+    out = _gpu_gemm(a, a_s, w, w_s, offs, cnt)
+    ref = oracle.grouped_gemm(a, a_s, w, w_s, offs, cnt)
+    rows = valid_rows(offs, cnt)
+    if data == "codes":
+        absterm = oracle.grouped_gemm(a & 0x7F, a_s, w & 0x7F, w_s, offs, cnt)
+        assert_gemm_close(out[rows], ref[rows], absterm[rows], "gemm full grid")
+    else:
+        assert_bf16_close(out[rows], ref[rows], "gemm full grid")
+    assert np.all(out[np.setdiff1d(np.arange(cap), rows)] == 0x7FC1)
 
 
 @pytest.mark.parametrize("El,max_tokens,n_out,k_in,tile", [
