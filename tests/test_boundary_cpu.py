@@ -110,3 +110,141 @@ def test_forward_rejects_small_workspace_and_overlap():
     assert L.moe_forward_chunked(*args, out, ws, need - 1, None, None) == 3
     assert L.moe_forward_chunked(*args, C.c_void_p(0x40000000 + 256), ws, need, None, None) == 1
     assert b"overlaps" in L.moe_last_error()
+
+
+# ---- the Python binding checks every tensor before a pointer reaches the C ABI
+import torch  # noqa: E402
+
+
+def _cpu_layer(El=4, K=256, N=128, Eg=8, emap=None):
+    z = lambda *s: torch.zeros(s, dtype=torch.uint8)
+    f = lambda *s: torch.ones(s, dtype=torch.float32)
+    return moe.MoeLayer(z(El, 2 * N, K), f(El, 2 * N // 128, K // 128), z(El, K, N), f(El, K // 128, N // 128),
+                        Eg, emap)
+
+
+def _good_call(M=10, K=256, T=2):
+    return dict(x=torch.zeros((M, K), dtype=torch.int16), topk_ids=torch.zeros((M, T), dtype=torch.int32),
+                topk_weights=torch.ones((M, T), dtype=torch.float32))
+
+
+@pytest.mark.parametrize("bad,exc,match", [
+    ("ids_int64", TypeError, "topk_ids has dtype torch.int64"),
+    ("weights_f64", TypeError, "topk_weights has dtype torch.float64"),
+    ("weights_shape", ValueError, "topk_weights has shape"),
+    ("x_noncontig", ValueError, "x must be contiguous"),
+    ("x_width", ValueError, "x has shape"),
+    ("x_float", TypeError, "x has dtype torch.float32"),
+    ("ids_rows", ValueError, "topk_ids has shape"),
+    ("out_shape", ValueError, "out has shape"),
+    ("pcc_shape", ValueError, "per_chunk_counts has shape"),
+])
+def test_layer_forward_rejects_bad_tensors(bad, exc, match):
+    layer = _cpu_layer()
+    a = _good_call()
+    kw = {}
+    if bad == "ids_int64":
+        a["topk_ids"] = a["topk_ids"].long()
+    elif bad == "weights_f64":
+        a["topk_weights"] = a["topk_weights"].double()
+    elif bad == "weights_shape":
+        a["topk_weights"] = torch.ones((10, 3), dtype=torch.float32)
+    elif bad == "x_noncontig":
+        a["x"] = torch.zeros((256, 10), dtype=torch.int16).t()
+    elif bad == "x_width":
+        a["x"] = torch.zeros((10, 128), dtype=torch.int16)
+    elif bad == "x_float":
+        a["x"] = torch.zeros((10, 256), dtype=torch.float32)
+    elif bad == "ids_rows":
+        a["topk_ids"] = torch.zeros((9, 2), dtype=torch.int32)
+    elif bad == "out_shape":
+        kw["out"] = torch.zeros((10, 128), dtype=torch.int16)
+    elif bad == "pcc_shape":
+        kw["chunk_size"] = 4
+        kw["per_chunk_counts"] = torch.zeros((2, 4), dtype=torch.int32)   # 3 chunks of 4 tokens
+    with pytest.raises(exc, match=match):
+        layer.forward(a["x"], a["topk_ids"], a["topk_weights"], **kw)
+
+
+def test_layer_forward_needs_tensors_on_the_gpu():
+    # well-formed tensors still never reach the library from host memory
+    layer = _cpu_layer()
+    a = _good_call()
+    with pytest.raises(ValueError, match="current CUDA device"):
+        layer.forward(a["x"], a["topk_ids"], a["topk_weights"])
+
+
+@pytest.mark.parametrize("bad,exc,match", [
+    ("w13_float", TypeError, "w13 has dtype"),
+    ("w13_s_shape", ValueError, "w13_s has shape"),
+    ("w2_shape", ValueError, "w2 has shape"),
+    ("w2_s_dtype", TypeError, "w2_s has dtype"),
+    ("map_int64", TypeError, "expert_map has dtype"),
+    ("map_len", ValueError, "expert_map has shape"),
+])
+def test_layer_rejects_bad_weights(bad, exc, match):
+    El, K, N, Eg = 4, 256, 128, 8
+    w13 = torch.zeros((El, 2 * N, K), dtype=torch.uint8)
+    w13_s = torch.ones((El, 2, 2), dtype=torch.float32)
+    w2 = torch.zeros((El, K, N), dtype=torch.uint8)
+    w2_s = torch.ones((El, 2, 1), dtype=torch.float32)
+    emap = None
+    if bad == "w13_float":
+        w13 = w13.float()
+    elif bad == "w13_s_shape":
+        w13_s = torch.ones((El, 2, 1), dtype=torch.float32)
+    elif bad == "w2_shape":
+        w2 = torch.zeros((El, N, K), dtype=torch.uint8)
+    elif bad == "w2_s_dtype":
+        w2_s = w2_s.half()
+    elif bad == "map_int64":
+        emap = torch.zeros(Eg, dtype=torch.int64)
+    elif bad == "map_len":
+        emap = torch.zeros(Eg + 1, dtype=torch.int32)
+    with pytest.raises(exc, match=match):
+        moe.MoeLayer(w13, w13_s, w2, w2_s, Eg, emap)
+
+
+def test_op_wrappers_check_before_calling():
+    cap, k_in, El, n_out = 300, 256, 3, 384
+    a = torch.zeros((cap, k_in), dtype=torch.uint8)
+    a_s = torch.ones((cap, 2), dtype=torch.float32)
+    w = torch.zeros((El, n_out, k_in), dtype=torch.uint8)
+    w_s = torch.ones((El, 3, 2), dtype=torch.float32)
+    offs = torch.zeros(El + 1, dtype=torch.int32)
+    cnt = torch.zeros(El, dtype=torch.int32)
+    out = torch.zeros((cap, n_out), dtype=torch.int16)
+    with pytest.raises(ValueError, match="a_s has shape"):
+        moe.moe_grouped_gemm_fp8(a, a_s[:, :1].contiguous(), w, w_s, offs, cnt, out)
+    with pytest.raises(ValueError, match="expert_offsets has shape"):
+        moe.moe_grouped_gemm_fp8(a, a_s, w, w_s, offs[:El].contiguous(), cnt, out)
+    with pytest.raises(ValueError, match="out has shape"):
+        moe.moe_grouped_gemm_fp8(a, a_s, w, w_s, offs, cnt, out[:, :128].contiguous())
+    with pytest.raises(ValueError, match="current CUDA device"):
+        moe.moe_grouped_gemm_fp8(a, a_s, w, w_s, offs, cnt, out)
+    y = torch.zeros((50, 256), dtype=torch.int16)
+    with pytest.raises(TypeError, match="inv_perm has dtype torch.int64"):
+        moe.moe_unpermute_weight_reduce(y, torch.zeros((10, 2), dtype=torch.int64),
+                                        torch.ones((10, 2)), 0, torch.zeros((10, 256), dtype=torch.int16))
+    with pytest.raises(ValueError, match="q_s has shape"):
+        moe.moe_act_quant(y, 128, moe.MOE_ACT_SILU_MUL, torch.zeros((50, 128), dtype=torch.uint8),
+                          torch.zeros((50, 2), dtype=torch.float32))
+    with pytest.raises(ValueError, match="a_perm has shape"):
+        moe.moe_quant_permute(torch.zeros((10, 256), dtype=torch.int16), torch.zeros((10, 2), dtype=torch.int32),
+                              None, 0, None, 8, 8, 128, 100, torch.zeros((99, 256), dtype=torch.uint8),
+                              torch.zeros((100, 2)), torch.zeros(8, dtype=torch.int32),
+                              torch.zeros(9, dtype=torch.int32), torch.zeros((10, 2), dtype=torch.int32),
+                              torch.zeros(100, dtype=torch.int32), torch.zeros(256, dtype=torch.uint8))
+
+
+def test_forward_workspace_slices_leave_guard_bands():
+    for p in (moe.problem(8192, 2048, 768, 8, 128, 64, chunk_size=64), moe.problem(130, 256, 128, 3, 16, 8),
+              moe.problem(1, 128, 128, 1, 4, 4)):
+        sl = moe.moe_forward_workspace_slices(p)
+        total = moe.moe_forward_workspace_size(p)
+        assert len(sl) == 8
+        ends = [o + n for o, n in sl]
+        nxt = [o for o, _ in sl[1:]] + [total]
+        for (o, n), e, q in zip(sl, ends, nxt):
+            assert o % 256 == 0 and n > 0
+            assert q - e >= 256, "no guard band after a slice"

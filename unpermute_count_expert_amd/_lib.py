@@ -36,7 +36,7 @@ class MoeProblem(C.Structure):
 
 
 EXPORTS = ["moe_status_string", "moe_last_error", "moe_max_rows", "moe_grouped_gemm_tile_rows",
-           "moe_forward_workspace_size",
+           "moe_forward_workspace_size", "moe_forward_workspace_slices",
            "moe_permute_workspace_size", "moe_count", "moe_permute", "moe_grouped_gemm_fp8",
            "moe_grouped_gemm_fp8_act_quant", "moe_act_quant", "moe_quant_permute", "moe_unpermute_weight_reduce",
            "moe_forward_chunked"]
@@ -58,6 +58,8 @@ def load() -> C.CDLL:
         L.moe_grouped_gemm_tile_rows.argtypes = [I64, I32]; L.moe_grouped_gemm_tile_rows.restype = I32
         L.moe_forward_workspace_size.argtypes = [C.POINTER(MoeProblem), C.POINTER(SZ)]
         L.moe_permute_workspace_size.argtypes = [I64, I32, I32, C.POINTER(SZ)]
+        L.moe_forward_workspace_slices.argtypes = [C.POINTER(MoeProblem), C.POINTER(SZ), C.POINTER(SZ), I32,
+                                                   C.POINTER(I32)]
         L.moe_count.argtypes = [P, I64, P, I32, I32, P, P, P]
         L.moe_permute.argtypes = [P, P, P, P, I32, I64, I32, I32, P, I32, I32, I32, I64,
                                   P, P, P, P, P, P, P, SZ, P]
@@ -94,6 +96,61 @@ def _stream(stream=None):
     return C.c_void_p(stream.cuda_stream)
 
 
+# ---- argument checks -----------------------------------------------------------
+# The C ABI sees raw pointers only, so a tensor of the wrong dtype, shape or
+# layout would be read with the wrong strides or past its end.  Every wrapper
+# below checks dtype, contiguity and shape first, then that every tensor sits
+# on the current CUDA device, and raises before anything reaches the library.
+BF16 = (torch.int16, torch.bfloat16)          # bf16 values or their raw bits
+E4M3 = (torch.uint8, torch.float8_e4m3fn)     # e4m3 codes
+I32 = (torch.int32,)
+F32 = (torch.float32,)
+
+
+def check_arg(t, name: str, dtypes, shape=None, min_rows=None, optional=False):
+    """dtype in dtypes, contiguous, and shape == `shape` (None entries match
+    any size; with min_rows the first dimension may be larger than
+    shape[0] if it is at least min_rows)."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, not {type(t).__name__}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}; expected {' or '.join(str(d) for d in dtypes)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None:
+        got = tuple(t.shape)
+        ok = len(got) == len(shape)
+        for i, (g_, w_) in enumerate(zip(got, shape)):
+            if i == 0 and min_rows is not None:
+                ok = ok and g_ >= min_rows
+            elif w_ is not None:
+                ok = ok and g_ == w_
+        if not ok:
+            want = tuple("*" if w_ is None else w_ for w_ in shape)
+            extra = f" (first dimension >= {min_rows})" if min_rows is not None else ""
+            raise ValueError(f"{name} has shape {got}; expected {want}{extra}")
+
+
+def check_device(*tensors):
+    """Every given tensor is on the current CUDA device (the library runs on
+    the current device)."""
+    for t in tensors:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"a tensor is on {t.device}; the library needs tensors on the current CUDA device")
+        if t.device.index != torch.cuda.current_device():
+            raise ValueError(f"a tensor is on {t.device}, the current device is cuda:{torch.cuda.current_device()}")
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
 def moe_max_rows(Mc: int, topk: int, El: int, align: int = 128) -> int:
     return int(load().moe_max_rows(Mc, topk, El, align))
 
@@ -112,6 +169,17 @@ def moe_forward_workspace_size(p: MoeProblem) -> int:
     return int(n.value)
 
 
+def moe_forward_workspace_slices(p: MoeProblem):
+    """[(offset, bytes)] of the slices moe_forward_chunked carves from its
+    workspace; the bytes between a slice's end and the next offset are a
+    guard band no kernel touches."""
+    offs = (C.c_size_t * 16)()
+    lens = (C.c_size_t * 16)()
+    n = C.c_int32(0)
+    _check(load().moe_forward_workspace_slices(C.byref(p), offs, lens, 16, C.byref(n)), "moe_forward_workspace_slices")
+    return [(int(offs[i]), int(lens[i])) for i in range(min(n.value, 16))]
+
+
 def moe_permute_workspace_size(Mc: int, topk: int, El: int) -> int:
     n = C.c_size_t(0)
     _check(load().moe_permute_workspace_size(Mc, topk, El, C.byref(n)), "moe_permute_workspace_size")
@@ -119,43 +187,90 @@ def moe_permute_workspace_size(Mc: int, topk: int, El: int) -> int:
 
 
 def moe_count(topk_ids, expert_map, Eg, El, counts, invalid_ids=None, stream=None):
+    check_arg(topk_ids, "topk_ids", I32)
+    check_arg(expert_map, "expert_map", I32, (Eg,), optional=True)
+    check_arg(counts, "counts", I32, (El,))
+    check_arg(invalid_ids, "invalid_ids", I32, (1,), optional=True)
+    check_device(topk_ids, expert_map, counts, invalid_ids)
     _check(load().moe_count(_ptr(topk_ids), topk_ids.numel(), _ptr(expert_map), Eg, El, _ptr(counts),
                             _ptr(invalid_ids), _stream(stream)), "moe_count")
 
 
+def _check_permute_outputs(Mc, K, topk, El, cap_rows, a_perm, a_perm_s, counts, expert_offsets, inv_perm,
+                           row_src, workspace):
+    check_arg(a_perm, "a_perm", E4M3, (None, K), min_rows=cap_rows)
+    check_arg(a_perm_s, "a_perm_s", F32, (None, K // 128), min_rows=cap_rows)
+    check_arg(counts, "counts", I32, (El,))
+    check_arg(expert_offsets, "expert_offsets", I32, (El + 1,))
+    check_arg(inv_perm, "inv_perm", I32, (Mc, topk))
+    check_arg(row_src, "row_src", I32, (None,), min_rows=cap_rows)
+    check_arg(workspace, "workspace", (torch.uint8, torch.int32))
+
+
 def moe_permute(a_q, a_s, topk_ids, topk_weights, apply_on_input, expert_map, Eg, El, align, cap_rows,
                 a_perm, a_perm_s, counts, expert_offsets, inv_perm, row_src, workspace, stream=None):
+    check_arg(a_q, "a_q", E4M3, (None, None))
     Mc, K = a_q.shape
+    check_arg(a_s, "a_s", F32, (Mc, K // 128))
+    check_arg(topk_ids, "topk_ids", I32, (Mc, None))
     topk = topk_ids.shape[1]
+    check_arg(topk_weights, "topk_weights", F32, (Mc, topk), optional=not apply_on_input)
+    check_arg(expert_map, "expert_map", I32, (Eg,), optional=True)
+    _check_permute_outputs(Mc, K, topk, El, cap_rows, a_perm, a_perm_s, counts, expert_offsets, inv_perm,
+                           row_src, workspace)
+    check_device(a_q, a_s, topk_ids, topk_weights, expert_map, a_perm, a_perm_s, counts, expert_offsets,
+                 inv_perm, row_src, workspace)
     _check(load().moe_permute(_ptr(a_q), _ptr(a_s), _ptr(topk_ids), _ptr(topk_weights), apply_on_input,
                               Mc, K, topk, _ptr(expert_map), Eg, El, align, cap_rows, _ptr(a_perm),
                               _ptr(a_perm_s), _ptr(counts), _ptr(expert_offsets), _ptr(inv_perm),
-                              _ptr(row_src), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                              _stream(stream)), "moe_permute")
+                              _ptr(row_src), _ptr(workspace), _nbytes(workspace), _stream(stream)), "moe_permute")
 
 
 def moe_quant_permute(x, topk_ids, topk_weights, apply_on_input, expert_map, Eg, El, align, cap_rows,
                       a_perm, a_perm_s, counts, expert_offsets, inv_perm, row_src, workspace, stream=None):
+    check_arg(x, "x", BF16, (None, None))
     Mc, K = x.shape
+    check_arg(topk_ids, "topk_ids", I32, (Mc, None))
     topk = topk_ids.shape[1]
+    check_arg(topk_weights, "topk_weights", F32, (Mc, topk), optional=not apply_on_input)
+    check_arg(expert_map, "expert_map", I32, (Eg,), optional=True)
+    _check_permute_outputs(Mc, K, topk, El, cap_rows, a_perm, a_perm_s, counts, expert_offsets, inv_perm,
+                           row_src, workspace)
+    check_device(x, topk_ids, topk_weights, expert_map, a_perm, a_perm_s, counts, expert_offsets, inv_perm,
+                 row_src, workspace)
     _check(load().moe_quant_permute(_ptr(x), _ptr(topk_ids), _ptr(topk_weights), apply_on_input,
                                     Mc, K, topk, _ptr(expert_map), Eg, El, align, cap_rows, _ptr(a_perm),
                                     _ptr(a_perm_s), _ptr(counts), _ptr(expert_offsets), _ptr(inv_perm),
-                                    _ptr(row_src), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                    _stream(stream)), "moe_quant_permute")
+                                    _ptr(row_src), _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "moe_quant_permute")
+
+
+def _check_gemm_operands(a, a_s, w, w_s, expert_offsets, counts):
+    check_arg(a, "a", E4M3, (None, None))
+    cap_rows, k_in = a.shape
+    check_arg(a_s, "a_s", F32, (cap_rows, k_in // 128))
+    check_arg(w, "w", E4M3, (None, None, k_in))
+    El, n_out, _ = w.shape
+    check_arg(w_s, "w_s", F32, (El, n_out // 128, k_in // 128))
+    check_arg(expert_offsets, "expert_offsets", I32, (El + 1,))
+    check_arg(counts, "counts", I32, (El,))
+    return cap_rows, k_in, El, n_out
 
 
 def moe_grouped_gemm_fp8(a, a_s, w, w_s, expert_offsets, counts, out, stream=None):
-    cap_rows, k_in = a.shape
-    El, n_out, _ = w.shape
+    cap_rows, k_in, El, n_out = _check_gemm_operands(a, a_s, w, w_s, expert_offsets, counts)
+    check_arg(out, "out", BF16, (cap_rows, n_out))
+    check_device(a, a_s, w, w_s, expert_offsets, counts, out)
     _check(load().moe_grouped_gemm_fp8(_ptr(a), _ptr(a_s), _ptr(w), _ptr(w_s), _ptr(expert_offsets),
                                        _ptr(counts), El, cap_rows, n_out, k_in, _ptr(out),
                                        _stream(stream)), "moe_grouped_gemm_fp8")
 
 
 def moe_grouped_gemm_fp8_act_quant(a, a_s, w13, w13_s, expert_offsets, counts, q, q_s, stream=None):
-    cap_rows, k_in = a.shape
-    El, two_n, _ = w13.shape
+    cap_rows, k_in, El, two_n = _check_gemm_operands(a, a_s, w13, w13_s, expert_offsets, counts)
+    check_arg(q, "q", E4M3, (cap_rows, two_n // 2))
+    check_arg(q_s, "q_s", F32, (cap_rows, two_n // 256))
+    check_device(a, a_s, w13, w13_s, expert_offsets, counts, q, q_s)
     _check(load().moe_grouped_gemm_fp8_act_quant(_ptr(a), _ptr(a_s), _ptr(w13), _ptr(w13_s),
                                                  _ptr(expert_offsets), _ptr(counts), El, cap_rows, two_n // 2,
                                                  k_in, _ptr(q), _ptr(q_s), _stream(stream)),
@@ -163,23 +278,56 @@ def moe_grouped_gemm_fp8_act_quant(a, a_s, w13, w13_s, expert_offsets, counts, q
 
 
 def moe_act_quant(inp, n, mode, q, q_s, expert_offsets=None, counts=None, El=0, stream=None):
+    width = n if mode == MOE_ACT_IDENTITY else 2 * n
+    check_arg(inp, "in", BF16, (None, width))
     rows = inp.shape[0]
+    check_arg(q, "q", E4M3, (rows, n))
+    check_arg(q_s, "q_s", F32, (rows, n // 128))
+    check_arg(expert_offsets, "expert_offsets", I32, (El + 1,), optional=True)
+    check_arg(counts, "counts", I32, (El,), optional=True)
+    check_device(inp, q, q_s, expert_offsets, counts)
     _check(load().moe_act_quant(_ptr(inp), rows, n, mode, _ptr(expert_offsets), _ptr(counts), El,
                                 _ptr(q), _ptr(q_s), _stream(stream)), "moe_act_quant")
 
 
 def moe_unpermute_weight_reduce(y, inv_perm, topk_weights, apply_on_input, out, stream=None):
+    check_arg(y, "y", BF16, (None, None))
     y_rows, K = y.shape
+    check_arg(inv_perm, "inv_perm", I32, (None, None))
     Mc, topk = inv_perm.shape
+    check_arg(topk_weights, "topk_weights", F32, (Mc, topk), optional=bool(apply_on_input))
+    check_arg(out, "out", BF16, (Mc, K))
+    check_device(y, inv_perm, topk_weights, out)
     _check(load().moe_unpermute_weight_reduce(_ptr(y), y_rows, _ptr(inv_perm), _ptr(topk_weights), Mc, K,
                                               topk, apply_on_input, _ptr(out), _stream(stream)),
            "moe_unpermute_weight_reduce")
 
 
+def check_forward_args(p: MoeProblem, x, topk_ids, topk_weights, expert_map, w13, w13_s, w2, w2_s, out,
+                       per_chunk_counts=None):
+    """dtype, layout and shape checks of moe_forward_chunked's tensors
+    against the problem p (no device check)."""
+    M, K, N, T, El, Eg = p.M, p.K, p.N, p.topk, p.num_local_experts, p.num_global_experts
+    check_arg(x, "x", BF16, (M, K))
+    check_arg(topk_ids, "topk_ids", I32, (M, T))
+    check_arg(topk_weights, "topk_weights", F32, (M, T))
+    check_arg(expert_map, "expert_map", I32, (Eg,), optional=True)
+    check_arg(w13, "w13", E4M3, (El, 2 * N, K))
+    check_arg(w13_s, "w13_s", F32, (El, 2 * N // 128, K // 128))
+    check_arg(w2, "w2", E4M3, (El, K, N))
+    check_arg(w2_s, "w2_s", F32, (El, K // 128, N // 128))
+    check_arg(out, "out", BF16, (M, K))
+    cs = M if (p.chunk_size <= 0 or p.chunk_size >= M) else p.chunk_size
+    nch = -(-M // cs) if M > 0 else 0
+    check_arg(per_chunk_counts, "per_chunk_counts", I32, (nch, El), optional=True)
+
+
 def moe_forward_chunked(p: MoeProblem, x, topk_ids, topk_weights, expert_map, w13, w13_s, w2, w2_s, out,
                         workspace, per_chunk_counts=None, stream=None):
+    check_forward_args(p, x, topk_ids, topk_weights, expert_map, w13, w13_s, w2, w2_s, out, per_chunk_counts)
+    check_arg(workspace, "workspace", (torch.uint8,))
+    check_device(x, topk_ids, topk_weights, expert_map, w13, w13_s, w2, w2_s, out, workspace, per_chunk_counts)
     _check(load().moe_forward_chunked(C.byref(p), _ptr(x), _ptr(topk_ids), _ptr(topk_weights),
                                       _ptr(expert_map), _ptr(w13), _ptr(w13_s), _ptr(w2), _ptr(w2_s),
-                                      _ptr(out), _ptr(workspace),
-                                      workspace.numel() * workspace.element_size(),
+                                      _ptr(out), _ptr(workspace), _nbytes(workspace),
                                       _ptr(per_chunk_counts), _stream(stream)), "moe_forward_chunked")
