@@ -115,14 +115,19 @@ __device__ __forceinline__ v8i frag2(const uint8_t* lo, const uint8_t* hi, int i
     return v8i{l.x, l.y, l.z, l.w, h.x, h.y, h.z, h.w};
 }
 
-// LDS DMA: lane l's 16 (4) bytes from sbase + voff land at LDS byte m0 + 16*l (4*l)
-__device__ __forceinline__ void dma16(uint32_t m0, uint32_t voff, const void* sbase) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(sbase)
-                 : "memory", "m0");
+// LDS DMA (global_load_lds_dwordx4 / _dword): lane l's 16 (4) bytes from
+// sbase + voff land at LDS byte lds + 16*l (4*l).  The compiler owns M0,
+// which carries the wave-uniform LDS base; sbase is wave-uniform and voff a
+// 32-bit per-lane offset, so the load takes the scalar-base form.  The
+// compiler does not wait for these writes before later LDS reads: the K loop
+// does that itself (wait_loads_barrier_c).
+typedef __attribute__((address_space(3))) void* lds_ptr;
+__device__ __forceinline__ lds_ptr lds_at(uint32_t lds) { return (lds_ptr)(uintptr_t)lds; }
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, const void* sbase) {
+    __builtin_amdgcn_global_load_lds(static_cast<const uint8_t*>(sbase) + voff, lds_at(lds), 16, 0, 0);
 }
-__device__ __forceinline__ void dma4(uint32_t m0, uint32_t voff, const void* sbase) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(m0), "v"(voff), "s"(sbase)
-                 : "memory", "m0");
+__device__ __forceinline__ void dma4(uint32_t lds, uint32_t voff, const void* sbase) {
+    __builtin_amdgcn_global_load_lds(static_cast<const uint8_t*>(sbase) + voff, lds_at(lds), 4, 0, 0);
 }
 
 // Wait until at most N of this wave's vector-memory loads issued after the
