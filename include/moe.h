@@ -86,6 +86,17 @@ int64_t moe_max_rows(int64_t Mc, int32_t topk, int32_t El, int32_t align);
  * largest chunk and reused by every chunk). */
 int moe_forward_workspace_size(const moe_problem* p, size_t* bytes);
 
+/* The slices moe_forward_chunked carves from its workspace for problem p:
+ * *num_slices receives their number (8: permuted rows then act codes,
+ * their scales, h then y, counts, offsets, inv_perm, row_src, the permute's
+ * per-block histogram); the first min(max_slices, *num_slices) byte offsets
+ * and lengths are written to offsets[] and bytes[].  Between the end of a
+ * slice and the next slice's offset (and up to the workspace size after the
+ * last) lies a guard band that no kernel reads or writes: a caller can fill
+ * the workspace with a pattern and check the bands after a call. */
+int moe_forward_workspace_slices(const moe_problem* p, size_t* offsets, size_t* bytes, int32_t max_slices,
+                                 int32_t* num_slices);
+
 /* Workspace bytes moe_permute needs for Mc tokens. */
 int moe_permute_workspace_size(int64_t Mc, int32_t topk, int32_t El, size_t* bytes);
 

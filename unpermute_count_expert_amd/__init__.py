@@ -6,7 +6,7 @@ The compute lives in libmoe_hip.so (C ABI in include/moe.h); this package is
 its ctypes binding plus a small device-resident layer wrapper.
 """
 from ._lib import (MOE_ACT_IDENTITY, MOE_ACT_SILU_MUL, MoeError, MoeProblem, load,  # noqa: F401
-                   moe_act_quant, moe_count, moe_forward_chunked, moe_forward_workspace_size,
+                   moe_act_quant, moe_count, moe_forward_chunked, moe_forward_workspace_size, moe_forward_workspace_slices,
                    moe_grouped_gemm_fp8, moe_grouped_gemm_tile_rows, moe_max_rows, moe_permute, moe_permute_workspace_size,
                    moe_quant_permute,
                    moe_unpermute_weight_reduce, problem)

@@ -85,14 +85,22 @@ size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
 // The forward workspace, carved once for the largest chunk and reused by all.
 //   bufA   a_perm [cap,K] then act_q [cap,N]          (e4m3)
 //   bufAs  a_perm_s then act_s                         (fp32 scales)
-//   bufB   a_q, a_s (before the permute), then h [cap,2N], then y [cap,K] (bf16)
+//   bufB   h [cap,2N], then y [cap,K]                  (bf16)
 //   small  counts, offsets, inv_perm, row_src, per-block histogram
-// Each buffer is dead before it is reused: GEMM1 reads bufA and writes bufB,
-// act-quant reads bufB and writes bufA, GEMM2 reads bufA and writes bufB,
-// the unpermute reads bufB.  The output never aliases the workspace.
+// The input quantisation is fused into the permute's scatter, so no a_q /
+// a_s buffer exists.  Each buffer is dead before it is reused: GEMM w13
+// reads bufA and writes bufB, the SiLU-mul requant reads bufB and writes
+// bufA, GEMM w2 reads bufA and writes bufB, the unpermute reads bufB.  The
+// output never aliases the workspace.  Every slice is followed by a guard
+// band of kGuard bytes that no kernel touches, so a write past a slice's end
+// is visible to a caller that fills the workspace with a pattern first.
+constexpr size_t kGuard = 256;
+constexpr int kSlices = 8;
+
 struct Plan {
     int64_t cs, cap, nblk;
     size_t bufA, bufAs, bufB, counts, offsets, inv, rsrc, hist, total;
+    size_t off[kSlices], len[kSlices];   // the slices above, in this order
 };
 
 Plan make_plan(const moe_problem& p) {
@@ -104,15 +112,30 @@ Plan make_plan(const moe_problem& p) {
     const int64_t K = p.K, N = p.N, El = p.num_local_experts;
     const int64_t wA = K > N ? K : N;
     const int64_t wB = (2 * N > K ? 2 * N : K) * 2;
+    const size_t len[kSlices] = {
+        (size_t)pl.cap * wA,                        // bufA
+        (size_t)pl.cap * (wA / moe::kGroup) * 4,    // bufAs
+        (size_t)pl.cap * wB,                        // bufB
+        (size_t)El * 4,                             // counts
+        (size_t)(El + 1) * 4,                       // offsets
+        (size_t)pl.cs * p.topk * 4,                 // inv_perm
+        (size_t)pl.cap * 4,                         // row_src
+        (size_t)pl.nblk * El * 4,                   // histogram
+    };
     size_t off = 0;
-    pl.bufA = off;  off += up256((size_t)pl.cap * wA);
-    pl.bufAs = off; off += up256((size_t)pl.cap * (wA / moe::kGroup) * 4);
-    pl.bufB = off;  off += up256((size_t)pl.cap * wB);
-    pl.counts = off;  off += up256((size_t)El * 4);
-    pl.offsets = off; off += up256((size_t)(El + 1) * 4);
-    pl.inv = off;     off += up256((size_t)pl.cs * p.topk * 4);
-    pl.rsrc = off;    off += up256((size_t)pl.cap * 4);
-    pl.hist = off;    off += up256((size_t)pl.nblk * El * 4);
+    for (int i = 0; i < kSlices; ++i) {
+        pl.off[i] = off;
+        pl.len[i] = len[i];
+        off += up256(len[i]) + kGuard;
+    }
+    pl.bufA = pl.off[0];
+    pl.bufAs = pl.off[1];
+    pl.bufB = pl.off[2];
+    pl.counts = pl.off[3];
+    pl.offsets = pl.off[4];
+    pl.inv = pl.off[5];
+    pl.rsrc = pl.off[6];
+    pl.hist = pl.off[7];
     pl.total = off;
     return pl;
 }
@@ -169,6 +192,22 @@ int moe_forward_workspace_size(const moe_problem* p, size_t* bytes) {
     if (st) return st;
     REQUIRE(bytes != nullptr, MOE_ERR_INVALID_ARG, "bytes is NULL");
     *bytes = make_plan(*p).total;
+    return MOE_OK;
+}
+
+int moe_forward_workspace_slices(const moe_problem* p, size_t* offsets, size_t* bytes, int32_t max_slices,
+                                 int32_t* num_slices) {
+    int st = check_problem(p);
+    if (st) return st;
+    REQUIRE(num_slices != nullptr, MOE_ERR_INVALID_ARG, "num_slices is NULL");
+    REQUIRE(max_slices >= 0 && (max_slices == 0 || (offsets != nullptr && bytes != nullptr)),
+            MOE_ERR_INVALID_ARG, "offsets / bytes are NULL");
+    const Plan pl = make_plan(*p);
+    *num_slices = kSlices;
+    for (int i = 0; i < kSlices && i < max_slices; ++i) {
+        offsets[i] = pl.off[i];
+        bytes[i] = pl.len[i];
+    }
     return MOE_OK;
 }
 
