@@ -230,6 +230,27 @@ int moe_forward_chunked(const moe_problem* p, const uint16_t* x, const int32_t* 
                         void* workspace, size_t workspace_bytes, int32_t* per_chunk_counts,
                         void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation as moe_forward_chunked, bit for bit, with the workspace taken
+ * from a fixed array of MOE_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds on each GPU it runs on (allocated with the library's code object on
+ * that device and kept until the process ends).  Nothing is allocated or
+ * freed by the call.  The caller still passes every input and the output.
+ * Problems whose workspace (moe_forward_workspace_size) exceeds the array
+ * return MOE_ERR_WORKSPACE_TOO_SMALL before anything is enqueued: at the
+ * K=2048, N=768, topk 8, align 128 shape that is chunks up to ~3300 tokens
+ * with 128 local experts.  Every call on a GPU uses that GPU's one array,
+ * which keeps the last call's contents (nothing in it needs to start at
+ * zero): calls that overlap in time on one GPU (other streams, other host
+ * threads) race, and the caller must order them. */
+#define MOE_NOALLOC_SCRATCH_BYTES (256u << 20)
+size_t moe_noalloc_scratch_bytes(void);
+int moe_forward_chunked_noalloc(const moe_problem* p, const uint16_t* x, const int32_t* topk_ids,
+                                const float* topk_weights, const int32_t* expert_map, const uint8_t* w13,
+                                const float* w13_s, const uint8_t* w2, const float* w2_s, uint16_t* out,
+                                int32_t* per_chunk_counts, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

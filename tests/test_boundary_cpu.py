@@ -248,3 +248,19 @@ def test_forward_workspace_slices_leave_guard_bands():
         for (o, n), e, q in zip(sl, ends, nxt):
             assert o % 256 == 0 and n > 0
             assert q - e >= 256, "no guard band after a slice"
+
+
+def test_noalloc_forward_rejects_a_problem_beyond_the_scratch():
+    # the size check comes before any device call: these pointers are never used
+    L = moe.load()
+    assert moe._lib.moe_noalloc_scratch_bytes() == 256 << 20
+    big = moe.problem(65536, 2048, 768, 8, 128, 128)
+    assert moe.moe_forward_workspace_size(big) > moe._lib.moe_noalloc_scratch_bytes()
+    fake = C.c_void_p(0x100000)
+    out = C.c_void_p(0x4000000000)
+    args = [fake, fake, fake, None, fake, fake, fake, fake, out, None, None]
+    assert L.moe_forward_chunked_noalloc(C.byref(big), *args) == 3
+    assert b"scratch" in L.moe_last_error()
+    # the same problem in chunks small enough for the array passes the size check
+    small = moe.problem(65536, 2048, 768, 8, 128, 128, chunk_size=1024)
+    assert moe.moe_forward_workspace_size(small) <= moe._lib.moe_noalloc_scratch_bytes()

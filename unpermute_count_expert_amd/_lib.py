@@ -39,7 +39,7 @@ EXPORTS = ["moe_status_string", "moe_last_error", "moe_max_rows", "moe_grouped_g
            "moe_forward_workspace_size", "moe_forward_workspace_slices",
            "moe_permute_workspace_size", "moe_count", "moe_permute", "moe_grouped_gemm_fp8",
            "moe_grouped_gemm_fp8_act_quant", "moe_act_quant", "moe_quant_permute", "moe_unpermute_weight_reduce",
-           "moe_forward_chunked"]
+           "moe_forward_chunked", "moe_forward_chunked_noalloc", "moe_noalloc_scratch_bytes"]
 
 _lib = None
 
@@ -71,8 +71,11 @@ def load() -> C.CDLL:
         L.moe_unpermute_weight_reduce.argtypes = [P, I64, P, P, I64, I32, I32, I32, P, P]
         L.moe_forward_chunked.argtypes = [C.POINTER(MoeProblem), P, P, P, P, P, P, P, P, P, P, SZ,
                                           P, P]
+        L.moe_forward_chunked_noalloc.argtypes = [C.POINTER(MoeProblem), P, P, P, P, P, P, P, P, P, P, P]
+        L.moe_noalloc_scratch_bytes.argtypes = []; L.moe_noalloc_scratch_bytes.restype = SZ
         for name in EXPORTS:
-            if name not in ("moe_status_string", "moe_last_error", "moe_max_rows", "moe_grouped_gemm_tile_rows"):
+            if name not in ("moe_status_string", "moe_last_error", "moe_max_rows", "moe_grouped_gemm_tile_rows",
+                            "moe_noalloc_scratch_bytes"):
                 getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -331,3 +334,19 @@ def moe_forward_chunked(p: MoeProblem, x, topk_ids, topk_weights, expert_map, w1
                                       _ptr(expert_map), _ptr(w13), _ptr(w13_s), _ptr(w2), _ptr(w2_s),
                                       _ptr(out), _ptr(workspace), _nbytes(workspace),
                                       _ptr(per_chunk_counts), _stream(stream)), "moe_forward_chunked")
+
+
+def moe_noalloc_scratch_bytes() -> int:
+    return int(load().moe_noalloc_scratch_bytes())
+
+
+def moe_forward_chunked_noalloc(p: MoeProblem, x, topk_ids, topk_weights, expert_map, w13, w13_s, w2, w2_s, out,
+                                per_chunk_counts=None, stream=None):
+    """moe_forward_chunked with the workspace taken from the library's fixed
+    per-GPU scratch array: nothing is allocated (see include/moe.h)."""
+    check_forward_args(p, x, topk_ids, topk_weights, expert_map, w13, w13_s, w2, w2_s, out, per_chunk_counts)
+    check_device(x, topk_ids, topk_weights, expert_map, w13, w13_s, w2, w2_s, out, per_chunk_counts)
+    _check(load().moe_forward_chunked_noalloc(C.byref(p), _ptr(x), _ptr(topk_ids), _ptr(topk_weights),
+                                              _ptr(expert_map), _ptr(w13), _ptr(w13_s), _ptr(w2), _ptr(w2_s),
+                                              _ptr(out), _ptr(per_chunk_counts), _stream(stream)),
+           "moe_forward_chunked_noalloc")

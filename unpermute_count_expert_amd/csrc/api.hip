@@ -425,41 +425,16 @@ int moe_unpermute_weight_reduce(const uint16_t* y, int64_t y_rows, const int32_t
     return MOE_OK;
 }
 
-int moe_forward_chunked(const moe_problem* p, const uint16_t* x, const int32_t* topk_ids,
-                        const float* topk_weights, const int32_t* expert_map, const uint8_t* w13,
-                        const float* w13_s, const uint8_t* w2, const float* w2_s, uint16_t* out,
-                        void* workspace, size_t workspace_bytes, int32_t* per_chunk_counts,
-                        void* stream) {
-    int st = check_problem(p);
-    if (st) return st;
-    const moe_problem& P = *p;
-    REQUIRE(expert_map != nullptr || P.num_local_experts <= P.num_global_experts, MOE_ERR_SHAPE,
-            "El > Eg without an expert map");
-    if (P.M == 0) return MOE_OK;
-    REQUIRE_PTR(x);
-    REQUIRE_PTR(topk_ids);
-    REQUIRE_PTR(topk_weights);
-    REQUIRE_PTR(w13);
-    REQUIRE_PTR(w13_s);
-    REQUIRE_PTR(w2);
-    REQUIRE_PTR(w2_s);
-    REQUIRE_PTR(out);
-    REQUIRE_PTR(workspace);
-    REQUIRE(expert_map == nullptr || aligned16(expert_map), MOE_ERR_INVALID_ARG, "expert_map alignment");
-    REQUIRE(per_chunk_counts == nullptr || aligned16(per_chunk_counts), MOE_ERR_INVALID_ARG,
-            "per_chunk_counts alignment");
-    const Plan pl = make_plan(P);
-    REQUIRE(workspace_bytes >= pl.total, MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes",
-            workspace_bytes, pl.total);
-    const size_t out_bytes = (size_t)P.M * P.K * 2;
-    REQUIRE(!overlaps(out, out_bytes, workspace, pl.total), MOE_ERR_INVALID_ARG, "out overlaps the workspace");
-    REQUIRE(!overlaps(out, out_bytes, x, out_bytes), MOE_ERR_INVALID_ARG, "out overlaps x");
-    int cus = 0;
-    st = check_device(&cus);
-    if (st) return st;
+}  // extern "C"
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
+namespace {
+
+// The chunk loop of moe_forward_chunked over an already validated problem
+// and a workspace of at least make_plan(*p).total bytes.
+int forward_impl(const moe_problem& P, const Plan& pl, const uint16_t* x, const int32_t* topk_ids,
+                 const float* topk_weights, const int32_t* expert_map, const uint8_t* w13, const float* w13_s,
+                 const uint8_t* w2, const float* w2_s, uint16_t* out, uint8_t* ws, int32_t* per_chunk_counts,
+                 int cus, hipStream_t s) {
     uint8_t* bufA = ws + pl.bufA;
     float* bufAs = reinterpret_cast<float*>(ws + pl.bufAs);
     uint16_t* hy = reinterpret_cast<uint16_t*>(ws + pl.bufB);
@@ -491,6 +466,111 @@ int moe_forward_chunked(const moe_problem* p, const uint16_t* x, const int32_t* 
         HIP_OK(moe::launch_unpermute(hy, pl.cap, inv, w_c, Mc, (int)K, (int)T, on_in, out + t0 * K, s));
     }
     return MOE_OK;
+}
+
+// Checks of moe_forward_chunked's arguments other than the workspace.
+int check_forward(const moe_problem* p, const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
+                  const int32_t* expert_map, const uint8_t* w13, const float* w13_s, const uint8_t* w2,
+                  const float* w2_s, uint16_t* out, int32_t* per_chunk_counts) {
+    int st = check_problem(p);
+    if (st) return st;
+    const moe_problem& P = *p;
+    REQUIRE(expert_map != nullptr || P.num_local_experts <= P.num_global_experts, MOE_ERR_SHAPE,
+            "El > Eg without an expert map");
+    if (P.M == 0) return MOE_OK;
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(topk_ids);
+    REQUIRE_PTR(topk_weights);
+    REQUIRE_PTR(w13);
+    REQUIRE_PTR(w13_s);
+    REQUIRE_PTR(w2);
+    REQUIRE_PTR(w2_s);
+    REQUIRE_PTR(out);
+    REQUIRE(expert_map == nullptr || aligned16(expert_map), MOE_ERR_INVALID_ARG, "expert_map alignment");
+    REQUIRE(per_chunk_counts == nullptr || aligned16(per_chunk_counts), MOE_ERR_INVALID_ARG,
+            "per_chunk_counts alignment");
+    const size_t out_bytes = (size_t)P.M * P.K * 2;
+    REQUIRE(!overlaps(out, out_bytes, x, out_bytes), MOE_ERR_INVALID_ARG, "out overlaps x");
+    return MOE_OK;
+}
+
+// ---- the forward without allocation --------------------------------------
+// The workspace of moe_forward_chunked_noalloc: one fixed device array per
+// GPU, allocated with the code object when the library is loaded on a device
+// and held until the process ends.  Host code never uses its name as an
+// address (that is a host-side stand-in): each device's address is taken
+// once with hipGetSymbolAddress and kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = size_t(MOE_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::atomic<uint8_t*> g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (looked up on the first call on
+// each device, with that device current).
+int scratch_for_current_device(uint8_t** ptr) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice failed");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED_DEVICE, "device %d", dev);
+    uint8_t* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        void* q = nullptr;
+        HIP_OK(hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)));
+        REQUIRE(q != nullptr && aligned16(q), MOE_ERR_HIP, "hipGetSymbolAddress gave %p", q);
+        p = static_cast<uint8_t*>(q);
+        g_scratch_ptr[dev].store(p, std::memory_order_release);   // the same value if two threads race here
+    }
+    *ptr = p;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward_chunked(const moe_problem* p, const uint16_t* x, const int32_t* topk_ids,
+                        const float* topk_weights, const int32_t* expert_map, const uint8_t* w13,
+                        const float* w13_s, const uint8_t* w2, const float* w2_s, uint16_t* out,
+                        void* workspace, size_t workspace_bytes, int32_t* per_chunk_counts,
+                        void* stream) {
+    int st = check_forward(p, x, topk_ids, topk_weights, expert_map, w13, w13_s, w2, w2_s, out, per_chunk_counts);
+    if (st) return st;
+    if (p->M == 0) return MOE_OK;
+    REQUIRE_PTR(workspace);
+    const Plan pl = make_plan(*p);
+    REQUIRE(workspace_bytes >= pl.total, MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes",
+            workspace_bytes, pl.total);
+    REQUIRE(!overlaps(out, (size_t)p->M * p->K * 2, workspace, pl.total), MOE_ERR_INVALID_ARG,
+            "out overlaps the workspace");
+    int cus = 0;
+    st = check_device(&cus);
+    if (st) return st;
+    return forward_impl(*p, pl, x, topk_ids, topk_weights, expert_map, w13, w13_s, w2, w2_s, out,
+                        static_cast<uint8_t*>(workspace), per_chunk_counts, cus, static_cast<hipStream_t>(stream));
+}
+
+size_t moe_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int moe_forward_chunked_noalloc(const moe_problem* p, const uint16_t* x, const int32_t* topk_ids,
+                                const float* topk_weights, const int32_t* expert_map, const uint8_t* w13,
+                                const float* w13_s, const uint8_t* w2, const float* w2_s, uint16_t* out,
+                                int32_t* per_chunk_counts, void* stream) {
+    int st = check_forward(p, x, topk_ids, topk_weights, expert_map, w13, w13_s, w2, w2_s, out, per_chunk_counts);
+    if (st) return st;
+    if (p->M == 0) return MOE_OK;
+    const Plan pl = make_plan(*p);
+    REQUIRE(pl.total <= kScratchBytes, MOE_ERR_WORKSPACE_TOO_SMALL,
+            "the problem needs %zu workspace bytes, more than the %zu of the fixed scratch array: use a smaller "
+            "chunk_size or moe_forward_chunked with a workspace", pl.total, kScratchBytes);
+    int cus = 0;
+    st = check_device(&cus);
+    if (st) return st;
+    uint8_t* ws = nullptr;
+    st = scratch_for_current_device(&ws);
+    if (st) return st;
+    REQUIRE(!overlaps(out, (size_t)p->M * p->K * 2, ws, kScratchBytes), MOE_ERR_INVALID_ARG,
+            "out overlaps the scratch array");
+    return forward_impl(*p, pl, x, topk_ids, topk_weights, expert_map, w13, w13_s, w2, w2_s, out, ws,
+                        per_chunk_counts, cus, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"
