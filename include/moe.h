@@ -230,6 +230,39 @@ int moe_forward_chunked(const moe_problem* p, const uint16_t* x, const int32_t* 
                         void* workspace, size_t workspace_bytes, int32_t* per_chunk_counts,
                         void* stream);
 
+/* The experts on the batched, masked layout (the batched DeepGEMM experts
+ * variant named in [P20903] bot Highlights, for low-latency dispatch):
+ * tokens already routed to slot e of a_q [El, max_tokens, K] e4m3 with
+ * scales a_s [El, max_tokens, K/128] f32, the first counts[e] rows of slot e
+ * valid (counts clamped to [0, max_tokens]).  For every valid row i of slot e
+ *   act = SiLU-mul requant of bf16(GEMM(a_q[e,i], w13[e]))   (as
+ *         moe_grouped_gemm_fp8_act_quant),
+ *   out[e, i, :] = bf16(GEMM(act, w2[e]))                   (as
+ *         moe_grouped_gemm_fp8),
+ * the same bits as those two calls with expert_offsets[e] = e * max_tokens.
+ * Rows past a slot's count are not written.  out [El, max_tokens, K] bf16;
+ * the weighted reduce over a token's experts belongs to the combine that
+ * follows and is not done here.  w13 [El,2N,K], w13_s [El,2N/128,K/128],
+ * w2 [El,K,N], w2_s [El,K/128,N/128]; workspace >=
+ * moe_batched_workspace_size(El, max_tokens, N) bytes. */
+int moe_batched_workspace_size(int32_t El, int64_t max_tokens, int32_t N, size_t* bytes);
+int moe_experts_batched_masked(const uint8_t* a_q, const float* a_s, const int32_t* counts, int32_t El,
+                               int64_t max_tokens, int32_t K, int32_t N, const uint8_t* w13, const float* w13_s,
+                               const uint8_t* w2, const float* w2_s, uint16_t* out, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Plain HBM streams, timed beside the memory-bound kernels as their measured
+ * ceilings (not part of the layer): MOE_STREAM_READ reads `bytes` from src
+ * (dst: >= 16 bytes of device memory, receives nothing unless the data hash
+ * to one fixed value); MOE_STREAM_WRITE_NT / MOE_STREAM_WRITE write `bytes`
+ * to dst with non-temporal / ordinary 16-byte stores; MOE_STREAM_COPY copies
+ * `bytes` from src to dst (non-overlapping).  bytes: a multiple of 16. */
+#define MOE_STREAM_READ 0
+#define MOE_STREAM_WRITE_NT 1
+#define MOE_STREAM_COPY 2
+#define MOE_STREAM_WRITE 3
+int moe_hbm_stream(int32_t mode, const void* src, void* dst, size_t bytes, void* stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * computation as moe_forward_chunked, bit for bit, with the workspace taken

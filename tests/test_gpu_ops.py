@@ -15,7 +15,7 @@ import torch
 import oracle
 import unpermute_count_expert_amd as moe
 from unpermute_count_expert_amd import generators as gen
-from tests.gpu_helpers import (announce, assert_bf16_close, assert_gemm_close, dev, empty, filled, host,
+from tests.gpu_helpers import (DEV, announce, assert_bf16_close, assert_gemm_close, dev, empty, filled, host,
                                valid_rows)
 
 pytestmark = pytest.mark.gpu
@@ -581,3 +581,75 @@ def test_unpermute_parity(M, K, T, on_input):
     got = host(out, bf16=True)
     ref = oracle.unpermute(y, inv_ref, w, on_input)
     np.testing.assert_array_equal(got, ref)   # same fmaf order on both sides
+
+
+# ------------------------------------------------- batched, masked experts
+@pytest.mark.parametrize("El,max_tokens,K,N", [
+    (16, 16, 2048, 768),     # decode-sized slots at the layer's shape
+    (8, 300, 512, 256),      # slots longer than a 256-row tile
+    (64, 1, 256, 128),       # one token per slot
+])
+def test_batched_masked_experts_parity(El, max_tokens, K, N):
+    """moe_experts_batched_masked (the experts on the [El, max_tokens, K]
+    layout of low-latency dispatch) computes the same bits as the op chain
+    on the same slots: GEMM w13, the masked SiLU-mul requant, GEMM w2 with
+    expert_offsets[e] = e * max_tokens and the counts cut at the slot.  The
+    chain's steps against the oracle: h and y within 1e-3 + 1e-2|ref|, the act
+    codes bit-exact given the GPU's h.  Slots: empty, full, over-full (cut)."""
+    announce("batched masked experts", El, max_tokens, K, N)
+    rng = np.random.default_rng(El * 7 + max_tokens)
+    cnt = rng.integers(0, max_tokens + 1, El).astype(np.int32)
+    cnt[0], cnt[-1] = 0, max_tokens
+    cnt[1] = max_tokens + 9                      # cut at the slot
+    cut = np.minimum(cnt, max_tokens).astype(np.int32)
+    rows = El * max_tokens
+    a, a_s = oracle.act_quant_identity(gen.bf16_bits(rng.standard_normal((rows, K), dtype=np.float32)))
+    w13, w13_s = gen.block_weights(rng, El, 2 * N, K)
+    w2, w2_s = gen.block_weights(rng, El, K, N)
+    offs = (np.arange(El + 1) * max_tokens).astype(np.int32)
+    d = dict(a=dev(a), a_s=dev(a_s), w13=dev(w13), w13_s=dev(w13_s), w2=dev(w2), w2_s=dev(w2_s))
+    out = filled((El, max_tokens, K), "bf16", 0x7FC1)
+    ws = empty((moe._lib.moe_batched_workspace_size(El, max_tokens, N),), torch.uint8)
+    moe._lib.moe_experts_batched_masked(d["a"].view(El, max_tokens, K), d["a_s"].view(El, max_tokens, K // 128),
+                                        dev(cnt), d["w13"], d["w13_s"], d["w2"], d["w2_s"], out, ws)
+    got = host(out, bf16=True).reshape(rows, K)
+    # the op chain on the cut slots
+    h = filled((rows, 2 * N), "bf16", 0)
+    moe.moe_grouped_gemm_fp8(d["a"], d["a_s"], d["w13"], d["w13_s"], dev(offs), dev(cut), h)
+    q = filled((rows, N), torch.uint8, 0)
+    s = filled((rows, N // 128), torch.float32, 0)
+    moe.moe_act_quant(h, N, moe.MOE_ACT_SILU_MUL, q, s, dev(offs), dev(cut), El)
+    y = filled((rows, K), "bf16", 0x7FC1)
+    moe.moe_grouped_gemm_fp8(q, s, d["w2"], d["w2_s"], dev(offs), dev(cut), y)
+    valid = valid_rows(offs, cut)
+    np.testing.assert_array_equal(got[valid], host(y, bf16=True)[valid])
+    assert np.all(got[np.setdiff1d(np.arange(rows), valid)] == 0x7FC1), "a row past a slot's count was written"
+    # the chain against the oracle
+    hg, qg, sg = host(h, bf16=True), host(q), host(s)
+    h_ref = oracle.grouped_gemm(a, a_s, w13, w13_s, offs, cut)
+    assert_bf16_close(hg[valid], h_ref[valid], "batched h")
+    qr, sr = oracle.silu_mul_quant(hg, offs, cut, El)
+    np.testing.assert_array_equal(qg[valid], qr[valid])
+    np.testing.assert_array_equal(sg[valid], sr[valid])
+    y_ref = oracle.grouped_gemm(qg, sg, w2, w2_s, offs, cut)
+    assert_bf16_close(got[valid], y_ref[valid], "batched out")
+
+
+# ------------------------------------------------------------ HBM streams
+def test_hbm_streams_move_every_byte():
+    """The measured-ceiling streams: the copy reproduces its source exactly
+    (including a tail that is not a whole grid stride), and both writes touch
+    every byte."""
+    announce("hbm streams")
+    n = (3 << 20) + 48
+    src = torch.from_numpy(np.random.default_rng(3).integers(0, 256, n, dtype=np.uint8)).to(DEV)
+    dst = filled((n,), torch.uint8, 0)
+    moe._lib.moe_hbm_stream(moe._lib.MOE_STREAM_COPY, src, dst, n)
+    np.testing.assert_array_equal(host(dst), host(src))
+    for mode in (moe._lib.MOE_STREAM_WRITE_NT, moe._lib.MOE_STREAM_WRITE):
+        dst.fill_(0)
+        moe._lib.moe_hbm_stream(mode, None, dst, n)
+        assert (host(dst) != 0).all()
+    sink = filled((16,), torch.uint8, 0)
+    moe._lib.moe_hbm_stream(moe._lib.MOE_STREAM_READ, src, sink, n)
+    torch.cuda.synchronize()

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe_hip.so")
 
 MOE_ACT_IDENTITY = 0
 MOE_ACT_SILU_MUL = 1
+MOE_STREAM_READ, MOE_STREAM_WRITE_NT, MOE_STREAM_COPY, MOE_STREAM_WRITE = 0, 1, 2, 3
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_WORKSPACE_TOO_SMALL",
           4: "MOE_ERR_UNSUPPORTED_DEVICE", 5: "MOE_ERR_HIP"}
 
@@ -39,7 +40,8 @@ EXPORTS = ["moe_status_string", "moe_last_error", "moe_max_rows", "moe_grouped_g
            "moe_forward_workspace_size", "moe_forward_workspace_slices",
            "moe_permute_workspace_size", "moe_count", "moe_permute", "moe_grouped_gemm_fp8",
            "moe_grouped_gemm_fp8_act_quant", "moe_act_quant", "moe_quant_permute", "moe_unpermute_weight_reduce",
-           "moe_forward_chunked", "moe_forward_chunked_noalloc", "moe_noalloc_scratch_bytes"]
+           "moe_forward_chunked", "moe_forward_chunked_noalloc", "moe_noalloc_scratch_bytes", "moe_hbm_stream",
+           "moe_batched_workspace_size", "moe_experts_batched_masked"]
 
 _lib = None
 
@@ -72,6 +74,9 @@ def load() -> C.CDLL:
         L.moe_forward_chunked.argtypes = [C.POINTER(MoeProblem), P, P, P, P, P, P, P, P, P, P, SZ,
                                           P, P]
         L.moe_forward_chunked_noalloc.argtypes = [C.POINTER(MoeProblem), P, P, P, P, P, P, P, P, P, P, P]
+        L.moe_hbm_stream.argtypes = [I32, P, P, SZ, P]
+        L.moe_batched_workspace_size.argtypes = [I32, I64, I32, C.POINTER(SZ)]
+        L.moe_experts_batched_masked.argtypes = [P, P, P, I32, I64, I32, I32, P, P, P, P, P, P, SZ, P]
         L.moe_noalloc_scratch_bytes.argtypes = []; L.moe_noalloc_scratch_bytes.restype = SZ
         for name in EXPORTS:
             if name not in ("moe_status_string", "moe_last_error", "moe_max_rows", "moe_grouped_gemm_tile_rows",
@@ -350,3 +355,39 @@ def moe_forward_chunked_noalloc(p: MoeProblem, x, topk_ids, topk_weights, expert
                                               _ptr(expert_map), _ptr(w13), _ptr(w13_s), _ptr(w2), _ptr(w2_s),
                                               _ptr(out), _ptr(per_chunk_counts), _stream(stream)),
            "moe_forward_chunked_noalloc")
+
+
+def moe_hbm_stream(mode: int, src, dst, nbytes: int, stream=None):
+    """A plain HBM read / write / copy stream of nbytes (a measured ceiling)."""
+    check_arg(dst, "dst", (torch.uint8,))
+    check_arg(src, "src", (torch.uint8,), optional=True)
+    if dst.numel() < (16 if mode == MOE_STREAM_READ else nbytes) or (src is not None and src.numel() < nbytes):
+        raise ValueError("buffers smaller than the stream")
+    check_device(src, dst)
+    _check(load().moe_hbm_stream(mode, _ptr(src), _ptr(dst), nbytes, _stream(stream)), "moe_hbm_stream")
+
+
+def moe_batched_workspace_size(El: int, max_tokens: int, N: int) -> int:
+    n = C.c_size_t(0)
+    _check(load().moe_batched_workspace_size(El, max_tokens, N, C.byref(n)), "moe_batched_workspace_size")
+    return int(n.value)
+
+
+def moe_experts_batched_masked(a_q, a_s, counts, w13, w13_s, w2, w2_s, out, workspace, stream=None):
+    """The experts on the batched, masked layout: a_q [El, max_tokens, K],
+    counts [El] valid rows per slot -> out [El, max_tokens, K] bf16."""
+    check_arg(a_q, "a_q", E4M3, (None, None, None))
+    El, max_tokens, K = a_q.shape
+    check_arg(a_s, "a_s", F32, (El, max_tokens, K // 128))
+    check_arg(counts, "counts", I32, (El,))
+    check_arg(w13, "w13", E4M3, (El, None, K))
+    N = w13.shape[1] // 2
+    check_arg(w13_s, "w13_s", F32, (El, 2 * N // 128, K // 128))
+    check_arg(w2, "w2", E4M3, (El, K, N))
+    check_arg(w2_s, "w2_s", F32, (El, K // 128, N // 128))
+    check_arg(out, "out", BF16, (El, max_tokens, K))
+    check_arg(workspace, "workspace", (torch.uint8,))
+    check_device(a_q, a_s, counts, w13, w13_s, w2, w2_s, out, workspace)
+    _check(load().moe_experts_batched_masked(_ptr(a_q), _ptr(a_s), _ptr(counts), El, max_tokens, K, N, _ptr(w13),
+                                             _ptr(w13_s), _ptr(w2), _ptr(w2_s), _ptr(out), _ptr(workspace),
+                                             _nbytes(workspace), _stream(stream)), "moe_experts_batched_masked")

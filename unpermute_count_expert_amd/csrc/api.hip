@@ -548,6 +548,103 @@ int moe_forward_chunked(const moe_problem* p, const uint16_t* x, const int32_t* 
                         static_cast<uint8_t*>(workspace), per_chunk_counts, cus, static_cast<hipStream_t>(stream));
 }
 
+namespace {
+
+// The batched entry's workspace: offsets, cut counts, act codes and scales.
+struct BatchedPlan {
+    size_t offsets, cut, act_q, act_s, total;
+};
+
+BatchedPlan batched_plan(int32_t El, int64_t max_tokens, int32_t N) {
+    BatchedPlan b{};
+    const size_t rows = (size_t)El * (size_t)max_tokens;
+    size_t off = 0;
+    b.offsets = off; off += up256((size_t)(El + 1) * 4);
+    b.cut = off;     off += up256((size_t)El * 4);
+    b.act_q = off;   off += up256(rows * N);
+    b.act_s = off;   off += up256(rows * (N / moe::kGroup) * 4);
+    b.total = off;
+    return b;
+}
+
+int check_batched_shape(int32_t El, int64_t max_tokens, int32_t K, int32_t N) {
+    REQUIRE(El >= 1 && El <= moe::kMaxLocalExperts, MOE_ERR_SHAPE, "El=%d outside [1,1024]", El);
+    REQUIRE(max_tokens >= 0 && (int64_t)El * max_tokens < (int64_t(1) << 31), MOE_ERR_SHAPE,
+            "max_tokens=%lld", (long long)max_tokens);
+    REQUIRE(K > 0 && K % moe::kGroup == 0 && K <= 65536, MOE_ERR_SHAPE,
+            "K=%d is not a positive multiple of 128 up to 65536", K);
+    REQUIRE(N > 0 && N % moe::kGroup == 0 && N <= 32768, MOE_ERR_SHAPE,
+            "N=%d is not a positive multiple of 128 up to 32768", N);
+    return MOE_OK;
+}
+
+}  // namespace
+
+int moe_batched_workspace_size(int32_t El, int64_t max_tokens, int32_t N, size_t* bytes) {
+    int st = check_batched_shape(El, max_tokens, 128, N);
+    if (st) return st;
+    REQUIRE(bytes != nullptr, MOE_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = batched_plan(El, max_tokens, N).total;
+    return MOE_OK;
+}
+
+int moe_experts_batched_masked(const uint8_t* a_q, const float* a_s, const int32_t* counts, int32_t El,
+                               int64_t max_tokens, int32_t K, int32_t N, const uint8_t* w13, const float* w13_s,
+                               const uint8_t* w2, const float* w2_s, uint16_t* out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    int st = check_batched_shape(El, max_tokens, K, N);
+    if (st) return st;
+    if (max_tokens == 0) return MOE_OK;
+    REQUIRE_PTR(a_q);
+    REQUIRE_PTR(a_s);
+    REQUIRE_PTR(counts);
+    REQUIRE_PTR(w13);
+    REQUIRE_PTR(w13_s);
+    REQUIRE_PTR(w2);
+    REQUIRE_PTR(w2_s);
+    REQUIRE_PTR(out);
+    REQUIRE_PTR(workspace);
+    const BatchedPlan b = batched_plan(El, max_tokens, N);
+    REQUIRE(workspace_bytes >= b.total, MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes,
+            b.total);
+    const int64_t rows = (int64_t)El * max_tokens;
+    const size_t out_bytes = (size_t)rows * K * 2;
+    REQUIRE(!overlaps(out, out_bytes, workspace, b.total), MOE_ERR_INVALID_ARG, "out overlaps the workspace");
+    REQUIRE(!overlaps(out, out_bytes, a_q, (size_t)rows * K), MOE_ERR_INVALID_ARG, "out overlaps a_q");
+    int cus = 0;
+    st = check_device(&cus);
+    if (st) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    int32_t* offsets = reinterpret_cast<int32_t*>(ws + b.offsets);
+    int32_t* cut = reinterpret_cast<int32_t*>(ws + b.cut);
+    uint8_t* act_q = ws + b.act_q;
+    float* act_s = reinterpret_cast<float*>(ws + b.act_s);
+    HIP_OK(moe::launch_slot_offsets(counts, El, max_tokens, offsets, cut, s));
+    // gate/up GEMM with the SiLU-mul requant in its epilogue: h never
+    // reaches memory
+    HIP_OK(moe::launch_grouped_gemm_act(a_q, a_s, w13, w13_s, offsets, cut, El, rows, N, K, act_q, act_s, rows,
+                                        cus, s));
+    HIP_OK(moe::launch_grouped_gemm(act_q, act_s, w2, w2_s, offsets, cut, El, rows, K, N, out, rows, cus, s));
+    return MOE_OK;
+}
+
+int moe_hbm_stream(int32_t mode, const void* src, void* dst, size_t bytes, void* stream) {
+    REQUIRE(mode >= MOE_STREAM_READ && mode <= MOE_STREAM_WRITE, MOE_ERR_INVALID_ARG, "mode=%d", mode);
+    REQUIRE(bytes % 16 == 0, MOE_ERR_SHAPE, "bytes=%zu is not a multiple of 16", bytes);
+    REQUIRE_PTR(dst);
+    if (mode == MOE_STREAM_READ || mode == MOE_STREAM_COPY) REQUIRE_PTR(src);
+    if (mode == MOE_STREAM_COPY)
+        REQUIRE(!overlaps(src, bytes, dst, bytes), MOE_ERR_INVALID_ARG, "src and dst overlap");
+    if (bytes == 0) return MOE_OK;
+    int cus = 0;
+    int st = check_device(&cus);
+    if (st) return st;
+    HIP_OK(moe::launch_stream(mode, src, dst, bytes, static_cast<uint32_t*>(dst), cus,
+                              static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
 size_t moe_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 int moe_forward_chunked_noalloc(const moe_problem* p, const uint16_t* x, const int32_t* topk_ids,

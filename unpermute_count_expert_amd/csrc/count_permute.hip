@@ -38,6 +38,20 @@ __global__ void k_fill_i32(int32_t* __restrict__ p, int64_t n, int32_t v) {
         p[i] = v;
 }
 
+// The batched, masked layout: slot e holds rows [e * max_tokens,
+// (e + 1) * max_tokens), the first counts[e] of them valid.  offsets[e] =
+// e * max_tokens, cut[e] = counts[e] clamped to [0, max_tokens].
+__global__ void k_slot_offsets(const int32_t* __restrict__ counts, int El, int64_t max_tokens,
+                               int32_t* __restrict__ offsets, int32_t* __restrict__ cut) {
+    for (int e = blockIdx.x * blockDim.x + threadIdx.x; e <= El; e += gridDim.x * blockDim.x) {
+        offsets[e] = (int32_t)(e * max_tokens);
+        if (e < El) {
+            const int64_t c = counts[e];
+            cut[e] = (int32_t)(c < 0 ? 0 : (c > max_tokens ? max_tokens : c));
+        }
+    }
+}
+
 // Each wave of the block keeps its own LDS histogram (fewer conflicting
 // atomics), and each block adds its totals to counts with one global atomic
 // per expert.
@@ -429,6 +443,12 @@ int bits_for(int El) {
 }
 
 }  // namespace
+
+hipError_t launch_slot_offsets(const int32_t* counts, int El, int64_t max_tokens, int32_t* offsets, int32_t* cut,
+                               hipStream_t s) {
+    k_slot_offsets<<<(unsigned)((El + 256) / 256), 256, 0, s>>>(counts, El, max_tokens, offsets, cut);
+    return hipGetLastError();
+}
 
 hipError_t launch_count(const int32_t* ids, int64_t num_pairs, const int32_t* emap, int Eg, int El,
                         int32_t* counts, int32_t* invalid, hipStream_t s) {

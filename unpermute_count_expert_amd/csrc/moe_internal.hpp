@@ -40,6 +40,11 @@ hipError_t launch_quant_permute(const uint16_t* x, const int32_t* ids, const flo
                                 int32_t* offsets, int32_t* inv_perm, int32_t* row_src, int32_t* hist,
                                 int32_t* counts_copy, hipStream_t s);
 
+// The batched, masked layout [El, max_tokens, ...]: offsets [El+1] =
+// e * max_tokens and the counts cut to [0, max_tokens].
+hipError_t launch_slot_offsets(const int32_t* counts, int El, int64_t max_tokens, int32_t* offsets, int32_t* cut,
+                               hipStream_t s);
+
 // ---- activation quantisation ------------------------------------------------
 // rows_hint: at most this many rows are valid (the chunk's routed pairs in
 // the forward; rows otherwise).  It sizes the grid of a masked launch, which
@@ -68,5 +73,11 @@ hipError_t launch_grouped_gemm_act(const uint8_t* a, const float* a_s, const uin
 hipError_t launch_unpermute(const uint16_t* y, int64_t y_rows, const int32_t* inv_perm,
                             const float* topk_w, int64_t Mc, int K, int topk, int apply_on_input, uint16_t* out,
                             hipStream_t s);
+
+// ---- HBM streams (measured ceilings) -------------------------------------------
+// mode: MOE_STREAM_* of moe.h; sink receives nothing in practice (read mode
+// keeps its loads live through it).
+hipError_t launch_stream(int mode, const void* src, void* dst, size_t bytes, uint32_t* sink, int num_cus,
+                         hipStream_t s);
 
 }  // namespace moe
