@@ -155,14 +155,55 @@ def count_scaled(iters, stream):
 
 
 def ceilings(iters, stream):
-    """Measured HBM ceiling on this GPU for context: a 1 GiB device copy
-    (read + write)."""
+    """Measured HBM ceilings on this GPU: the library's plain streams over
+    1 GiB (16-byte accesses, eight in flight per lane, one block per CU): a
+    read, a write with non-temporal stores, a write with ordinary stores, and
+    a copy (read + write); plus torch's copy_ of the same size for
+    reference."""
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
     b = torch.empty_like(a)
+    res = {}
+    for name, mode, moved in (("read", moe._lib.MOE_STREAM_READ, n), ("write_nt", moe._lib.MOE_STREAM_WRITE_NT, n),
+                              ("write", moe._lib.MOE_STREAM_WRITE, n), ("copy", moe._lib.MOE_STREAM_COPY, 2 * n)):
+        fn = lambda: moe._lib.moe_hbm_stream(mode, a, b, n)
+        fn()
+        st = stats([timed(fn, 1, stream) for _ in range(iters)])
+        res[name + "_GB/s"] = round(moved / (st["median"] * 1e-3) / 1e9, 1)
     cp = stats([timed(lambda: b.copy_(a), 1, stream) for _ in range(iters)])
-    return {"copy_GB/s": round(2 * n / (cp["median"] * 1e-3) / 1e9, 1),
-            "note": "torch copy_ of 1 GiB (read + write), median of %d" % iters}
+    res["torch_copy_GB/s"] = round(2 * n / (cp["median"] * 1e-3) / 1e9, 1)
+    res["note"] = "1 GiB streams, median of %d; copy counts read + written bytes" % iters
+    return res
+
+
+def batched_masked(iters, stream):
+    """moe_experts_batched_masked at a decode size: 256 tokens x top-8 routed
+    uniformly over 128 experts, the 64 of them local to this GPU (EP rank 1 of
+    2), so ~1024 rows over 64 slots of max_tokens = 64; K = 2048, N = 768."""
+    rng = np.random.default_rng(12)
+    El, max_tokens, K, N = 64, 64, 2048, 768
+    ids = np.argsort(-rng.standard_normal((256, 128)), axis=1)[:, :8]
+    cnt = np.bincount(ids[ids >= 64] - 64, minlength=El).astype(np.int32)
+    rows = El * max_tokens
+    a = torch.from_numpy(rng.integers(0, 0x7E, (El, max_tokens, K), dtype=np.uint8)).to("cuda:0")
+    a_s = torch.full((El, max_tokens, K // 128), 0.01, dtype=torch.float32, device="cuda:0")
+    w13, w13_s = gen.block_weights(rng, El, 2 * N, K)
+    w2, w2_s = gen.block_weights(rng, El, K, N)
+    w13, w13_s, w2, w2_s = dev(w13), dev(w13_s), dev(w2), dev(w2_s)
+    out = torch.empty((El, max_tokens, K), dtype=torch.int16, device="cuda:0")
+    ws = torch.empty(moe._lib.moe_batched_workspace_size(El, max_tokens, N), dtype=torch.uint8, device="cuda:0")
+    counts = dev(cnt)
+    fn = lambda: moe._lib.moe_experts_batched_masked(a, a_s, counts, w13, w13_s, w2, w2_s, out, ws)
+    for _ in range(200):
+        fn()
+    st = stats([timed(fn, 1, stream) for _ in range(iters)])
+    P = int(cnt.sum())
+    wbytes = 2 * N * K + K * N
+    ne = int((cnt > 0).sum())
+    return {"workload": f"{El} local experts x {max_tokens} slots, {P} routed rows (256 tokens x top-8 over 128 "
+                        f"experts), K={K} N={N}", "ms": st["median"], "p10": st["p10"], "p90": st["p90"],
+            "weight_GB/s": round(ne * wbytes / (st["median"] * 1e-3) / 1e9, 1),
+            "TFLOP/s": round(2.0 * P * (2 * N * K + K * N) / (st["median"] * 1e-3) / 1e12, 1)}
 
 
 def algorithmic(cfg, counts: np.ndarray, R: int):
@@ -185,7 +226,13 @@ def algorithmic(cfg, counts: np.ndarray, R: int):
         "gemm_w2": P * N + Ene * K * N + 2 * P * K + 4 * P * N / 128 + 4 * Ene * (K // 128) * (N // 128),
         "unpermute": 2 * P * K + 8 * M * T + 2 * M * K,
     }
-    return P, Ene, g1_flops, g2_flops, by
+    # (read, written) bytes of the memory-bound ops
+    rw = {
+        "quant_permute": (2 * M * K + 8 * M * T, P * K + 4 * P * K / 128 + 4 * M * T + 4 * R),
+        "silu_mul_quant": (4 * P * N, P * N + 4 * P * N / 128),
+        "unpermute": (2 * P * K + 8 * M * T, 2 * M * K),
+    }
+    return P, Ene, g1_flops, g2_flops, by, rw
 
 
 def cpu_baseline(inp, on_input, target_s=15.0):
@@ -263,8 +310,8 @@ def main():
     ap.add_argument("--config", default="C5u", choices=sorted(gen.CONFIGS))
     ap.add_argument("--op-iters", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--other-layers", action="store_true",
-                    help="also time short runs of the other layer configurations")
+    ap.add_argument("--no-other-layers", action="store_true",
+                    help="skip the short runs of the other layer configurations")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--profile-op", default=None,
                     help="time only this op (count, quant_permute, input_quant, permute, gemm_w13, silu_mul_quant, "
@@ -298,6 +345,22 @@ def main():
                           "ms": round(ops[args.profile_op][0], 5), "config": cfg.name}), flush=True)
         return
 
+    # the GPU reaches its sustained clock only after ~0.1 s of load: layer
+    # steps for 0.3 s first, then the per-op measurements, then the W warm-up
+    # and K timed layer steps
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < 0.3:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+    ops, counts, R = per_op_times(layer, d, on_input, args.op_iters, stream)
+    flush = Flusher()
+    ops_cold, _, _ = per_op_times(layer, d, on_input, args.op_iters, stream, flush=flush)
+    fused, _, _ = per_op_times(layer, d, on_input, args.op_iters, stream, only="gemm_w13_act")
+    unfused_in, _, _ = per_op_times(layer, d, on_input, args.op_iters, stream, fused_input=False)
+    count_big = count_scaled(args.op_iters, stream)
+    ceil = ceilings(5, stream)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -313,7 +376,6 @@ def main():
     warm = [evs[k].elapsed_time(evs[k + 1]) for k in range(args.steps)]
     ms = evs[0].elapsed_time(evs[-1]) / args.steps
 
-    flush = Flusher()
     cold = []
     for _ in range(args.steps):
         flush()
@@ -324,11 +386,7 @@ def main():
         e1.synchronize()
         cold.append(e0.elapsed_time(e1))
 
-    ops, counts, R = per_op_times(layer, d, on_input, args.op_iters, stream)
-    ops_cold, _, _ = per_op_times(layer, d, on_input, args.op_iters, stream, flush=flush)
-    fused, _, _ = per_op_times(layer, d, on_input, args.op_iters, stream, only="gemm_w13_act")
-    unfused_in, _, _ = per_op_times(layer, d, on_input, args.op_iters, stream, fused_input=False)
-    P, Ene, g1f, g2f, by = algorithmic(cfg, counts, R)
+    P, Ene, g1f, g2f, by, rw = algorithmic(cfg, counts, R)
     ops_out = {}
     for name in ops:
         st = stats(ops[name])
@@ -339,6 +397,13 @@ def main():
             rec["TFLOP/s"] = round(g1f / (t * 1e-3) / 1e12, 1)
         if name == "gemm_w2":
             rec["TFLOP/s"] = round(g2f / (t * 1e-3) / 1e12, 1)
+        if name in rw:
+            # the time the same bytes take on the measured streams: reads at
+            # the read stream's rate, writes at the non-temporal write stream's
+            floor = rw[name][0] / (ceil["read_GB/s"] * 1e9) + rw[name][1] / (ceil["write_nt_GB/s"] * 1e9)
+            rec["read_MB"], rec["write_MB"] = round(rw[name][0] / 1e6, 1), round(rw[name][1] / 1e6, 1)
+            rec["measured_stream_floor_ms"] = round(floor * 1e3, 5)
+            rec["frac_of_measured_streams"] = round(floor * 1e3 / t, 4)
         tc = stats(ops_cold[name])["median"]
         rec["cold_ms"] = tc
         rec["cold_GB/s"] = round(by[name] / (tc * 1e-3) / 1e9, 1)
@@ -382,12 +447,13 @@ def main():
         "gemm_tflops_both": round(gemm_both, 1),
         "gemm_frac_both": round(gemm_both / PEAK_FP8_TFLOPS, 4),
         "ops": ops_out,
-        "count_scaled_2^24_pairs": count_scaled(args.op_iters, stream),
-        "ceilings": ceilings(5, stream),
+        "count_scaled_2^24_pairs": count_big,
+        "ceilings": ceil,
+        "batched_masked_experts": batched_masked(args.op_iters, stream),
         "wall_s_timed": round(wall, 3),
         "input_gen_s": round(t_gen, 1),
     }
-    if args.other_layers:
+    if not args.no_other_layers:
         line["other_layers"] = other_layers([n for n in ("C5h", "C5u_on", "C3", "C4", "C2") if n != cfg.name])
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, on_input, args.cpu_seconds)
