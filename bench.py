@@ -112,7 +112,7 @@ def per_op_times(layer, d, on_input, iters, stream, only=None, flush=None, fused
         fused_input = False
     b = StepBuffers(layer, d["x"].shape[0], d["ids"].shape[1])
     ops = step_ops(layer, d["x"], d["ids"], d["w"], on_input, b, fused=(only == "gemm_w13_act"),
-                   fused_input=fused_input)
+                   fused_input=fused_input, reduce=(only == "gemm_w2_reduce"))
     names = list(ops)
     if only is not None:
         names = names[:names.index(only) + 1]
@@ -315,7 +315,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--profile-op", default=None,
                     help="time only this op (count, quant_permute, input_quant, permute, gemm_w13, silu_mul_quant, "
-                         "gemm_w2, unpermute, or gemm_w13_act: the fused variant) or 'copy'; for profiler runs")
+                         "gemm_w2, unpermute, gemm_w13_act: the fused gate/up variant, or gemm_w2_reduce: the down GEMM with "
+                         "the weight-and-reduce) or 'copy'; for profiler runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -357,6 +358,7 @@ def main():
     flush = Flusher()
     ops_cold, _, _ = per_op_times(layer, d, on_input, args.op_iters, stream, flush=flush)
     fused, _, _ = per_op_times(layer, d, on_input, args.op_iters, stream, only="gemm_w13_act")
+    reduced, _, _ = per_op_times(layer, d, on_input, args.op_iters, stream, only="gemm_w2_reduce")
     unfused_in, _, _ = per_op_times(layer, d, on_input, args.op_iters, stream, fused_input=False)
     count_big = count_scaled(args.op_iters, stream)
     ceil = ceilings(5, stream)
@@ -412,6 +414,10 @@ def main():
     ops_out["gemm_w13_act (fused variant, not on the forward path)"] = {
         "ms": round(tf, 5), "GB/s": round(by["gemm_w13_act"] / (tf * 1e-3) / 1e9, 1),
         "TFLOP/s": round(g1f / (tf * 1e-3) / 1e12, 1)}
+    tr = reduced["gemm_w2_reduce"][0]
+    ops_out["gemm_w2_reduce (w2 with the weight-and-reduce in its epilogue, not on the forward path)"] = {
+        "ms": round(tr, 5), "vs_gemm_w2_plus_unpermute_ms": round(stats(ops["gemm_w2"])["median"]
+                                                                  + stats(ops["unpermute"])["median"], 5)}
     for name in ("input_quant", "permute"):
         tu = stats(unfused_in[name])["median"]
         ops_out[name + " (separate call, not on the forward path)"] = {

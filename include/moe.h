@@ -188,6 +188,27 @@ int moe_grouped_gemm_fp8_act_quant(const uint8_t* a, const float* a_s, const uin
                                    const int32_t* counts, int32_t El, int64_t cap_rows, int32_t N,
                                    int32_t k_in, uint8_t* q, float* q_s, void* stream);
 
+/* The down grouped GEMM with the unpermute's topk weight-and-reduce in its
+ * epilogue (weight-and-reduce inside the experts, [P20725] Purpose/Changes;
+ * output (M, K), [P20903] bot Highlights): y = moe_grouped_gemm_fp8(a, w) on
+ * the valid rows, and out = moe_unpermute_weight_reduce(y, inv_perm,
+ * topk_weights, apply_on_input), the same bits as those two calls.  Each tile
+ * that has written its y rows counts, per row, that row's token up (row_src
+ * gives the token of a row); the tile that completes a token's valid rows for
+ * its 256 columns folds them in k order (fmaf from +0, one bf16 rounding), so
+ * the result does not depend on which tile finishes last.  y [cap_rows,n_out]
+ * bf16 (written), counters [Mc, ceil(n_out/256)] int32 device memory (any
+ * contents on entry; zero on exit), out [Mc, n_out] bf16 (tokens without a
+ * valid row get +0).  Other arguments as moe_grouped_gemm_fp8 and
+ * moe_unpermute_weight_reduce; row_src and inv_perm as moe_permute writes
+ * them (row_src [cap_rows]: token of a valid row). */
+int moe_grouped_gemm_fp8_weight_reduce(const uint8_t* a, const float* a_s, const uint8_t* w, const float* w_s,
+                                       const int32_t* expert_offsets, const int32_t* counts, int32_t El,
+                                       int64_t cap_rows, int32_t n_out, int32_t k_in, const int32_t* row_src,
+                                       const int32_t* inv_perm, const float* topk_weights, int32_t apply_on_input,
+                                       int64_t Mc, int32_t topk, uint16_t* y, int32_t* counters, uint16_t* out,
+                                       void* stream);
+
 /* Per-token-group (1x128) fp8 quantisation.
  *   MOE_ACT_IDENTITY: v = in[r, :n]                        (in is [rows, n])
  *   MOE_ACT_SILU_MUL: v = bf16(silu(in[r, :n]) * in[r, n:2n]) (in is [rows, 2n])

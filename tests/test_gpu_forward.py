@@ -391,3 +391,30 @@ def test_forward_is_deterministic():
     a, _ = _forward(layer, d, cfg.M, 0, 0)
     b, _ = _forward(layer, d, cfg.M, 0, 0)
     np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("name,cfg,on_input", [CASES[i] for i in (0, 2, 3, 5, 6, 8, 9, 12, 13)],
+                         ids=[CASES[i][0] for i in (0, 2, 3, 5, 6, 8, 9, 12, 13)])
+def test_gemm_w2_with_weight_reduce(name, cfg, on_input):
+    """The down GEMM with the unpermute's weight-and-reduce folded into its
+    epilogue (moe_grouped_gemm_fp8_weight_reduce): y and out are the same
+    bits as GEMM w2 followed by the separate unpermute, which are checked
+    against the oracle in test_layer_parity; tokens without a local row get
+    +0; the counters are zero afterwards; a second call gives the same bits."""
+    announce("gemm w2 + weight-reduce", name, on_input)
+    inp = _inputs(cfg)
+    M, K, T = cfg.M, cfg.K, cfg.topk
+    layer = _layer(inp)
+    d = dict(x=dev(inp.x), ids=dev(inp.topk_ids), w=dev(inp.topk_weights))
+    b = run_steps(layer, d["x"], d["ids"], d["w"], on_input)
+    cap = b.cap
+    rows = valid_rows(host(b.offsets), host(b.counts))
+    for rep in range(2):
+        y = filled((cap, K), "bf16", 0x7FC1)
+        out = filled((M, K), "bf16", 0x7FC1)
+        cnt = filled((M, -(-K // 256)), torch.int32, 12345 if rep == 0 else 0)
+        moe._lib.moe_grouped_gemm_fp8_weight_reduce(b.act_q, b.act_s, layer.w2, layer.w2_s, b.offsets, b.counts,
+                                                    b.row_src, b.inv_perm, d["w"], on_input, y, cnt, out)
+        np.testing.assert_array_equal(host(y, bf16=True)[rows], host(b.y, bf16=True)[rows])
+        np.testing.assert_array_equal(host(out, bf16=True), host(b.out, bf16=True))
+        assert (host(cnt) == 0).all(), "a token counter was left non-zero"

@@ -41,7 +41,7 @@ EXPORTS = ["moe_status_string", "moe_last_error", "moe_max_rows", "moe_grouped_g
            "moe_permute_workspace_size", "moe_count", "moe_permute", "moe_grouped_gemm_fp8",
            "moe_grouped_gemm_fp8_act_quant", "moe_act_quant", "moe_quant_permute", "moe_unpermute_weight_reduce",
            "moe_forward_chunked", "moe_forward_chunked_noalloc", "moe_noalloc_scratch_bytes", "moe_hbm_stream",
-           "moe_batched_workspace_size", "moe_experts_batched_masked"]
+           "moe_batched_workspace_size", "moe_experts_batched_masked", "moe_grouped_gemm_fp8_weight_reduce"]
 
 _lib = None
 
@@ -75,6 +75,8 @@ def load() -> C.CDLL:
                                           P, P]
         L.moe_forward_chunked_noalloc.argtypes = [C.POINTER(MoeProblem), P, P, P, P, P, P, P, P, P, P, P]
         L.moe_hbm_stream.argtypes = [I32, P, P, SZ, P]
+        L.moe_grouped_gemm_fp8_weight_reduce.argtypes = [P, P, P, P, P, P, I32, I64, I32, I32, P, P, P, I32, I64, I32,
+                                                         P, P, P, P]
         L.moe_batched_workspace_size.argtypes = [I32, I64, I32, C.POINTER(SZ)]
         L.moe_experts_batched_masked.argtypes = [P, P, P, I32, I64, I32, I32, P, P, P, P, P, P, SZ, P]
         L.moe_noalloc_scratch_bytes.argtypes = []; L.moe_noalloc_scratch_bytes.restype = SZ
@@ -391,3 +393,24 @@ def moe_experts_batched_masked(a_q, a_s, counts, w13, w13_s, w2, w2_s, out, work
     _check(load().moe_experts_batched_masked(_ptr(a_q), _ptr(a_s), _ptr(counts), El, max_tokens, K, N, _ptr(w13),
                                              _ptr(w13_s), _ptr(w2), _ptr(w2_s), _ptr(out), _ptr(workspace),
                                              _nbytes(workspace), _stream(stream)), "moe_experts_batched_masked")
+
+
+def moe_grouped_gemm_fp8_weight_reduce(a, a_s, w, w_s, expert_offsets, counts, row_src, inv_perm, topk_weights,
+                                       apply_on_input, y, counters, out, stream=None):
+    """The down GEMM with the unpermute's weight-and-reduce in its epilogue:
+    y = GEMM(a, w) on the valid rows and out [Mc, n_out] = the weighted sum of
+    each token's rows of y (the same bits as the two separate calls)."""
+    cap_rows, k_in, El, n_out = _check_gemm_operands(a, a_s, w, w_s, expert_offsets, counts)
+    check_arg(row_src, "row_src", I32, (None,), min_rows=cap_rows)
+    check_arg(inv_perm, "inv_perm", I32, (None, None))
+    Mc, topk = inv_perm.shape
+    check_arg(topk_weights, "topk_weights", F32, (Mc, topk), optional=bool(apply_on_input))
+    check_arg(y, "y", BF16, (cap_rows, n_out))
+    check_arg(counters, "counters", I32, (Mc, (n_out + 255) // 256))
+    check_arg(out, "out", BF16, (Mc, n_out))
+    check_device(a, a_s, w, w_s, expert_offsets, counts, row_src, inv_perm, topk_weights, y, counters, out)
+    _check(load().moe_grouped_gemm_fp8_weight_reduce(_ptr(a), _ptr(a_s), _ptr(w), _ptr(w_s), _ptr(expert_offsets),
+                                                     _ptr(counts), El, cap_rows, n_out, k_in, _ptr(row_src),
+                                                     _ptr(inv_perm), _ptr(topk_weights), apply_on_input, Mc, topk,
+                                                     _ptr(y), _ptr(counters), _ptr(out), _stream(stream)),
+           "moe_grouped_gemm_fp8_weight_reduce")

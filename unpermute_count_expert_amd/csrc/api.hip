@@ -353,6 +353,51 @@ int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const uint8_t* w, c
     return MOE_OK;
 }
 
+int moe_grouped_gemm_fp8_weight_reduce(const uint8_t* a, const float* a_s, const uint8_t* w, const float* w_s,
+                                       const int32_t* expert_offsets, const int32_t* counts, int32_t El,
+                                       int64_t cap_rows, int32_t n_out, int32_t k_in, const int32_t* row_src,
+                                       const int32_t* inv_perm, const float* topk_weights, int32_t apply_on_input,
+                                       int64_t Mc, int32_t topk, uint16_t* y, int32_t* counters, uint16_t* out,
+                                       void* stream) {
+    REQUIRE(El >= 1 && El <= moe::kMaxLocalExperts, MOE_ERR_SHAPE, "El=%d outside [1,1024]", El);
+    REQUIRE(n_out > 0 && n_out % moe::kGroup == 0 && n_out <= 65536, MOE_ERR_SHAPE,
+            "n_out=%d is not a positive multiple of 128 up to 65536", n_out);
+    REQUIRE(k_in > 0 && k_in % moe::kGroup == 0 && k_in <= 65536, MOE_ERR_SHAPE,
+            "k_in=%d is not a positive multiple of 128 up to 65536", k_in);
+    REQUIRE(cap_rows >= 0 && cap_rows < (int64_t(1) << 31), MOE_ERR_SHAPE, "cap_rows=%lld", (long long)cap_rows);
+    REQUIRE(Mc >= 0 && topk >= 1 && topk <= 256, MOE_ERR_SHAPE, "Mc=%lld topk=%d", (long long)Mc, topk);
+    REQUIRE(apply_on_input == 0 || apply_on_input == 1, MOE_ERR_INVALID_ARG, "apply_on_input=%d", apply_on_input);
+    if (Mc == 0) return MOE_OK;
+    REQUIRE_PTR(inv_perm);
+    REQUIRE_PTR(counters);
+    REQUIRE_PTR(out);
+    if (!apply_on_input) REQUIRE_PTR(topk_weights);
+    if (cap_rows > 0) {
+        REQUIRE_PTR(a);
+        REQUIRE_PTR(a_s);
+        REQUIRE_PTR(w);
+        REQUIRE_PTR(w_s);
+        REQUIRE_PTR(expert_offsets);
+        REQUIRE_PTR(counts);
+        REQUIRE_PTR(row_src);
+        REQUIRE_PTR(y);
+    }
+    const size_t out_bytes = (size_t)Mc * n_out * 2;
+    REQUIRE(!overlaps(out, out_bytes, y, (size_t)cap_rows * n_out * 2), MOE_ERR_INVALID_ARG, "out overlaps y");
+    REQUIRE(!overlaps(counters, (size_t)Mc * ((n_out + 255) / 256) * 4, y, (size_t)cap_rows * n_out * 2),
+            MOE_ERR_INVALID_ARG, "counters overlap y");
+    int cus = 0;
+    int st = check_device(&cus);
+    if (st) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    HIP_OK(moe::launch_reduce_prep(inv_perm, Mc, topk, cap_rows, n_out, counters, out, s));
+    if (cap_rows > 0)
+        HIP_OK(moe::launch_grouped_gemm_reduce(a, a_s, w, w_s, expert_offsets, counts, El, cap_rows, n_out, k_in, y,
+                                               row_src, inv_perm, topk_weights, apply_on_input, Mc, topk, counters,
+                                               out, cap_rows, cus, s));
+    return MOE_OK;
+}
+
 int moe_grouped_gemm_fp8_act_quant(const uint8_t* a, const float* a_s, const uint8_t* w13,
                                    const float* w13_s, const int32_t* expert_offsets,
                                    const int32_t* counts, int32_t El, int64_t cap_rows, int32_t N,

@@ -235,12 +235,36 @@ struct TileWalk {
 // written to q [rows, N] and q_s [rows, N/128].  A tile then holds 128 gate
 // and the matching 128 up columns, and each lane owns matched gate/up pairs,
 // so no intermediate h is stored.
-template <bool KACT, int MI>
+//
+// RED (with KACT = false; the down GEMM with the unpermute's weight-and-reduce
+// folded into its epilogue): out is y as above, and for every token t of the
+// chunk and column n, red_out[t, n] = bf16(fmaf chain over k = 0..topk-1 with
+// a valid row r = inv_perm[t, k] of w'_k * y[r, n]), w'_k = topk_w[t, k] or 1
+// on input: the same bits as moe_unpermute_weight_reduce.  A tile that has
+// stored its y rows makes them visible device-wide and counts, per row, its
+// token's (token, n-tile) counter up; the tile that brings a counter to the
+// token's number of valid rows folds that token's rows for its columns (the
+// other rows were made visible before their counts) and sets the counter back
+// to zero.  Nothing waits for another tile.  The counters must be zero on entry
+// and are zero again on exit; tokens without a valid row are written by the
+// launcher's preparation kernel.
+struct ReduceArgs {
+    const int32_t* row_src;   // [cap_rows] token of each row, -1 on padding
+    const int32_t* inv_perm;  // [Mc, topk]
+    const float* topk_w;      // [Mc, topk]
+    int on_input;
+    int topk;
+    int64_t Mc;
+    int32_t* cnt;             // [Mc, ceil(n_out / 256)]
+    uint16_t* out;            // [Mc, n_out]
+};
+
+template <bool KACT, int MI, bool RED = false>
 __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
     const uint8_t* __restrict__ a, const float* __restrict__ a_s, const uint8_t* __restrict__ w,
     const float* __restrict__ w_s, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ counts, int El, int64_t cap_rows, int n_out, int k_in,
-    uint16_t* __restrict__ out, uint8_t* __restrict__ q, float* __restrict__ q_s) {
+    uint16_t* __restrict__ out, uint8_t* __restrict__ q, float* __restrict__ q_s, ReduceArgs red) {
     using Sh = Shape<MI>;
     constexpr int BM = Sh::BM, kStageA = Sh::kStageA, kStage = Sh::kStage, kStages = Sh::kStages;
     constexpr int kADma = Sh::kADma, kDmaPerStep = Sh::kDmaPerStep, kScaleRows = Sh::kScaleRows;
@@ -254,6 +278,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
     __shared__ int s_wsum[kWaves];
     __shared__ float s_amax[KACT ? 4 : 1][KACT ? BM : 1];   // per-wave-column partial group maxima
     __shared__ __attribute__((aligned(16))) float s_inv[KACT ? BM : 1];   // 448 / d of each row
+    __shared__ int s_fold[RED ? BM : 1];   // tokens this tile completes
+    __shared__ int s_nfold;
     const int n_half = n_out / 2;                 // N when KACT
 
     const int tid = threadIdx.x;
@@ -526,6 +552,60 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
                             if (row0 + mi * 16 + v < cur.row_end) store_row(mi, v);
                 }
             }
+            if constexpr (RED) {
+                // ---- weight-and-reduce of the tokens this tile completes ----
+                // the y stores of every wave, visible device-wide before any
+                // count of this tile
+                if (tid == 0) s_nfold = 0;
+                __threadfence();
+                __syncthreads();
+                const int ntn_ = (n_out + BN - 1) / BN;
+                if (tid < BM) {
+                    const int row = cur.m0 + tid;
+                    const int64_t t = row < cur.row_end ? (int64_t)red.row_src[row] : -1;
+                    if (t >= 0 && t < red.Mc) {
+                        int need = 0;
+                        for (int k = 0; k < red.topk; ++k) {
+                            const int r = red.inv_perm[t * red.topk + k];
+                            need += (r >= 0 && r < cap_rows) ? 1 : 0;
+                        }
+                        const int old = atomicAdd(&red.cnt[t * ntn_ + cur.tn], 1);
+                        if (old + 1 == need) s_fold[atomicAdd(&s_nfold, 1)] = (int)t;
+                    }
+                }
+                __syncthreads();
+                const int nfold = s_nfold;
+                if (nfold > 0) {
+                    // the other tiles' y rows of these tokens: counted after
+                    // they were made visible
+                    __threadfence();
+                    const int c = cur.n0 + 4 * lane;   // this lane's 4 columns
+                    for (int f = wave; f < nfold; f += kWaves) {
+                        const int64_t t = s_fold[f];
+                        if (4 * lane < n_valid) {
+                            float acc4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                            for (int k = 0; k < red.topk; ++k) {
+                                const int r = red.inv_perm[t * red.topk + k];
+                                if (r < 0 || r >= cap_rows) continue;
+                                const float wk = red.on_input ? 1.0f : red.topk_w[t * red.topk + k];
+                                const v2i yv = *reinterpret_cast<const v2i*>(out + (int64_t)r * n_out + c);
+                                const uint32_t lo = (uint32_t)yv.x, hi = (uint32_t)yv.y;
+                                acc4[0] = __builtin_fmaf(wk, __uint_as_float(lo << 16), acc4[0]);
+                                acc4[1] = __builtin_fmaf(wk, __uint_as_float(lo & 0xffff0000u), acc4[1]);
+                                acc4[2] = __builtin_fmaf(wk, __uint_as_float(hi << 16), acc4[2]);
+                                acc4[3] = __builtin_fmaf(wk, __uint_as_float(hi & 0xffff0000u), acc4[3]);
+                            }
+                            v2i o;
+                            o.x = (int)f32x2_to_bf16x2(acc4[0], acc4[1]);
+                            o.y = (int)f32x2_to_bf16x2(acc4[2], acc4[3]);
+                            __builtin_nontemporal_store(o, reinterpret_cast<v2i*>(red.out + t * n_out + c));
+                        }
+                        if (lane == 0) red.cnt[t * ntn_ + cur.tn] = 0;
+                    }
+                }
+                // s_fold and s_nfold are reused by the next tile
+                __syncthreads();
+            }
         } else {
             // ---- epilogue: SiLU-and-mul and per-128 requant ----------------
             // This lane holds, for 4 * MI rows, act columns 2fr and 2fr+1 of
@@ -677,11 +757,32 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_s, const uint8_t
     if (gemm_tile_rows(rows_hint, El) == 256) {
         const int64_t grid = gemm_grid(cap_rows, El, n_out, Shape<8>::BM, num_cus);
         k_grouped_gemm<false, 8><<<(unsigned)grid, kThreads, 0, s>>>(a, a_s, w, w_s, offsets, counts, El,
-                                                                      cap_rows, n_out, k_in, out, nullptr, nullptr);
+                                                                      cap_rows, n_out, k_in, out, nullptr, nullptr, ReduceArgs{});
     } else {
         const int64_t grid = gemm_grid(cap_rows, El, n_out, Shape<4>::BM, num_cus);
         k_grouped_gemm<false, 4><<<(unsigned)grid, kThreads, 0, s>>>(a, a_s, w, w_s, offsets, counts, El,
-                                                                      cap_rows, n_out, k_in, out, nullptr, nullptr);
+                                                                      cap_rows, n_out, k_in, out, nullptr, nullptr, ReduceArgs{});
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm_reduce(const uint8_t* a, const float* a_s, const uint8_t* w, const float* w_s,
+                                      const int32_t* offsets, const int32_t* counts, int El, int64_t cap_rows,
+                                      int n_out, int k_in, uint16_t* y, const int32_t* row_src,
+                                      const int32_t* inv_perm, const float* topk_w, int on_input, int64_t Mc,
+                                      int topk, int32_t* cnt, uint16_t* out, int64_t rows_hint, int num_cus,
+                                      hipStream_t s) {
+    const ReduceArgs red{row_src, inv_perm, topk_w, on_input, topk, Mc, cnt, out};
+    if (gemm_tile_rows(rows_hint, El) == 256) {
+        const int64_t grid = gemm_grid(cap_rows, El, n_out, Shape<8>::BM, num_cus);
+        k_grouped_gemm<false, 8, true><<<(unsigned)grid, kThreads, 0, s>>>(a, a_s, w, w_s, offsets, counts, El,
+                                                                            cap_rows, n_out, k_in, y, nullptr,
+                                                                            nullptr, red);
+    } else {
+        const int64_t grid = gemm_grid(cap_rows, El, n_out, Shape<4>::BM, num_cus);
+        k_grouped_gemm<false, 4, true><<<(unsigned)grid, kThreads, 0, s>>>(a, a_s, w, w_s, offsets, counts, El,
+                                                                            cap_rows, n_out, k_in, y, nullptr,
+                                                                            nullptr, red);
     }
     return hipGetLastError();
 }
@@ -693,11 +794,11 @@ hipError_t launch_grouped_gemm_act(const uint8_t* a, const float* a_s, const uin
     if (gemm_tile_rows(rows_hint, El) == 256) {
         const int64_t grid = gemm_grid(cap_rows, El, 2 * N, Shape<8>::BM, num_cus);
         k_grouped_gemm<true, 8><<<(unsigned)grid, kThreads, 0, s>>>(a, a_s, w13, w13_s, offsets, counts, El,
-                                                                     cap_rows, 2 * N, k_in, nullptr, q, q_s);
+                                                                     cap_rows, 2 * N, k_in, nullptr, q, q_s, ReduceArgs{});
     } else {
         const int64_t grid = gemm_grid(cap_rows, El, 2 * N, Shape<4>::BM, num_cus);
         k_grouped_gemm<true, 4><<<(unsigned)grid, kThreads, 0, s>>>(a, a_s, w13, w13_s, offsets, counts, El,
-                                                                     cap_rows, 2 * N, k_in, nullptr, q, q_s);
+                                                                     cap_rows, 2 * N, k_in, nullptr, q, q_s, ReduceArgs{});
     }
     return hipGetLastError();
 }

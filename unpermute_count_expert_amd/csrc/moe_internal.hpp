@@ -69,6 +69,21 @@ hipError_t launch_grouped_gemm_act(const uint8_t* a, const float* a_s, const uin
                                    int El, int64_t cap_rows, int N, int k_in, uint8_t* q, float* q_s,
                                    int64_t rows_hint, int num_cus, hipStream_t s);
 
+// The down GEMM with the unpermute's weight-and-reduce in its epilogue: y
+// [cap_rows, n_out] as launch_grouped_gemm, and out [Mc, n_out] as
+// launch_unpermute of that y.  cnt [Mc, ceil(n_out / 256)] must be zero on
+// entry (launch_reduce_prep) and is zero again on exit.
+hipError_t launch_grouped_gemm_reduce(const uint8_t* a, const float* a_s, const uint8_t* w, const float* w_s,
+                                      const int32_t* offsets, const int32_t* counts, int El, int64_t cap_rows,
+                                      int n_out, int k_in, uint16_t* y, const int32_t* row_src,
+                                      const int32_t* inv_perm, const float* topk_w, int on_input, int64_t Mc,
+                                      int topk, int32_t* cnt, uint16_t* out, int64_t rows_hint, int num_cus,
+                                      hipStream_t s);
+// Zeroes cnt [Mc, ceil(K / 256)] and writes +0 output rows for the tokens
+// without a valid row.
+hipError_t launch_reduce_prep(const int32_t* inv_perm, int64_t Mc, int topk, int64_t y_rows, int K, int32_t* cnt,
+                              uint16_t* out, hipStream_t s);
+
 // ---- unpermute ----------------------------------------------------------------
 hipError_t launch_unpermute(const uint16_t* y, int64_t y_rows, const int32_t* inv_perm,
                             const float* topk_w, int64_t Mc, int K, int topk, int apply_on_input, uint16_t* out,

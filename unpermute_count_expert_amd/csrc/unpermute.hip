@@ -154,7 +154,36 @@ __global__ __launch_bounds__(kThreads) void k_unpermute(const uint16_t* __restri
     }
 }
 
+// Before the down GEMM with the weight-and-reduce in its epilogue: one wave
+// per token zeroes the token's (token, n-tile) counters and, when none of its
+// topk rows is valid (no tile will complete it), writes its output row as +0.
+__global__ __launch_bounds__(kThreads) void k_reduce_prep(const int32_t* __restrict__ inv_perm, int64_t Mc, int topk,
+                                                          int64_t y_rows, int K, int32_t* __restrict__ cnt, int ntn,
+                                                          uint16_t* __restrict__ out) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t t = (int64_t)blockIdx.x * kTokensPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    if (t >= Mc) return;
+    for (int j = lane; j < ntn; j += kWave) cnt[t * ntn + j] = 0;
+    bool any = false;
+    for (int k = lane; k < topk; k += kWave) {
+        const int r = inv_perm[t * topk + k];
+        any |= r >= 0 && r < y_rows;
+    }
+    if (__ballot(any) == 0)
+        for (int c0 = lane * 8; c0 < K; c0 += kWave * 8)
+            *reinterpret_cast<uint4*>(out + t * K + c0) = uint4{0, 0, 0, 0};
+}
+
 }  // namespace
+
+hipError_t launch_reduce_prep(const int32_t* inv_perm, int64_t Mc, int topk, int64_t y_rows, int K, int32_t* cnt,
+                              uint16_t* out, hipStream_t s) {
+    if (Mc <= 0) return hipSuccess;
+    const int ntn = (K + 255) / 256;
+    k_reduce_prep<<<(unsigned)((Mc + kTokensPerBlock - 1) / kTokensPerBlock), kThreads, 0, s>>>(
+        inv_perm, Mc, topk, y_rows, K, cnt, ntn, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_unpermute(const uint16_t* y, int64_t y_rows, const int32_t* inv_perm,
                             const float* topk_w, int64_t Mc, int K, int topk, int apply_on_input, uint16_t* out,

@@ -5,7 +5,8 @@ With the defaults the ops are exactly the kernels moe_forward_chunked runs,
 in its order: the input quant fused into the permute (moe_quant_permute),
 the gate/up GEMM writing h, a separate SiLU-mul requant, the down GEMM and
 the unpermute (plus the standalone count, which the forward does inside the
-permute).  fused_input=False runs the input quant and the permute as two
+permute).  reduce=True runs the down GEMM with the weight-and-reduce in its
+epilogue (moe_grouped_gemm_fp8_weight_reduce) instead of the last two.  fused_input=False runs the input quant and the permute as two
 calls instead, keeping a_q / a_s; fused=True uses the gate/up GEMM fused with
 the SiLU-mul requant (moe_grouped_gemm_fp8_act_quant), so h never reaches
 memory.  The forward call runs on one reused workspace; this form trades
@@ -38,10 +39,11 @@ class StepBuffers:
         self.y = e((cap, K), b16)
         self.out = e((M, K), b16)
         self.count_only = e((El,), i32)
+        self.red_cnt = e((M, -(-K // 256)), i32)
 
 
 def step_ops(layer, x, topk_ids, topk_weights, apply_on_input: int, b: StepBuffers, fused: bool = False,
-             fused_input: bool = True):
+             fused_input: bool = True, reduce: bool = False):
     """Ordered {name: thunk}; running them in order computes the layer into b.out."""
     Eg, El, K, N, A = layer.Eg, layer.El, layer.K, layer.N, layer.align
     emap = layer.expert_map
@@ -65,6 +67,11 @@ def step_ops(layer, x, topk_ids, topk_weights, apply_on_input: int, b: StepBuffe
                                                             b.offsets, b.counts, b.h)
         ops["silu_mul_quant"] = lambda: _lib.moe_act_quant(b.h, N, _lib.MOE_ACT_SILU_MUL, b.act_q, b.act_s,
                                                            b.offsets, b.counts, El)
+    if reduce:
+        ops["gemm_w2_reduce"] = lambda: _lib.moe_grouped_gemm_fp8_weight_reduce(
+            b.act_q, b.act_s, layer.w2, layer.w2_s, b.offsets, b.counts, b.row_src, b.inv_perm, topk_weights,
+            apply_on_input, b.y, b.red_cnt, b.out)
+        return ops
     ops["gemm_w2"] = lambda: _lib.moe_grouped_gemm_fp8(b.act_q, b.act_s, layer.w2, layer.w2_s, b.offsets,
                                                        b.counts, b.y)
     ops["unpermute"] = lambda: _lib.moe_unpermute_weight_reduce(b.y, b.inv_perm, topk_weights,
@@ -73,9 +80,9 @@ def step_ops(layer, x, topk_ids, topk_weights, apply_on_input: int, b: StepBuffe
 
 
 def run_steps(layer, x, topk_ids, topk_weights, apply_on_input: int = 0, b: StepBuffers = None,
-              fused: bool = False, fused_input: bool = True):
+              fused: bool = False, fused_input: bool = True, reduce: bool = False):
     if b is None:
         b = StepBuffers(layer, x.shape[0], topk_ids.shape[1], x.device)
-    for fn in step_ops(layer, x, topk_ids, topk_weights, apply_on_input, b, fused, fused_input).values():
+    for fn in step_ops(layer, x, topk_ids, topk_weights, apply_on_input, b, fused, fused_input, reduce).values():
         fn()
     return b
