@@ -87,9 +87,13 @@ int64_t moe_max_rows(int64_t Mc, int32_t topk, int32_t El, int32_t align);
 int moe_forward_workspace_size(const moe_problem* p, size_t* bytes);
 
 /* The slices moe_forward_chunked carves from its workspace for problem p:
- * *num_slices receives their number (8: permuted rows then act codes,
+ * *num_slices receives their number (10: permuted rows then act codes,
  * their scales, h then y, counts, offsets, inv_perm, row_src, the permute's
- * per-block histogram); the first min(max_slices, *num_slices) byte offsets
+ * per-block histogram, the fp32 partial sums of the GEMMs with K split for
+ * small chunks (empty when the plan splits neither GEMM) and the two
+ * GEMMs' segment counts), times the lanes (two with two chunks or more:
+ * the second lane's ten slices follow the first's, in the same order); the
+ * first min(max_slices, *num_slices) byte offsets
  * and lengths are written to offsets[] and bytes[].  Between the end of a
  * slice and the next slice's offset (and up to the workspace size after the
  * last) lies a guard band that no kernel reads or writes: a caller can fill
@@ -235,6 +239,57 @@ int moe_unpermute_weight_reduce(const uint16_t* y, int64_t y_rows, const int32_t
                                 const float* topk_weights, int64_t Mc, int32_t K, int32_t topk,
                                 int32_t apply_on_input, uint16_t* out, void* stream);
 
+/* moe_grouped_gemm_fp8 for experts of few rows (the layer's small chunks,
+ * e.g. the 64-token chunks of [P20392 Purpose]): 64-row output tiles, and
+ * the option of cutting K so that a few tiles still spread over all CUs.
+ *   part NULL: out exactly as moe_grouped_gemm_fp8 (the same bits).
+ *   part set:  when the tiles fill fewer than four rounds of the CUs, K is cut
+ *     into S = nsplit segments of k_in/nsplit (nsplit in 1..8 dividing
+ *     k_in/128), else S = 1; info[0] receives S.  Slab s of part holds, for
+ *     each valid row, the fp32 sum over the groups g of segment s of the
+ *     terms a_s[r,g] * w_s[e,n/128,g] * sum_{k in g} a[r,k] w[e,n,k], folded
+ *     in g order as the whole-K GEMM folds them: part[s, v, n], where v is
+ *     the row's place in the valid rows of all experts in expert order
+ *     (expert e's rows from sum_{e'<e} counts[e']).  bf16 of the slabs' sum
+ *     in slab order is the GEMM's output (with S = 1, out's exact bits).
+ *     part [nsplit, part_rows, n_out] f32; rows at places >= part_rows are
+ *     not stored; out is not written.
+ * Other arguments, limits and errors as moe_grouped_gemm_fp8. */
+int moe_grouped_gemm_fp8_small(const uint8_t* a, const float* a_s, const uint8_t* w, const float* w_s,
+                               const int32_t* expert_offsets, const int32_t* counts, int32_t El, int64_t cap_rows,
+                               int32_t n_out, int32_t k_in, uint16_t* out, float* part, int64_t part_rows,
+                               int32_t nsplit, int32_t* info, void* stream);
+
+/* moe_act_quant in MOE_ACT_SILU_MUL mode, masked, whose input h is given as
+ * moe_grouped_gemm_fp8_small's partial sums: h[r, c] = bf16 of the sum, in
+ * slab order, of the first min(info[0], nsplit) slabs of part [nsplit,
+ * part_rows, 2n] at row r's valid-row place (a place >= part_rows reads
+ * as 0).  q, q_s and every other argument as moe_act_quant; the codes equal
+ * moe_act_quant's on that h. */
+int moe_act_quant_partials(const float* part, const int32_t* info, int64_t part_rows, int32_t nsplit, int64_t rows,
+                           int32_t n, const int32_t* expert_offsets, const int32_t* counts, int32_t El, uint8_t* q,
+                           float* q_s, void* stream);
+
+/* moe_unpermute_weight_reduce whose y is given as moe_grouped_gemm_fp8_small's
+ * partial sums: y[r, c] = bf16 of the sum, in slab order, of the first
+ * min(info[0], nsplit) slabs of part [nsplit, part_rows, K] at row r's
+ * valid-row place (expert_offsets / counts / El locate it; y_rows bounds r
+ * as before).  An index that is no expert's valid row is not folded.  The
+ * output equals moe_unpermute_weight_reduce's on that y. */
+int moe_unpermute_partials(const float* part, const int32_t* info, int64_t part_rows, int32_t nsplit,
+                           const int32_t* expert_offsets, const int32_t* counts, int32_t El, int64_t y_rows,
+                           const int32_t* inv_perm, const float* topk_weights, int64_t Mc, int32_t K, int32_t topk,
+                           int32_t apply_on_input, uint16_t* out, void* stream);
+
+/* How moe_forward_chunked runs problem p: *small_tiles = 1 when its chunks
+ * take moe_grouped_gemm_fp8_small (at most 64 routed rows per local expert
+ * on average); *nsplit_w13 / *nsplit_w2 the K segments those GEMMs are
+ * given (1: K whole, bf16 h / y), *part_rows the rows of the partial
+ * slabs (0 without a cut), *lanes the chunk lanes (2 with two chunks or
+ * more).  Any output pointer may be NULL. */
+int moe_forward_plan_info(const moe_problem* p, int32_t* small_tiles, int32_t* nsplit_w13, int32_t* nsplit_w2,
+                          int64_t* part_rows, int32_t* lanes);
+
 /* The whole layer, chunked over M [P20392 Purpose]: for each chunk of
  * chunk_size tokens (the last one may be short) it runs input quant, count,
  * permute, GEMM(w13), SiLU-mul requant, GEMM(w2) and unpermute into the
@@ -244,7 +299,14 @@ int moe_unpermute_weight_reduce(const uint16_t* y, int64_t y_rows, const int32_t
  * [Eg] or NULL, w13 [El,2N,K] e4m3, w13_s [El,2N/128,K/128] f32, w2 [El,K,N]
  * e4m3, w2_s [El,K/128,N/128] f32, out [M,K] bf16, workspace >=
  * moe_forward_workspace_size(p).  per_chunk_counts: NULL or device
- * [num_chunks, El] int32 receiving each chunk's counts. */
+ * [num_chunks, El] int32 receiving each chunk's counts.
+ * Chunks of at most 64 routed rows per expert take the small-tile GEMMs
+ * (moe_forward_plan_info).  With two chunks or more, consecutive chunks
+ * alternate between two copies of the workspace slices and two library
+ * streams (created on the first such call on a device and kept), which wait
+ * for the work enqueued on `stream` before the call, and on which `stream`
+ * waits after it: every chunk computes what it computes alone, and work
+ * enqueued on `stream` afterwards sees the whole output. */
 int moe_forward_chunked(const moe_problem* p, const uint16_t* x, const int32_t* topk_ids,
                         const float* topk_weights, const int32_t* expert_map, const uint8_t* w13,
                         const float* w13_s, const uint8_t* w2, const float* w2_s, uint16_t* out,

@@ -86,6 +86,25 @@ def valid_rows(offsets: np.ndarray, counts: np.ndarray) -> np.ndarray:
                           + [np.zeros(0, np.int64)]).astype(np.int64)
 
 
+def partial_rows(part: torch.Tensor, info: torch.Tensor, offsets: np.ndarray, counts: np.ndarray,
+                 cap: int) -> np.ndarray:
+    """bf16 bits [cap, n] of the rows a small-tile GEMM left as partial slabs
+    part [nsplit, part_rows, n]: the fp32 sum of the first S = info[0] slabs
+    in slab order, rounded to nearest-even bf16, at the valid rows (place v
+    is the v-th valid row in expert order); the other rows are 0."""
+    p = host(part)
+    S = int(host(info)[0])
+    assert 1 <= S <= p.shape[0], f"segment count {S} outside 1..{p.shape[0]}"
+    acc = p[0].astype(np.float32).copy()
+    for sg in range(1, S):
+        acc = (acc + p[sg]).astype(np.float32)
+    bits = torch.from_numpy(acc).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    rows = valid_rows(offsets, counts)
+    out = np.zeros((cap, p.shape[2]), np.uint16)
+    out[rows] = bits[:len(rows)]
+    return out
+
+
 def bf16_ulp(v: np.ndarray) -> np.ndarray:
     """bf16 spacing at |v| (as float64)."""
     a = np.abs(np.asarray(v, np.float64)).astype(np.float32)

@@ -205,6 +205,30 @@ def test_layer_rejects_bad_weights(bad, exc, match):
         moe.MoeLayer(w13, w13_s, w2, w2_s, Eg, emap)
 
 
+def test_small_gemm_and_partial_wrappers_check_before_calling():
+    t = lambda shape, dt: torch.zeros(shape, dtype=dt)
+    u8, f32, i32, b16 = torch.uint8, torch.float32, torch.int32, torch.int16
+    a, a_s = t((100, 256), u8), t((100, 2), f32)
+    w, w_s = t((4, 512, 256), u8), t((4, 4, 2), f32)
+    offs, cnt = t((5,), i32), t((4,), i32)
+    with pytest.raises(ValueError, match="out"):
+        moe.moe_grouped_gemm_fp8_small(a, a_s, w, w_s, offs, cnt, out=t((100, 256), b16))
+    with pytest.raises(ValueError, match="part"):
+        moe.moe_grouped_gemm_fp8_small(a, a_s, w, w_s, offs, cnt, part=t((3, 50, 512), f32), nsplit=2,
+                                       info=t((1,), i32))
+    with pytest.raises(ValueError, match="info"):
+        moe.moe_grouped_gemm_fp8_small(a, a_s, w, w_s, offs, cnt, part=t((2, 50, 512), f32), nsplit=2)
+    with pytest.raises(ValueError, match="q"):
+        moe.moe_act_quant_partials(t((2, 50, 512), f32), t((1,), i32), 256, 100, offs, cnt, t((100, 128), u8),
+                                   t((100, 2), f32))
+    with pytest.raises(TypeError, match="part"):
+        moe.moe_unpermute_partials(t((2, 50, 256), b16), t((1,), i32), offs, cnt, 100, t((8, 4), i32),
+                                   t((8, 4), f32), 0, t((8, 256), b16))
+    with pytest.raises(ValueError, match="out"):
+        moe.moe_unpermute_partials(t((2, 50, 256), f32), t((1,), i32), offs, cnt, 100, t((8, 4), i32),
+                                   t((8, 4), f32), 0, t((8, 128), b16))
+
+
 def test_op_wrappers_check_before_calling():
     cap, k_in, El, n_out = 300, 256, 3, 384
     a = torch.zeros((cap, k_in), dtype=torch.uint8)
@@ -242,12 +266,52 @@ def test_forward_workspace_slices_leave_guard_bands():
               moe.problem(1, 128, 128, 1, 4, 4)):
         sl = moe.moe_forward_workspace_slices(p)
         total = moe.moe_forward_workspace_size(p)
-        assert len(sl) == 8
+        lanes = moe.moe_forward_plan_info(p)["lanes"]
+        assert len(sl) == 10 * lanes
         ends = [o + n for o, n in sl]
         nxt = [o for o, _ in sl[1:]] + [total]
-        for (o, n), e, q in zip(sl, ends, nxt):
-            assert o % 256 == 0 and n > 0
+        for i, ((o, n), e, q) in enumerate(zip(sl, ends, nxt)):
+            # the partial sums (slice 8 of a lane) are empty when neither GEMM cuts K
+            assert o % 256 == 0 and (n > 0 or i % 10 == 8)
             assert q - e >= 256, "no guard band after a slice"
+        if lanes == 2:   # the second lane repeats the first's layout
+            assert [n for _, n in sl[10:]] == [n for _, n in sl[:10]]
+            assert sl[10][0] - sl[0][0] == total // 2
+    # 64-token chunks cut the gate/up GEMM's K; 1-group K and N cut neither
+    assert moe.moe_forward_workspace_slices(moe.problem(8192, 2048, 768, 8, 128, 64, chunk_size=64))[8][1] > 0
+    assert moe.moe_forward_workspace_slices(moe.problem(1, 128, 128, 1, 4, 4))[8][1] == 0
+
+
+@pytest.mark.parametrize("args,want", [
+    # 64 tokens, topk 4, 64 local experts: small tiles, w13 K (16 groups) in two, w2 K (6 groups) whole
+    (dict(M=64, K=2048, N=768, topk=4, Eg=128, El=64), dict(small_tiles=True, nsplit_w13=2, nsplit_w2=1,
+                                                          part_rows=256, lanes=1)),
+    # 8192 tokens in chunks of 64: the same per chunk, and two lanes
+    (dict(M=8192, K=2048, N=768, topk=8, Eg=128, El=64, chunk_size=64),
+     dict(small_tiles=True, nsplit_w13=2, nsplit_w2=1, part_rows=512, lanes=2)),
+    # a down projection of 16 groups is cut too
+    (dict(M=64, K=2048, N=2048, topk=8, Eg=64, El=64), dict(small_tiles=True, nsplit_w13=2, nsplit_w2=2,
+                                                          part_rows=512, lanes=1)),
+    # 4096 tokens, topk 8, 128 experts (256 rows each): the 128/256-row GEMMs, K whole
+    (dict(M=4096, K=2048, N=768, topk=8, Eg=128, El=128), dict(small_tiles=False, nsplit_w13=1, nsplit_w2=1,
+                                                             part_rows=0, lanes=1)),
+    # tiny K: small tiles without a cut
+    (dict(M=64, K=256, N=128, topk=2, Eg=8, El=8), dict(small_tiles=True, nsplit_w13=1, nsplit_w2=1,
+                                                      part_rows=0, lanes=1)),
+])
+def test_forward_plan_info(args, want):
+    a = dict(args)
+    p = moe.problem(a.pop("M"), a.pop("K"), a.pop("N"), a.pop("topk"), a.pop("Eg"), a.pop("El"), **a)
+    assert moe.moe_forward_plan_info(p) == want
+
+
+def test_noalloc_plan_stays_in_one_lane():
+    # chunked problems need two lanes' slices from moe_forward_chunked but one
+    # from the scratch of the no-alloc entry: its size check uses one lane
+    p = moe.problem(8192, 2048, 768, 8, 128, 64, chunk_size=64)
+    assert moe.moe_forward_plan_info(p)["lanes"] == 2
+    sl = moe.moe_forward_workspace_slices(p)
+    assert moe.moe_forward_workspace_size(p) == 2 * sl[10][0]
 
 
 def test_noalloc_forward_rejects_a_problem_beyond_the_scratch():
@@ -262,5 +326,7 @@ def test_noalloc_forward_rejects_a_problem_beyond_the_scratch():
     assert L.moe_forward_chunked_noalloc(C.byref(big), *args) == 3
     assert b"scratch" in L.moe_last_error()
     # the same problem in chunks small enough for the array passes the size check
+    # (one lane of slices: the no-alloc entry runs the chunks in order)
     small = moe.problem(65536, 2048, 768, 8, 128, 128, chunk_size=1024)
-    assert moe.moe_forward_workspace_size(small) <= moe._lib.moe_noalloc_scratch_bytes()
+    one_lane = moe.moe_forward_workspace_size(small) // moe.moe_forward_plan_info(small)["lanes"]
+    assert one_lane <= moe._lib.moe_noalloc_scratch_bytes()

@@ -37,7 +37,7 @@ import oracle
 import unpermute_count_expert_amd as moe
 from unpermute_count_expert_amd import generators as gen
 from unpermute_count_expert_amd.pipeline import StepBuffers, run_steps, step_ops
-from tests.gpu_helpers import (ATOL, RTOL, announce, bf16_f64, bf16_ulp, dev, filled, host, record,
+from tests.gpu_helpers import (ATOL, RTOL, announce, bf16_f64, bf16_ulp, dev, filled, host, partial_rows, record,
                                tight_excess, valid_rows)
 
 pytestmark = pytest.mark.gpu
@@ -69,6 +69,21 @@ def _forward(layer, d, M, chunk_size, on_input, want_counts=False):
     out = layer.forward(d["x"], d["ids"], d["w"], chunk_size=chunk_size, apply_on_input=on_input,
                         per_chunk_counts=pcc)
     return host(out, bf16=True), (host(pcc) if want_counts else None)
+
+
+def _ops_by_chunk(layer, d, M, cs, on_input):
+    """The op-by-op pipeline run on each chunk in turn, under the chunked
+    forward's plan; the concatenated outputs (bf16 bits)."""
+    T = d["ids"].shape[1]
+    pp = layer.problem(M, T, cs, on_input)
+    outs, bufs = [], {}
+    for t0 in range(0, M, cs):
+        Mc = min(cs, M - t0)
+        if Mc not in bufs:
+            bufs[Mc] = StepBuffers(layer, Mc, T, plan_problem=pp)
+        b = run_steps(layer, d["x"][t0:t0 + Mc], d["ids"][t0:t0 + Mc], d["w"][t0:t0 + Mc], on_input, bufs[Mc])
+        outs.append(host(b.out, bf16=True))
+    return np.concatenate(outs)
 
 
 def _sample(M, rng, n):
@@ -138,6 +153,12 @@ def check_layer(cfg, on_input, n_sample_rows=512, n_sample_tokens=48):
     g = {k: host(getattr(b, k)) for k in ("a_q", "a_s", "a_perm", "a_perm_s", "counts", "offsets", "inv_perm",
                                           "row_src", "act_q", "act_s", "count_only")}
     g["h"], g["y"], g["out"] = host(b.h, bf16=True), host(b.y, bf16=True), host(b.out, bf16=True)
+    # where the forward's plan cuts K of a GEMM, h (y) is the bf16 of its
+    # partial slabs' sum, which the requant (unpermute) forms itself
+    if b.part13 is not None:
+        g["h"] = partial_rows(b.part13, b.info13, g["offsets"], g["counts"], b.cap)
+    if b.part2 is not None:
+        g["y"] = partial_rows(b.part2, b.info2, g["offsets"], g["counts"], b.cap)
     rng = np.random.default_rng(cfg.seed + 1000 * on_input)
     name = f"{cfg.name}{'_on' if on_input else ''}"
 
@@ -181,15 +202,27 @@ def check_layer(cfg, on_input, n_sample_rows=512, n_sample_tokens=48):
     np.testing.assert_array_equal(g["act_q"][rows], q)
     np.testing.assert_array_equal(g["act_s"][rows], s)
 
-    # -- GEMM w13 fused with the SiLU-mul requant: the same bits as the chain
-    #    (h never leaves the kernel), on every valid row
+    # -- the plain grouped GEMM (whole K, 128/256-row tiles): bit-exact with
+    #    the small-tile GEMM without a K cut; within the tolerance otherwise
+    hp = filled(tuple(b.h.shape), "bf16", 0)
+    moe._lib.moe_grouped_gemm_fp8(b.a_perm, b.a_perm_s, layer.w13, layer.w13_s, b.offsets, b.counts, hp)
+    if b.part13 is None:
+        np.testing.assert_array_equal(host(hp, bf16=True)[rows], g["h"][rows])
+    else:
+        _tight(name, "plain-GEMM h", host(hp, bf16=True)[sr], h_ref)
+    cq, cs_ = filled(tuple(b.act_q.shape), torch.uint8, 0), filled(tuple(b.act_s.shape), torch.float32, 0.0)
+    moe._lib.moe_act_quant(hp, N, moe.MOE_ACT_SILU_MUL, cq, cs_, b.offsets, b.counts, El)
+    cq, cs_ = host(cq), host(cs_)
+
+    # -- GEMM w13 fused with the SiLU-mul requant: the same bits as the plain
+    #    chain (h never leaves the kernel), on every valid row
     fq = filled(tuple(b.act_q.shape), torch.uint8, 0xA5)
     fs = filled(tuple(b.act_s.shape), torch.float32, -7.0)
     moe._lib.moe_grouped_gemm_fp8_act_quant(b.a_perm, b.a_perm_s, layer.w13, layer.w13_s, b.offsets, b.counts,
                                             fq, fs)
     fq, fs = host(fq), host(fs)
-    np.testing.assert_array_equal(fq[rows], g["act_q"][rows])
-    np.testing.assert_array_equal(fs[rows], g["act_s"][rows])
+    np.testing.assert_array_equal(fq[rows], cq[rows])
+    np.testing.assert_array_equal(fs[rows], cs_[rows])
     pad = np.setdiff1d(np.arange(fq.shape[0]), rows)
     assert (fq[pad] == 0xA5).all() and (fs[pad] == -7.0).all(), "fused GEMM wrote a padding row"
     # ... and directly against the oracle (its exact GEMM, then its SiLU-mul
@@ -199,7 +232,7 @@ def check_layer(cfg, on_input, n_sample_rows=512, n_sample_tokens=48):
     # differ in a few codes (flips), at most 1% of codes overall
     q_or, s_or = oracle.silu_mul_quant(h_ref)
     ng = N // 128
-    hg = (g["h"][sr] == h_ref).reshape(len(sr), 2, ng, 128).all(axis=(1, 3))   # [rows, groups]: h alike
+    hg = (host(hp, bf16=True)[sr] == h_ref).reshape(len(sr), 2, ng, 128).all(axis=(1, 3))   # [rows, groups]: h alike
     q_f = fq[sr].reshape(len(sr), ng, 128)
     np.testing.assert_array_equal(q_f[hg], q_or.reshape(len(sr), ng, 128)[hg])
     np.testing.assert_array_equal(fs[sr][hg], s_or[hg])
@@ -213,14 +246,21 @@ def check_layer(cfg, on_input, n_sample_rows=512, n_sample_tokens=48):
     # -- unpermute of the GPU's y: bit-exact
     np.testing.assert_array_equal(g["out"], oracle.unpermute(g["y"], g["inv_perm"], inp.topk_weights, on_input))
 
-    # -- the fused entry point computes the same bits; chunking changes nothing
+    # -- the forward computes the same bits as the ops; chunked, it equals the
+    #    ops run chunk by chunk under the chunked plan (where no chunk cuts K
+    #    differently, the unchunked forward itself)
     full, pcc = _forward(layer, d, M, 0, on_input, want_counts=True)
     np.testing.assert_array_equal(full, g["out"])
     np.testing.assert_array_equal(pcc[0], counts)
+    chunked = None
     if cfg.chunk_size and cfg.chunk_size < M:
-        chunked, pcc = _forward(layer, d, M, cfg.chunk_size, on_input, want_counts=True)
-        np.testing.assert_array_equal(chunked, full)
         cs = cfg.chunk_size
+        chunked, pcc = _forward(layer, d, M, cs, on_input, want_counts=True)
+        np.testing.assert_array_equal(chunked, _ops_by_chunk(layer, d, M, cs, on_input))
+        pc = moe.moe_forward_plan_info(layer.problem(M, T, cs, on_input))
+        pf = moe.moe_forward_plan_info(layer.problem(M, T, 0, on_input))
+        if pc["nsplit_w13"] == pf["nsplit_w13"] == 1 and pc["nsplit_w2"] == pf["nsplit_w2"] == 1:
+            np.testing.assert_array_equal(chunked, full)
         for c in range(pcc.shape[0]):
             np.testing.assert_array_equal(
                 pcc[c], oracle.count(inp.topk_ids[c * cs:(c + 1) * cs], inp.expert_map, cfg.Eg, El)[0])
@@ -283,6 +323,12 @@ def check_layer(cfg, on_input, n_sample_rows=512, n_sample_tokens=48):
     assert n_bad <= MAX_E2E_EXCESS_FRAC * n_out, (
         f"{name}: {n_bad} of {n_out} outputs beyond 1e-3 + 1e-2|ref| of the all-oracle layer "
         f"(worst {worst_e2e:.3g}x)")
+    if chunked is not None:
+        # the chunked forward against the same all-oracle outputs, to the same cap
+        n_bad_c, _, worst_c = tight_excess(chunked[toks], ref)
+        record(case=name + " chunked", e2e_outputs_beyond_tol=f"{n_bad_c}/{n_out}", e2e_worst=round(worst_c, 3))
+        assert n_bad_c <= MAX_E2E_EXCESS_FRAC * n_out, (
+            f"{name} chunked: {n_bad_c} of {n_out} outputs beyond 1e-3 + 1e-2|ref| of the all-oracle layer")
 
 
 CASES = [

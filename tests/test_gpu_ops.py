@@ -15,7 +15,7 @@ import torch
 import oracle
 import unpermute_count_expert_amd as moe
 from unpermute_count_expert_amd import generators as gen
-from tests.gpu_helpers import (DEV, announce, assert_bf16_close, assert_gemm_close, dev, empty, filled, host,
+from tests.gpu_helpers import (DEV, announce, assert_bf16_close, assert_gemm_close, dev, empty, filled, host, partial_rows,
                                valid_rows)
 
 pytestmark = pytest.mark.gpu
@@ -496,6 +496,106 @@ def test_gemm_full_grid_every_row(El, hi, n_out, k_in, tile, data):
     else:
         assert_bf16_close(out[rows], ref[rows], "gemm full grid")
     assert np.all(out[np.setdiff1d(np.arange(cap), rows)] == 0x7FC1)
+
+
+def _small_operands(rng, El, hi, n_out, k_in, align=16):
+    cnt = rng.integers(0, hi + 1, El).astype(np.int32)
+    cnt[::7] = 0
+    offs, cnt = _segments(cnt, align)
+    cap = int(offs[-1]) + 3
+    a, a_s = oracle.act_quant_identity(gen.bf16_bits(rng.standard_normal((cap, k_in), dtype=np.float32)))
+    w, w_s = gen.block_weights(rng, El, n_out, k_in)
+    return a, a_s, w, w_s, offs, cnt, cap
+
+
+def _num_cus():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+@pytest.mark.parametrize("El,hi,n_out,k_in,nsplit", [
+    (64, 4, 1536, 2048, 2),     # 64-token decode chunk, gate/up: K cut in two
+    (64, 4, 1536, 2048, 8),     # eight segments of two groups
+    (16, 90, 512, 1024, 4),     # experts past one 64-row tile
+    (8, 3, 256, 2048, 1),       # one slab: whole-K sums
+    (40, 20, 768, 768, 3),      # down-projection K (6 groups) cut in three
+    (300, 30, 2048, 512, 2),    # tiles enough for four rounds: K kept whole
+])
+def test_small_gemm_and_partials(El, hi, n_out, k_in, nsplit):
+    """moe_grouped_gemm_fp8_small on layer-like data: without part, the bits
+    of moe_grouped_gemm_fp8 on every valid row and no other row written;
+    with part, info reports the cut (nsplit while the 64-row tiles fill
+    fewer than four rounds of the CUs, else 1), the slabs' sum in slab
+    order rounded to bf16 is within 1e-3 + 1e-2|ref| of the oracle's exact
+    GEMM (and is the plain GEMM's bits with one slab), and no slab row past
+    the valid rows is written."""
+    announce("small gemm", El, hi, n_out, k_in, nsplit)
+    rng = np.random.default_rng(El * 7 + hi + nsplit)
+    a, a_s, w, w_s, offs, cnt, cap = _small_operands(rng, El, hi, n_out, k_in)
+    rows = valid_rows(offs, cnt)
+    plain = _gpu_gemm(a, a_s, w, w_s, offs, cnt)
+    A, As, W, Ws, O, Cn = dev(a), dev(a_s), dev(w), dev(w_s), dev(offs), dev(cnt)
+    out = filled((cap, n_out), "bf16", 0x7FC1)
+    moe.moe_grouped_gemm_fp8_small(A, As, W, Ws, O, Cn, out=out)
+    o = host(out, bf16=True)
+    np.testing.assert_array_equal(o[rows], plain[rows])
+    assert np.all(o[np.setdiff1d(np.arange(cap), rows)] == 0x7FC1), "a row that is not valid was written"
+    pr = len(rows) + 5
+    part = filled((nsplit, pr, n_out), torch.float32, -3.0)
+    info = filled((1,), torch.int32, -1)
+    moe.moe_grouped_gemm_fp8_small(A, As, W, Ws, O, Cn, part=part, nsplit=nsplit, info=info)
+    tiles = int(((cnt + 63) // 64).sum()) * -(-n_out // 256)
+    want = nsplit if tiles < 4 * _num_cus() else 1
+    assert int(host(info)[0]) == want
+    h = partial_rows(part, info, offs, cnt, cap)
+    ref = oracle.grouped_gemm(a, a_s, w, w_s, offs, cnt)
+    assert_bf16_close(h[rows], ref[rows], "small gemm partials")
+    if want == 1:
+        np.testing.assert_array_equal(h[rows], plain[rows])
+    p = host(part)
+    assert np.all(p[:want, len(rows):] == -3.0), "a slab row past the valid rows was written"
+
+
+@pytest.mark.parametrize("El,hi,n,nsplit", [(64, 4, 768, 2), (16, 90, 256, 4), (8, 3, 128, 8), (30, 10, 384, 1)])
+def test_act_quant_and_unpermute_from_partials(El, hi, n, nsplit):
+    """The SiLU-mul requant and the unpermute that read the small GEMM's
+    partial slabs give the bits of moe_act_quant / the unpermute run on the
+    slabs' bf16 sum (formed on the host in slab order), on every valid row
+    and token, and leave rows that are not valid alone."""
+    announce("partials consumers", El, hi, n, nsplit)
+    rng = np.random.default_rng(El + hi + n + nsplit)
+    k_in = 1024
+    # the gate/up GEMM: 2n outputs as partial slabs
+    a, a_s, w, w_s, offs, cnt, cap = _small_operands(rng, El, hi, 2 * n, k_in)
+    rows = valid_rows(offs, cnt)
+    A, As, W, Ws, O, Cn = dev(a), dev(a_s), dev(w), dev(w_s), dev(offs), dev(cnt)
+    part = filled((nsplit, max(len(rows), 1), 2 * n), torch.float32, 0.0)
+    info = filled((1,), torch.int32, -1)
+    moe.moe_grouped_gemm_fp8_small(A, As, W, Ws, O, Cn, part=part, nsplit=nsplit, info=info)
+    h = partial_rows(part, info, offs, cnt, cap)
+    q1, s1 = filled((cap, n), torch.uint8, 0xA5), filled((cap, n // 128), torch.float32, -7.0)
+    moe.moe_act_quant_partials(part, info, n, cap, O, Cn, q1, s1)
+    q2, s2 = filled((cap, n), torch.uint8, 0), filled((cap, n // 128), torch.float32, 0.0)
+    moe.moe_act_quant(dev(h), n, moe.MOE_ACT_SILU_MUL, q2, s2, O, Cn, El)
+    q1, s1, q2, s2 = host(q1), host(s1), host(q2), host(s2)
+    np.testing.assert_array_equal(q1[rows], q2[rows])
+    np.testing.assert_array_equal(s1[rows], s2[rows])
+    pad = np.setdiff1d(np.arange(cap), rows)
+    assert (q1[pad] == 0xA5).all() and (s1[pad] == -7.0).all(), "the requant wrote a row that is not valid"
+    # the unpermute: every valid row is one (token, k) pair, some pairs -1
+    topk = 4
+    Mc = max(1, -(-len(rows) // topk) + 2)
+    inv = np.full(Mc * topk, -1, np.int32)
+    slots = rng.choice(Mc * topk, len(rows), replace=False)
+    inv[slots] = rng.permutation(rows).astype(np.int32)
+    inv = inv.reshape(Mc, topk)
+    tw = rng.uniform(0.05, 1.0, (Mc, topk)).astype(np.float32)
+    K = 2 * n   # the slabs' width serves as the output width
+    for on_input in (0, 1):
+        o1 = filled((Mc, K), "bf16", 0x7FC1)
+        moe.moe_unpermute_partials(part, info, O, Cn, cap, dev(inv), dev(tw), on_input, o1)
+        o2 = filled((Mc, K), "bf16", 0)
+        moe.moe_unpermute_weight_reduce(dev(h), dev(inv), dev(tw), on_input, o2)
+        np.testing.assert_array_equal(host(o1, bf16=True), host(o2, bf16=True))
 
 
 @pytest.mark.parametrize("El,max_tokens,n_out,k_in,tile", [

@@ -41,7 +41,9 @@ EXPORTS = ["moe_status_string", "moe_last_error", "moe_max_rows", "moe_grouped_g
            "moe_permute_workspace_size", "moe_count", "moe_permute", "moe_grouped_gemm_fp8",
            "moe_grouped_gemm_fp8_act_quant", "moe_act_quant", "moe_quant_permute", "moe_unpermute_weight_reduce",
            "moe_forward_chunked", "moe_forward_chunked_noalloc", "moe_noalloc_scratch_bytes", "moe_hbm_stream",
-           "moe_batched_workspace_size", "moe_experts_batched_masked", "moe_grouped_gemm_fp8_weight_reduce"]
+           "moe_batched_workspace_size", "moe_experts_batched_masked", "moe_grouped_gemm_fp8_weight_reduce",
+           "moe_grouped_gemm_fp8_small", "moe_act_quant_partials", "moe_unpermute_partials",
+           "moe_forward_plan_info"]
 
 _lib = None
 
@@ -71,6 +73,11 @@ def load() -> C.CDLL:
         L.moe_grouped_gemm_fp8_act_quant.argtypes = [P, P, P, P, P, P, I32, I64, I32, I32, P, P, P]
         L.moe_act_quant.argtypes = [P, I64, I32, I32, P, P, I32, P, P, P]
         L.moe_unpermute_weight_reduce.argtypes = [P, I64, P, P, I64, I32, I32, I32, P, P]
+        L.moe_grouped_gemm_fp8_small.argtypes = [P, P, P, P, P, P, I32, I64, I32, I32, P, P, I64, I32, P, P]
+        L.moe_act_quant_partials.argtypes = [P, P, I64, I32, I64, I32, P, P, I32, P, P, P]
+        L.moe_unpermute_partials.argtypes = [P, P, I64, I32, P, P, I32, I64, P, P, I64, I32, I32, I32, P, P]
+        L.moe_forward_plan_info.argtypes = [C.POINTER(MoeProblem), C.POINTER(I32), C.POINTER(I32),
+                                            C.POINTER(I32), C.POINTER(I64), C.POINTER(I32)]
         L.moe_forward_chunked.argtypes = [C.POINTER(MoeProblem), P, P, P, P, P, P, P, P, P, P, SZ,
                                           P, P]
         L.moe_forward_chunked_noalloc.argtypes = [C.POINTER(MoeProblem), P, P, P, P, P, P, P, P, P, P, P]
@@ -183,11 +190,13 @@ def moe_forward_workspace_slices(p: MoeProblem):
     """[(offset, bytes)] of the slices moe_forward_chunked carves from its
     workspace; the bytes between a slice's end and the next offset are a
     guard band no kernel touches."""
-    offs = (C.c_size_t * 16)()
-    lens = (C.c_size_t * 16)()
     n = C.c_int32(0)
-    _check(load().moe_forward_workspace_slices(C.byref(p), offs, lens, 16, C.byref(n)), "moe_forward_workspace_slices")
-    return [(int(offs[i]), int(lens[i])) for i in range(min(n.value, 16))]
+    _check(load().moe_forward_workspace_slices(C.byref(p), None, None, 0, C.byref(n)), "moe_forward_workspace_slices")
+    offs = (C.c_size_t * max(n.value, 1))()
+    lens = (C.c_size_t * max(n.value, 1))()
+    _check(load().moe_forward_workspace_slices(C.byref(p), offs, lens, n.value, C.byref(n)),
+           "moe_forward_workspace_slices")
+    return [(int(offs[i]), int(lens[i])) for i in range(n.value)]
 
 
 def moe_permute_workspace_size(Mc: int, topk: int, El: int) -> int:
@@ -311,6 +320,72 @@ def moe_unpermute_weight_reduce(y, inv_perm, topk_weights, apply_on_input, out, 
     _check(load().moe_unpermute_weight_reduce(_ptr(y), y_rows, _ptr(inv_perm), _ptr(topk_weights), Mc, K,
                                               topk, apply_on_input, _ptr(out), _stream(stream)),
            "moe_unpermute_weight_reduce")
+
+
+def moe_grouped_gemm_fp8_small(a, a_s, w, w_s, expert_offsets, counts, out=None, part=None, nsplit=1, info=None,
+                               stream=None):
+    """The small-chunk GEMM: bf16 out (part None), or fp32 partial slabs
+    part [nsplit, part_rows, n_out] and the segment count used in info [1]."""
+    cap_rows, k_in, El, n_out = _check_gemm_operands(a, a_s, w, w_s, expert_offsets, counts)
+    if part is None:
+        check_arg(out, "out", BF16, (cap_rows, n_out))
+        part_rows = 0
+    else:
+        check_arg(part, "part", F32, (nsplit, None, n_out))
+        check_arg(info, "info", I32, (1,), min_rows=1)
+        part_rows = part.shape[1]
+    check_device(a, a_s, w, w_s, expert_offsets, counts, out, part, info)
+    _check(load().moe_grouped_gemm_fp8_small(_ptr(a), _ptr(a_s), _ptr(w), _ptr(w_s), _ptr(expert_offsets),
+                                             _ptr(counts), El, cap_rows, n_out, k_in, _ptr(out), _ptr(part),
+                                             part_rows, nsplit, _ptr(info), _stream(stream)),
+           "moe_grouped_gemm_fp8_small")
+
+
+def moe_act_quant_partials(part, info, n, rows, expert_offsets, counts, q, q_s, stream=None):
+    """SiLU-mul requant of h given as the small GEMM's partial slabs
+    part [nsplit, part_rows, 2n]; q [rows, n], q_s [rows, n/128]."""
+    check_arg(part, "part", F32, (None, None, 2 * n))
+    nsplit, part_rows, _ = part.shape
+    check_arg(info, "info", I32, (1,))
+    check_arg(expert_offsets, "expert_offsets", I32, (None,))
+    El = expert_offsets.shape[0] - 1
+    check_arg(counts, "counts", I32, (El,))
+    check_arg(q, "q", E4M3, (rows, n))
+    check_arg(q_s, "q_s", F32, (rows, n // 128))
+    check_device(part, info, expert_offsets, counts, q, q_s)
+    _check(load().moe_act_quant_partials(_ptr(part), _ptr(info), part_rows, nsplit, rows, n, _ptr(expert_offsets),
+                                         _ptr(counts), El, _ptr(q), _ptr(q_s), _stream(stream)),
+           "moe_act_quant_partials")
+
+
+def moe_unpermute_partials(part, info, expert_offsets, counts, y_rows, inv_perm, topk_weights, apply_on_input, out,
+                           stream=None):
+    """Unpermute with weight-and-reduce of y given as the small GEMM's partial
+    slabs part [nsplit, part_rows, K]; out [Mc, K]."""
+    check_arg(part, "part", F32, (None, None, None))
+    nsplit, part_rows, K = part.shape
+    check_arg(info, "info", I32, (1,))
+    check_arg(expert_offsets, "expert_offsets", I32, (None,))
+    El = expert_offsets.shape[0] - 1
+    check_arg(counts, "counts", I32, (El,))
+    check_arg(inv_perm, "inv_perm", I32, (None, None))
+    Mc, topk = inv_perm.shape
+    check_arg(topk_weights, "topk_weights", F32, (Mc, topk), optional=bool(apply_on_input))
+    check_arg(out, "out", BF16, (Mc, K))
+    check_device(part, info, expert_offsets, counts, inv_perm, topk_weights, out)
+    _check(load().moe_unpermute_partials(_ptr(part), _ptr(info), part_rows, nsplit, _ptr(expert_offsets),
+                                         _ptr(counts), El, y_rows, _ptr(inv_perm), _ptr(topk_weights), Mc, K, topk,
+                                         apply_on_input, _ptr(out), _stream(stream)),
+           "moe_unpermute_partials")
+
+
+def moe_forward_plan_info(p: MoeProblem) -> dict:
+    """How moe_forward_chunked runs p: small_tiles, nsplit_w13, nsplit_w2,
+    part_rows, lanes."""
+    v = [C.c_int32(), C.c_int32(), C.c_int32(), C.c_int64(), C.c_int32()]
+    _check(load().moe_forward_plan_info(C.byref(p), *[C.byref(x) for x in v]), "moe_forward_plan_info")
+    return dict(small_tiles=bool(v[0].value), nsplit_w13=v[1].value, nsplit_w2=v[2].value, part_rows=v[3].value,
+                lanes=v[4].value)
 
 
 def check_forward_args(p: MoeProblem, x, topk_ids, topk_weights, expert_map, w13, w13_s, w2, w2_s, out,

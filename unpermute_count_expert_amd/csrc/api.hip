@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "moe.h"
 #include "moe_device.hpp"
@@ -87,6 +88,8 @@ size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
 //   bufAs  a_perm_s then act_s                         (fp32 scales)
 //   bufB   h [cap,2N], then y [cap,K]                  (bf16)
 //   small  counts, offsets, inv_perm, row_src, per-block histogram
+//   part   fp32 partial sums of a GEMM with K split, [S, pairs, n]
+//   info   the two split GEMMs' segment counts S
 // The input quantisation is fused into the permute's scatter, so no a_q /
 // a_s buffer exists.  Each buffer is dead before it is reused: GEMM w13
 // reads bufA and writes bufB, the SiLU-mul requant reads bufB and writes
@@ -94,16 +97,41 @@ size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
 // output never aliases the workspace.  Every slice is followed by a guard
 // band of kGuard bytes that no kernel touches, so a write past a slice's end
 // is visible to a caller that fills the workspace with a pattern first.
+//
+// Small chunks (at most 64 routed rows per expert on average) take the
+// GEMMs on 64-row tiles (launch_grouped_gemm_small).  Their tiles are too
+// few to spread evenly over the CUs (64 tokens, topk 8: ~300 tiles of w13
+// on 256 CUs, two rounds with the second a quarter full), so a GEMM whose K
+// holds 16 groups or more also cuts K into segments of at least 8 groups:
+// h (or y) then passes through part as fp32 partial sums, which the
+// SiLU-mul requant (or the unpermute) adds up in a fixed order, and bufB is
+// not used for it.  The cut is planned where the partials of the largest
+// chunk fit in kPartBudget bytes; the GEMM keeps K whole when its tiles
+// fill four rounds of the grid or more.
+//
+// Lanes: with two chunks or more, consecutive chunks alternate between two
+// copies of these slices (lane c % 2, the second at offset `one`) and two
+// library streams that fork from and join the caller's stream.  Chunk c + 1
+// then runs its kernels beside chunk c's: its permute and its GEMM's first
+// tiles fill the CUs that chunk c's last partial round of tiles, its
+// SiLU-mul requant and its unpermute leave idle.  Every chunk computes
+// exactly what it computes alone.
 constexpr size_t kGuard = 256;
-constexpr int kSlices = 8;
+constexpr int kSlices = 10;
+constexpr size_t kPartBudget = size_t(64) << 20;
 
 struct Plan {
     int64_t cs, cap, nblk;
-    size_t bufA, bufAs, bufB, counts, offsets, inv, rsrc, hist, total;
+    int lanes;               // 1, or 2 with two chunks or more
+    size_t one;              // bytes of one lane's slices
+    size_t bufA, bufAs, bufB, counts, offsets, inv, rsrc, hist, part, info, total;
+    bool small;              // the GEMMs on 64-row tiles
+    int64_t part_rows;       // pairs of the largest chunk, 0 without a split
+    int smax13, smax2;       // K segments of GEMM w13 and w2 (1: not split)
     size_t off[kSlices], len[kSlices];   // the slices above, in this order
 };
 
-Plan make_plan(const moe_problem& p) {
+Plan make_plan(const moe_problem& p, bool allow_lanes = true) {
     Plan pl{};
     pl.cs = (p.chunk_size <= 0 || p.chunk_size >= p.M) ? p.M : p.chunk_size;
     if (pl.cs < 1) pl.cs = 1;
@@ -112,6 +140,21 @@ Plan make_plan(const moe_problem& p) {
     const int64_t K = p.K, N = p.N, El = p.num_local_experts;
     const int64_t wA = K > N ? K : N;
     const int64_t wB = (2 * N > K ? 2 * N : K) * 2;
+    // the split: the segments of gemm_split_segments, fewer (still dividing
+    // K / 128) where the budget holds fewer partials
+    const int64_t pairs = pl.cs * p.topk;
+    pl.small = moe::gemm_small_chunk(pairs, (int)El);
+    auto segments = [&](int k_in, int64_t n) {
+        if (!pl.small) return 1;
+        const int64_t fit = (int64_t)(kPartBudget / ((size_t)pairs * (size_t)n * 4));
+        int sm = moe::gemm_split_segments(k_in);
+        while (sm > 1 && (sm > fit || (k_in / moe::kGroup) % sm != 0)) --sm;
+        return sm;
+    };
+    pl.smax13 = segments((int)K, 2 * N);
+    pl.smax2 = segments((int)N, K);
+    pl.part_rows = (pl.smax13 > 1 || pl.smax2 > 1) ? pairs : 0;
+    const int64_t part_w = (pl.smax13 * 2 * N > pl.smax2 * K) ? pl.smax13 * 2 * N : pl.smax2 * K;
     const size_t len[kSlices] = {
         (size_t)pl.cap * wA,                        // bufA
         (size_t)pl.cap * (wA / moe::kGroup) * 4,    // bufAs
@@ -121,6 +164,8 @@ Plan make_plan(const moe_problem& p) {
         (size_t)pl.cs * p.topk * 4,                 // inv_perm
         (size_t)pl.cap * 4,                         // row_src
         (size_t)pl.nblk * El * 4,                   // histogram
+        (size_t)pl.part_rows * part_w * 4,          // partial sums
+        (size_t)2 * 4,                              // split counts
     };
     size_t off = 0;
     for (int i = 0; i < kSlices; ++i) {
@@ -136,7 +181,11 @@ Plan make_plan(const moe_problem& p) {
     pl.inv = pl.off[5];
     pl.rsrc = pl.off[6];
     pl.hist = pl.off[7];
-    pl.total = off;
+    pl.part = pl.off[8];
+    pl.info = pl.off[9];
+    pl.one = off;
+    pl.lanes = (allow_lanes && p.M > pl.cs) ? 2 : 1;
+    pl.total = off * pl.lanes;
     return pl;
 }
 
@@ -203,10 +252,10 @@ int moe_forward_workspace_slices(const moe_problem* p, size_t* offsets, size_t* 
     REQUIRE(max_slices >= 0 && (max_slices == 0 || (offsets != nullptr && bytes != nullptr)),
             MOE_ERR_INVALID_ARG, "offsets / bytes are NULL");
     const Plan pl = make_plan(*p);
-    *num_slices = kSlices;
-    for (int i = 0; i < kSlices && i < max_slices; ++i) {
-        offsets[i] = pl.off[i];
-        bytes[i] = pl.len[i];
+    *num_slices = kSlices * pl.lanes;
+    for (int i = 0; i < kSlices * pl.lanes && i < max_slices; ++i) {
+        offsets[i] = (size_t)(i / kSlices) * pl.one + pl.off[i % kSlices];
+        bytes[i] = pl.len[i % kSlices];
     }
     return MOE_OK;
 }
@@ -470,16 +519,133 @@ int moe_unpermute_weight_reduce(const uint16_t* y, int64_t y_rows, const int32_t
     return MOE_OK;
 }
 
+int moe_grouped_gemm_fp8_small(const uint8_t* a, const float* a_s, const uint8_t* w, const float* w_s,
+                               const int32_t* expert_offsets, const int32_t* counts, int32_t El, int64_t cap_rows,
+                               int32_t n_out, int32_t k_in, uint16_t* out, float* part, int64_t part_rows,
+                               int32_t nsplit, int32_t* info, void* stream) {
+    REQUIRE(El >= 1 && El <= moe::kMaxLocalExperts, MOE_ERR_SHAPE, "El=%d outside [1,1024]", El);
+    REQUIRE(n_out > 0 && n_out % moe::kGroup == 0 && n_out <= 65536, MOE_ERR_SHAPE,
+            "n_out=%d is not a positive multiple of 128 up to 65536", n_out);
+    REQUIRE(k_in > 0 && k_in % moe::kGroup == 0 && k_in <= 65536, MOE_ERR_SHAPE,
+            "k_in=%d is not a positive multiple of 128 up to 65536", k_in);
+    REQUIRE(cap_rows >= 0 && cap_rows < (int64_t(1) << 31), MOE_ERR_SHAPE, "cap_rows=%lld", (long long)cap_rows);
+    if (part != nullptr) {
+        REQUIRE(nsplit >= 1 && nsplit <= 8 && (k_in / moe::kGroup) % nsplit == 0, MOE_ERR_SHAPE,
+                "nsplit=%d must be 1..8 and divide k_in/128=%d", nsplit, k_in / moe::kGroup);
+        REQUIRE(part_rows >= 1 && part_rows < (int64_t(1) << 31), MOE_ERR_SHAPE, "part_rows=%lld",
+                (long long)part_rows);
+        REQUIRE_PTR(info);
+    }
+    if (cap_rows == 0) return MOE_OK;
+    REQUIRE_PTR(a);
+    REQUIRE_PTR(a_s);
+    REQUIRE_PTR(w);
+    REQUIRE_PTR(w_s);
+    REQUIRE_PTR(expert_offsets);
+    REQUIRE_PTR(counts);
+    if (part == nullptr) REQUIRE_PTR(out);
+    int cus = 0;
+    int st = check_device(&cus);
+    if (st) return st;
+    HIP_OK(moe::launch_grouped_gemm_small(a, a_s, w, w_s, expert_offsets, counts, El, cap_rows, n_out, k_in, out,
+                                          part, part_rows, nsplit, info, cus, static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
+int moe_act_quant_partials(const float* part, const int32_t* info, int64_t part_rows, int32_t nsplit, int64_t rows,
+                           int32_t n, const int32_t* expert_offsets, const int32_t* counts, int32_t El, uint8_t* q,
+                           float* q_s, void* stream) {
+    REQUIRE(rows >= 0, MOE_ERR_SHAPE, "rows < 0");
+    REQUIRE(n > 0 && n % moe::kGroup == 0 && n <= 32768, MOE_ERR_SHAPE,
+            "n=%d is not a positive multiple of 128 up to 32768", n);
+    REQUIRE(El >= 1 && El <= moe::kMaxLocalExperts, MOE_ERR_SHAPE, "El=%d outside [1,1024]", El);
+    REQUIRE(nsplit >= 1 && nsplit <= 8, MOE_ERR_SHAPE, "nsplit=%d outside [1,8]", nsplit);
+    REQUIRE(part_rows >= 1 && part_rows < (int64_t(1) << 31), MOE_ERR_SHAPE, "part_rows=%lld", (long long)part_rows);
+    if (rows == 0) return MOE_OK;
+    REQUIRE_PTR(part);
+    REQUIRE_PTR(info);
+    REQUIRE_PTR(expert_offsets);
+    REQUIRE_PTR(counts);
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(q_s);
+    int st = check_device(nullptr);
+    if (st) return st;
+    HIP_OK(moe::launch_act_quant_part(part, info, part_rows, nsplit, rows, n, expert_offsets, counts, El, q, q_s,
+                                      rows, static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
+int moe_unpermute_partials(const float* part, const int32_t* info, int64_t part_rows, int32_t nsplit,
+                           const int32_t* expert_offsets, const int32_t* counts, int32_t El, int64_t y_rows,
+                           const int32_t* inv_perm, const float* topk_weights, int64_t Mc, int32_t K, int32_t topk,
+                           int32_t apply_on_input, uint16_t* out, void* stream) {
+    REQUIRE(Mc >= 0 && y_rows >= 0, MOE_ERR_SHAPE, "Mc / y_rows < 0");
+    REQUIRE(K > 0 && K % moe::kGroup == 0, MOE_ERR_SHAPE, "K=%d is not a positive multiple of 128", K);
+    REQUIRE(topk >= 1 && topk <= 256, MOE_ERR_SHAPE, "topk=%d outside [1,256]", topk);
+    REQUIRE(apply_on_input == 0 || apply_on_input == 1, MOE_ERR_INVALID_ARG, "apply_on_input=%d", apply_on_input);
+    REQUIRE(El >= 1 && El <= moe::kMaxLocalExperts, MOE_ERR_SHAPE, "El=%d outside [1,1024]", El);
+    REQUIRE(nsplit >= 1 && nsplit <= 8, MOE_ERR_SHAPE, "nsplit=%d outside [1,8]", nsplit);
+    REQUIRE(part_rows >= 1 && part_rows < (int64_t(1) << 31), MOE_ERR_SHAPE, "part_rows=%lld", (long long)part_rows);
+    if (Mc == 0) return MOE_OK;
+    REQUIRE_PTR(part);
+    REQUIRE_PTR(info);
+    REQUIRE_PTR(expert_offsets);
+    REQUIRE_PTR(counts);
+    REQUIRE_PTR(inv_perm);
+    REQUIRE_PTR(out);
+    if (!apply_on_input) REQUIRE_PTR(topk_weights);
+    REQUIRE(!overlaps(out, (size_t)Mc * K * 2, part, (size_t)nsplit * part_rows * K * 4), MOE_ERR_INVALID_ARG,
+            "out overlaps part");
+    int st = check_device(nullptr);
+    if (st) return st;
+    HIP_OK(moe::launch_unpermute_part(part, info, part_rows, nsplit, expert_offsets, counts, El, y_rows, inv_perm,
+                                      topk_weights, Mc, K, topk, apply_on_input, out,
+                                      static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
+int moe_forward_plan_info(const moe_problem* p, int32_t* small_tiles, int32_t* nsplit_w13, int32_t* nsplit_w2,
+                          int64_t* part_rows, int32_t* lanes) {
+    int st = check_problem(p);
+    if (st) return st;
+    const Plan pl = make_plan(*p);
+    if (small_tiles) *small_tiles = pl.small ? 1 : 0;
+    if (nsplit_w13) *nsplit_w13 = pl.part_rows > 0 ? pl.smax13 : 1;
+    if (nsplit_w2) *nsplit_w2 = pl.part_rows > 0 ? pl.smax2 : 1;
+    if (part_rows) *part_rows = pl.part_rows;
+    if (lanes) *lanes = pl.lanes;
+    return MOE_OK;
+}
+
 }  // extern "C"
 
 namespace {
 
-// The chunk loop of moe_forward_chunked over an already validated problem
-// and a workspace of at least make_plan(*p).total bytes.
-int forward_impl(const moe_problem& P, const Plan& pl, const uint16_t* x, const int32_t* topk_ids,
-                 const float* topk_weights, const int32_t* expert_map, const uint8_t* w13, const float* w13_s,
-                 const uint8_t* w2, const float* w2_s, uint16_t* out, uint8_t* ws, int32_t* per_chunk_counts,
-                 int cus, hipStream_t s) {
+// The two library streams of a device and the events that fork them from and
+// join them to the caller's stream; created on first use and kept.  The
+// mutex covers one call's enqueue: a wait on an event takes the event as last
+// recorded before the wait, so the next call may record it again.
+struct LaneStreams {
+    std::mutex mu;
+    bool ready = false;
+    hipStream_t s[2] = {nullptr, nullptr};
+    hipEvent_t fork = nullptr, join[2] = {nullptr, nullptr};
+};
+LaneStreams g_lanes[kMaxDevices];
+
+int lane_streams(LaneStreams** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice failed");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED_DEVICE, "device %d", dev);
+    *out = &g_lanes[dev];
+    return MOE_OK;
+}
+
+// Enqueues chunk c of the layer on stream s, with the slices of one lane at ws.
+int forward_chunk(const moe_problem& P, const Plan& pl, int64_t c, const uint16_t* x, const int32_t* topk_ids,
+                  const float* topk_weights, const int32_t* expert_map, const uint8_t* w13, const float* w13_s,
+                  const uint8_t* w2, const float* w2_s, uint16_t* out, uint8_t* ws, int32_t* per_chunk_counts,
+                  int cus, hipStream_t s) {
     uint8_t* bufA = ws + pl.bufA;
     float* bufAs = reinterpret_cast<float*>(ws + pl.bufAs);
     uint16_t* hy = reinterpret_cast<uint16_t*>(ws + pl.bufB);
@@ -488,29 +654,100 @@ int forward_impl(const moe_problem& P, const Plan& pl, const uint16_t* x, const 
     int32_t* inv = reinterpret_cast<int32_t*>(ws + pl.inv);
     int32_t* rsrc = reinterpret_cast<int32_t*>(ws + pl.rsrc);
     int32_t* hist = reinterpret_cast<int32_t*>(ws + pl.hist);
+    float* part = reinterpret_cast<float*>(ws + pl.part);
+    int32_t* info = reinterpret_cast<int32_t*>(ws + pl.info);
+    const bool split13 = pl.part_rows > 0 && pl.smax13 > 1;
+    const bool split2 = pl.part_rows > 0 && pl.smax2 > 1;
 
     const int64_t K = P.K, N = P.N, T = P.topk, El = P.num_local_experts;
     const int on_in = P.apply_router_weight_on_input;
-    const int64_t nchunks = (P.M + pl.cs - 1) / pl.cs;
-    for (int64_t c = 0; c < nchunks; ++c) {
-        const int64_t t0 = c * pl.cs;
-        const int64_t Mc = (t0 + pl.cs <= P.M) ? pl.cs : (P.M - t0);
-        const int32_t* ids_c = topk_ids + t0 * T;
-        const float* w_c = topk_weights + t0 * T;
-        // input quant fused into the permute's scatter
-        HIP_OK(moe::launch_quant_permute(x + t0 * K, ids_c, w_c, on_in, Mc, (int)K, (int)T, expert_map,
-                                         P.num_global_experts, (int)El, P.align, pl.cap, bufA, bufAs, counts,
-                                         offsets, inv, rsrc, hist,
-                                         per_chunk_counts ? per_chunk_counts + c * El : nullptr, s));
+    const int64_t t0 = c * pl.cs;
+    const int64_t Mc = (t0 + pl.cs <= P.M) ? pl.cs : (P.M - t0);
+    const int32_t* ids_c = topk_ids + t0 * T;
+    const float* w_c = topk_weights + t0 * T;
+    // input quant fused into the permute's scatter
+    HIP_OK(moe::launch_quant_permute(x + t0 * K, ids_c, w_c, on_in, Mc, (int)K, (int)T, expert_map,
+                                     P.num_global_experts, (int)El, P.align, pl.cap, bufA, bufAs, counts,
+                                     offsets, inv, rsrc, hist,
+                                     per_chunk_counts ? per_chunk_counts + c * El : nullptr, s));
+    if (pl.small) {
+        HIP_OK(moe::launch_grouped_gemm_small(bufA, bufAs, w13, w13_s, offsets, counts, (int)El, pl.cap,
+                                              (int)(2 * N), (int)K, hy, split13 ? part : nullptr, pl.part_rows,
+                                              pl.smax13, info, cus, s));
+    } else {
         HIP_OK(moe::launch_grouped_gemm(bufA, bufAs, w13, w13_s, offsets, counts, (int)El, pl.cap,
                                         (int)(2 * N), (int)K, hy, Mc * T, cus, s));
+    }
+    if (split13) {
+        HIP_OK(moe::launch_act_quant_part(part, info, pl.part_rows, pl.smax13, pl.cap, (int)N, offsets, counts,
+                                          (int)El, bufA, bufAs, Mc * T, s));
+    } else {
         HIP_OK(moe::launch_act_quant(hy, pl.cap, (int)N, moe::MOE_ACT_SILU_MUL_K, offsets, counts, (int)El,
                                      bufA, bufAs, Mc * T, s));
+    }
+    if (pl.small) {
+        HIP_OK(moe::launch_grouped_gemm_small(bufA, bufAs, w2, w2_s, offsets, counts, (int)El, pl.cap, (int)K,
+                                              (int)N, hy, split2 ? part : nullptr, pl.part_rows, pl.smax2, info + 1,
+                                              cus, s));
+    } else {
         HIP_OK(moe::launch_grouped_gemm(bufA, bufAs, w2, w2_s, offsets, counts, (int)El, pl.cap, (int)K,
                                         (int)N, hy, Mc * T, cus, s));
+    }
+    if (split2) {
+        HIP_OK(moe::launch_unpermute_part(part, info + 1, pl.part_rows, pl.smax2, offsets, counts, (int)El,
+                                          pl.cap, inv, w_c, Mc, (int)K, (int)T, on_in, out + t0 * K, s));
+    } else {
         HIP_OK(moe::launch_unpermute(hy, pl.cap, inv, w_c, Mc, (int)K, (int)T, on_in, out + t0 * K, s));
     }
     return MOE_OK;
+}
+
+// The chunk loop of moe_forward_chunked over an already validated problem
+// and a workspace of at least pl.total bytes.
+int forward_impl(const moe_problem& P, const Plan& pl, const uint16_t* x, const int32_t* topk_ids,
+                 const float* topk_weights, const int32_t* expert_map, const uint8_t* w13, const float* w13_s,
+                 const uint8_t* w2, const float* w2_s, uint16_t* out, uint8_t* ws, int32_t* per_chunk_counts,
+                 int cus, hipStream_t s) {
+    const int64_t nchunks = (P.M + pl.cs - 1) / pl.cs;
+    if (pl.lanes == 1 || nchunks < 2) {
+        for (int64_t c = 0; c < nchunks; ++c) {
+            const int st = forward_chunk(P, pl, c, x, topk_ids, topk_weights, expert_map, w13, w13_s, w2, w2_s, out,
+                                         ws, per_chunk_counts, cus, s);
+            if (st) return st;
+        }
+        return MOE_OK;
+    }
+    LaneStreams* L = nullptr;
+    int st = lane_streams(&L);
+    if (st) return st;
+    std::lock_guard<std::mutex> lock(L->mu);
+    if (!L->ready) {
+        for (int i = 0; i < 2; ++i) {
+            HIP_OK(hipStreamCreateWithFlags(&L->s[i], hipStreamNonBlocking));
+            HIP_OK(hipEventCreateWithFlags(&L->join[i], hipEventDisableTiming));
+        }
+        HIP_OK(hipEventCreateWithFlags(&L->fork, hipEventDisableTiming));
+        L->ready = true;
+    }
+    HIP_OK(hipEventRecord(L->fork, s));
+    HIP_OK(hipStreamWaitEvent(L->s[0], L->fork, 0));
+    HIP_OK(hipStreamWaitEvent(L->s[1], L->fork, 0));
+    // the lanes run free: holding chunk c + 1 until chunk c's gate/up GEMM is
+    // done was measured slower (8192 tokens in chunks of 64: 6.7 against
+    // 6.1 ms)
+    for (int64_t c = 0; c < nchunks; ++c) {
+        const int lane = (int)(c & 1);
+        st = forward_chunk(P, pl, c, x, topk_ids, topk_weights, expert_map, w13, w13_s, w2, w2_s, out,
+                           ws + lane * pl.one, per_chunk_counts, cus, L->s[lane]);
+        if (st) break;
+    }
+    // joined even after a failed launch, so the caller's stream never runs
+    // ahead of work already enqueued on the lanes
+    for (int i = 0; i < 2; ++i) {
+        HIP_OK(hipEventRecord(L->join[i], L->s[i]));
+        HIP_OK(hipStreamWaitEvent(s, L->join[i], 0));
+    }
+    return st;
 }
 
 // Checks of moe_forward_chunked's arguments other than the workspace.
@@ -699,7 +936,9 @@ int moe_forward_chunked_noalloc(const moe_problem* p, const uint16_t* x, const i
     int st = check_forward(p, x, topk_ids, topk_weights, expert_map, w13, w13_s, w2, w2_s, out, per_chunk_counts);
     if (st) return st;
     if (p->M == 0) return MOE_OK;
-    const Plan pl = make_plan(*p);
+    // one lane: the chunks run in order on the caller's stream alone, with no
+    // library stream or event created for them
+    const Plan pl = make_plan(*p, false);
     REQUIRE(pl.total <= kScratchBytes, MOE_ERR_WORKSPACE_TOO_SMALL,
             "the problem needs %zu workspace bytes, more than the %zu of the fixed scratch array: use a smaller "
             "chunk_size or moe_forward_chunked with a workspace", pl.total, kScratchBytes);

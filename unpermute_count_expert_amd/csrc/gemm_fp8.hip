@@ -63,13 +63,14 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;   // 8: 2 along M, 4 along N
 // Tile shape by MI, the 16-row MFMA blocks per wave (the tile has 2 * 16 * MI
 // rows): MI = 8 gives 256x256 tiles with two 64 KB LDS stages, MI = 4 gives
-// 128x256 tiles with three 48 KB stages.
+// 128x256 tiles with three 48 KB stages, MI = 2 (the K-split kernel for
+// experts of a few rows) 64x256 tiles with three 40 KB stages.
 template <int MI>
 struct Shape {
     static constexpr int BM = 32 * MI;
     static constexpr int kStageA = BM * BK;              // bytes
     static constexpr int kStage = kStageA + BN * BK;
-    static constexpr int kStages = MI == 4 ? 3 : 2;
+    static constexpr int kStages = MI == 8 ? 2 : 3;
     static constexpr int kADma = MI / 2;                  // 8-row A DMAs per wave and step
     static constexpr int kDmaPerStep = kADma + 4 + 1;     // + 4 B + 1 scale
     static constexpr int kScaleRows = 4 * MI;             // A scale rows per wave
@@ -158,23 +159,35 @@ __device__ __forceinline__ void rows_of(const int32_t* __restrict__ offsets, con
 // wave-uniform.
 struct TileCursor {
     int64_t t;           // tile index
-    int tm, tn;          // m-tile, n-tile
+    int tm, tn;          // m-tile, n-tile (split: n-tile + nsplit-th of K, see TileWalk)
     int e;               // expert of m-tile tm
     int e_lo, e_hi;      // its rows [e_lo, e_hi)
     bool valid;
     int m0, row_end, n0; // the tile: rows [m0, min(m0 + bm, row_end)), columns n0..
+    int seg, g0;         // K segment and its first K group (0 and 0 without a split)
 };
 
+// With a split of K into nsplit segments of kseg groups, the walk runs over
+// ntn * nsplit "n-tiles" per m-tile: n-tile tn of segment seg is number
+// seg * ntn_real + tn.
 struct TileWalk {
     const int32_t* offsets;
     const int32_t* counts;
     int64_t cap_rows;
     const int* s_tpre;
+    const int* s_lo;     // LDS copies of the experts' clamped rows, or null: read offsets/counts
+    const int* s_hi;
     int El, ntn, step_q, step_r;   // nslots = step_q * ntn + step_r
     int bm;                        // tile rows
     int64_t t_hi, nslots;
+    int ntn_real, kseg, nsplit;
 
     __device__ __forceinline__ void fill(TileCursor& c) const {
+        if (s_lo != nullptr) {
+            c.e_lo = __builtin_amdgcn_readfirstlane(s_lo[c.e]);
+            c.e_hi = __builtin_amdgcn_readfirstlane(s_hi[c.e]);
+            return;
+        }
         int64_t lo, hi;
         rows_of(offsets, counts, cap_rows, c.e, lo, hi);
         c.e_lo = __builtin_amdgcn_readfirstlane((int)lo);
@@ -186,15 +199,28 @@ struct TileWalk {
         m0 = max(c.e_lo, min(m0, c.e_hi - 1));
         c.m0 = __builtin_amdgcn_readfirstlane(min(m0, (int)cap_rows - 1));
         c.row_end = c.e_hi;
-        c.n0 = c.tn * BN;
+        if (nsplit > 1) {
+            const int seg = c.tn / ntn_real;
+            c.seg = seg;
+            c.g0 = seg * kseg;
+            c.n0 = (c.tn - seg * ntn_real) * BN;
+        } else {
+            c.seg = c.g0 = 0;
+            c.n0 = c.tn * BN;
+        }
     }
     __device__ __forceinline__ void start(TileCursor& c, int64_t t) const {
         c.t = t;
         c.valid = t < t_hi;
-        c.tm = c.tn = c.e = c.e_lo = c.e_hi = c.m0 = c.row_end = c.n0 = 0;
+        c.tm = c.tn = c.e = c.e_lo = c.e_hi = c.m0 = c.row_end = c.n0 = c.seg = c.g0 = 0;
         if (!c.valid) return;
-        c.tm = (int)(t / ntn);
-        c.tn = (int)(t - (int64_t)c.tm * ntn);
+        if (t < (int64_t)0x7fffffff) {   // a 32-bit division when it fits
+            c.tm = (int)t / ntn;
+            c.tn = (int)t - c.tm * ntn;
+        } else {
+            c.tm = (int)(t / ntn);
+            c.tn = (int)(t - (int64_t)c.tm * ntn);
+        }
         int lo = 0, hi = El - 1;  // largest e < El with s_tpre[e] <= tm
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -259,27 +285,62 @@ struct ReduceArgs {
     uint16_t* out;            // [Mc, n_out]
 };
 
-template <bool KACT, int MI, bool RED = false>
+// SMALL (with KACT = false and RED = false, MI = 2): the kernel for chunks
+// with few routed rows per expert.  Its 64-row tiles waste less of each
+// A step on copies of an expert's last row, and its 140 KB of LDS leave room
+// on a CU for the small kernels of the forward's other lane.  Its units are
+// short and each starts on another weight block, so the weight block scales
+// ride in the ring as well (one more dword DMA per step) instead of coming
+// through the scalar cache, whose miss at every unit start stalls the step.
+// Without part, the output is bf16 out as above.  With part, and when the
+// tiles fill fewer than four rounds of the grid, K is cut into sp.nsplit
+// equal segments (the launcher's nsplit divides k_in / 128) and the grid
+// walks (tile, segment) units; unit (tile, seg) folds the promoted group
+// terms of its segment in k order, as the whole-K loop does, and stores the
+// fp32 sums (not bf16) at part[seg, v, n], where v is the row's place among
+// the valid rows of all experts in expert order; info[0] receives the
+// segment count used (1 when not cut) and out is not written.  The consumer
+// adds the partials in segment order and rounds the sum to bf16.
+struct SplitArgs {
+    float* part;          // [nsplit, part_rows, n_out], or null: bf16 out
+    int32_t* info;        // segments used
+    int64_t part_rows;    // valid rows held per segment; rows past it are not stored
+    int nsplit;
+};
+
+template <bool KACT, int MI, bool RED = false, bool SMALL = false>
 __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
     const uint8_t* __restrict__ a, const float* __restrict__ a_s, const uint8_t* __restrict__ w,
     const float* __restrict__ w_s, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ counts, int El, int64_t cap_rows, int n_out, int k_in,
-    uint16_t* __restrict__ out, uint8_t* __restrict__ q, float* __restrict__ q_s, ReduceArgs red) {
+    uint16_t* __restrict__ out, uint8_t* __restrict__ q, float* __restrict__ q_s, ReduceArgs red,
+    SplitArgs sp) {
+    static_assert(!SMALL || (!KACT && !RED && MI == 2), "the small-chunk kernel is the plain one on 64-row tiles");
     using Sh = Shape<MI>;
     constexpr int BM = Sh::BM, kStageA = Sh::kStageA, kStage = Sh::kStage, kStages = Sh::kStages;
-    constexpr int kADma = Sh::kADma, kDmaPerStep = Sh::kDmaPerStep, kScaleRows = Sh::kScaleRows;
+    constexpr int kADma = Sh::kADma, kScaleRows = Sh::kScaleRows;
+    constexpr int kDmaPerStep = Sh::kDmaPerStep + (SMALL ? 1 : 0);   // + the weight scales
     // the 256-row fused kernel has room for the SiLU table next to its two
     // 64 KB stages; the 128-row one, with three 48 KB stages, computes SiLU
     constexpr bool kSiluLds = KACT && MI == 8;
     __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStage];
     __shared__ float s_silu[kSiluLds ? kSiluEntries : 1];
     __shared__ __attribute__((aligned(16))) float sAs[kStages][BM];   // [stage][row]
+    __shared__ float sWs[SMALL ? kStages : 1][2];                       // [stage][128-column block]
     __shared__ int s_tpre[kMaxLocalExperts + 1];
     __shared__ int s_wsum[kWaves];
     __shared__ float s_amax[KACT ? 4 : 1][KACT ? BM : 1];   // per-wave-column partial group maxima
     __shared__ __attribute__((aligned(16))) float s_inv[KACT ? BM : 1];   // 448 / d of each row
     __shared__ int s_fold[RED ? BM : 1];   // tokens this tile completes
     __shared__ int s_nfold;
+    __shared__ int s_vpre[SMALL ? kMaxLocalExperts + 1 : 1];   // valid rows before expert e, capped (split)
+    // every expert's clamped rows [lo, hi), read once here: the tile walk
+    // then finds them in LDS rather than in global memory (the fused kernel
+    // has no LDS left for them)
+    constexpr bool kLdsRows = !KACT;
+    __shared__ int s_lo[kLdsRows ? kMaxLocalExperts : 1];
+    __shared__ int s_hi[kLdsRows ? kMaxLocalExperts : 1];
+    __shared__ int64_t s_vwsum[SMALL ? kWaves : 1];
     const int n_half = n_out / 2;                 // N when KACT
 
     const int tid = threadIdx.x;
@@ -288,22 +349,39 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
     if constexpr (kSiluLds) silu_table_build(s_silu);   // published by the barriers below
 
     // ---- m-tile prefix over the experts' valid row counts ------------------
+    // (and, for the split, the valid-row prefix: the partials' row places)
     int ntl[2];
+    int64_t vl[2];
     int tsum = 0;
+    int64_t vsum = 0;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int e = tid * 2 + j;
         int nt = 0;
+        vl[j] = 0;
         if (e < El) {
             int64_t lo, hi;
             rows_of(offsets, counts, cap_rows, e, lo, hi);
             nt = (int)((hi - lo + BM - 1) / BM);
+            vl[j] = hi - lo;
+            if constexpr (kLdsRows) {
+                s_lo[e] = (int)lo;
+                s_hi[e] = (int)hi;
+            }
         }
         ntl[j] = nt;
         tsum += nt;
+        vsum += vl[j];
     }
     const int incl = wave_incl_scan(tsum);
     if (lane == kWave - 1) s_wsum[wave] = incl;
+    // rows are at most cap_rows < 2^31 per expert, so 64-bit sums; the stored
+    // row prefix is capped at part_rows
+    int64_t vin = 0;
+    if constexpr (SMALL) {
+        vin = wave_inclusive_scan(vsum);
+        if (lane == kWave - 1) s_vwsum[wave] = vin;
+    }
     __syncthreads();
     int excl = incl - tsum;
     for (int w2 = 0; w2 < wave; ++w2) excl += s_wsum[w2];
@@ -314,15 +392,35 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
         excl += ntl[j];
     }
     if (tid == kThreads - 1) s_tpre[El] = excl;
+    if constexpr (SMALL) {
+        int64_t vex = vin - vsum;
+        for (int w2 = 0; w2 < wave; ++w2) vex += s_vwsum[w2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int e = tid * 2 + j;
+            if (e < El) s_vpre[e] = (int)(vex < sp.part_rows ? vex : sp.part_rows);
+            vex += vl[j];
+        }
+    }
     __syncthreads();
 
     const int mtiles = __builtin_amdgcn_readfirstlane(s_tpre[El]);
     const int ntn = (n_out + BN - 1) / BN;   // the last n-tile may hold only 128 columns
     const int nb128 = n_out / 128;
     const int kg = k_in / BK;
-    const int64_t total = (int64_t)mtiles * ntn;
     const int xcd = blockIdx.x & 7;
     const int nslots = gridDim.x >> 3;
+    int nsplit = 1;
+    if constexpr (SMALL) {
+        if (sp.part != nullptr) {
+            const int64_t tiles = (int64_t)mtiles * ntn;
+            const int ns = sp.nsplit;   // checked here too: a bad count never leaves K short
+            nsplit = (tiles < 4 * (int64_t)gridDim.x && ns > 1 && ns <= 8 && kg % ns == 0) ? ns : 1;
+            if (blockIdx.x == 0 && tid == 0) sp.info[0] = nsplit;
+        }
+    }
+    const int kseg = kg / nsplit;   // K groups per unit
+    const int64_t total = (int64_t)mtiles * ntn * nsplit;
     const int64_t t_lo = total * xcd / 8 + (blockIdx.x >> 3);
     const int64_t t_hi = total * (xcd + 1) / 8;
 
@@ -331,13 +429,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
     walk.counts = counts;
     walk.cap_rows = cap_rows;
     walk.s_tpre = s_tpre;
+    walk.s_lo = kLdsRows ? s_lo : nullptr;
+    walk.s_hi = kLdsRows ? s_hi : nullptr;
     walk.El = El;
-    walk.ntn = ntn;
-    walk.step_q = nslots / ntn;
-    walk.step_r = nslots - walk.step_q * ntn;
+    walk.ntn = ntn * nsplit;
+    walk.step_q = nslots / walk.ntn;
+    walk.step_r = nslots - walk.step_q * walk.ntn;
     walk.t_hi = t_hi;
     walk.nslots = nslots;
     walk.bm = BM;
+    walk.ntn_real = ntn;
+    walk.kseg = kseg;
+    walk.nsplit = nsplit;
 
     const int wm = wave >> 2;   // 0..1
     const int wn = wave & 3;    // 0..3
@@ -374,6 +477,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
     const int rS = wave * kScaleRows + (lane & (kScaleRows - 1));
     const uint32_t lds_smem = (uint32_t)(uintptr_t)smem;
     const uint32_t lds_as = (uint32_t)(uintptr_t)&sAs[0][0];
+    const uint32_t lds_ws = (uint32_t)(uintptr_t)&sWs[0][0];
 
     // Loads issued by this wave so far, and the count right after each
     // pending step's DMAs (by ring slot).
@@ -392,6 +496,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
     const uint8_t* dA = a;
     const uint8_t* dB = w;
     const float* dS = a_s;
+    const float* dW = w_s;
+    uint32_t voW = 0;
 #define MOE_DMA_OFFSETS()                                                             \
     do {                                                                              \
         const int last_ = max(dT.row_end - 1 - dT.m0, 0);                             \
@@ -405,9 +511,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
         voS = (uint32_t)(min(rS, last_) * kg * 4);                                    \
         const int64_t brow0_ = KACT ? (int64_t)((wave & 1) ? n_half : 0) + (dT.n0 >> 1) \
                                     : (int64_t)dT.n0;                                 \
-        dA = a + (int64_t)dT.m0 * k_in;                                               \
-        dB = w + ((int64_t)dT.e * n_out + brow0_) * k_in;                             \
-        dS = a_s + (int64_t)dT.m0 * kg;                                               \
+        dA = a + (int64_t)dT.m0 * k_in + dT.g0 * BK;                                  \
+        dB = w + ((int64_t)dT.e * n_out + brow0_) * k_in + dT.g0 * BK;                \
+        dS = a_s + (int64_t)dT.m0 * kg + dT.g0;                                       \
+        if (SMALL) {                                                                  \
+            dW = w_s + (int64_t)dT.e * nb128 * kg + dT.g0;                            \
+            voW = (uint32_t)(min(dT.n0 / 128 + (lane & 1), nb128 - 1) * kg * 4);      \
+        }                                                                             \
     } while (0)
     // one step of DMAs into ring slot d_slot, then advance the cursor
 #define MOE_DMA_NEXT()                                                                \
@@ -415,9 +525,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
         const uint8_t* sa_ = dA;                                                      \
         const uint8_t* sb_ = dB;                                                      \
         const float* ss_ = dS;                                                        \
+        const float* sw_ = dW;                                                        \
         dA += BK;                                                                     \
         dB += BK;                                                                     \
         dS += 1;                                                                      \
+        dW += 1;                                                                      \
         const uint32_t base_ = lds_smem + d_slot * kStage;                            \
         _Pragma("unroll") for (int j_ = 0; j_ < kADma; ++j_)                          \
             dma16(base_ + (wave * kADma + j_) * 1024, voA[j_], sa_);                  \
@@ -427,12 +539,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
         dma16(base_ + kStageA + (wave * 4 + 3) * 1024, voB3, sb_);                    \
         if (lane < kScaleRows)                                                        \
             dma4(lds_as + d_slot * (BM * 4) + wave * (kScaleRows * 4), voS, ss_);     \
+        if (SMALL && lane < 2) /* every wave, the same two dwords */                  \
+            dma4(lds_ws + d_slot * 8, voW, sw_);                                      \
         loads += kDmaPerStep;                                                         \
         if (d_slot == 0) d_end0 = loads;                                              \
         else if (d_slot == 1) d_end1 = loads;                                         \
         else d_end2 = loads;                                                          \
         d_slot = d_slot == kStages - 1 ? 0 : d_slot + 1;                              \
-        if (++d_g == kg) {                                                            \
+        if (++d_g == kseg) {                                                          \
             d_g = 0;                                                                  \
             walk.next(dT);                                                            \
             if (dT.valid) MOE_DMA_OFFSETS();                                          \
@@ -452,7 +566,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
         // weight block-scale rows: plain, the 128-column block of this wave;
         // KACT, the gate block (MFMA blocks 0/1) and the up block (2/3)
         const int64_t ws_row = KACT ? ((int64_t)cur.e * nb128 + (cur.n0 >> 8)) * kg
-                                    : ((int64_t)cur.e * nb128 + min(cur.n0 / 128 + (wn >> 1), nb128 - 1)) * kg;
+                                    : ((int64_t)cur.e * nb128 + min(cur.n0 / 128 + (wn >> 1), nb128 - 1)) * kg +
+                                          cur.g0;
         const int64_t ws_row_up = ws_row + (int64_t)(n_half / 128) * kg;
         v4f acc[MI][4];
 #pragma unroll
@@ -460,7 +575,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-        for (int g = 0; g < kg; ++g) {
+        for (int g = 0; g < kseg; ++g) {
             // this step's DMAs complete, in every wave.  The loads issued after
             // them are the next kStages - 2 steps' DMAs: none with two
             // stages, where vmcnt(0) is exact; with three, one step's or (at
@@ -486,7 +601,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
                 const uint8_t* blo = smem + (sb + fB_lo);
                 const uint8_t* bhi = smem + (sb + fB_hi);
                 const float* scs = &sAs[slot][wm * 16 * MI + (lane >> 4) * 4];
-                const float ws = w_s[ws_row + g];
+                const float ws = SMALL ? sWs[slot][wn >> 1] : w_s[ws_row + g];
                 const float ws_up = KACT ? w_s[ws_row_up + g] : ws;
                 v8i bf[4];
 #pragma unroll
@@ -530,7 +645,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
             // kernel, so it need not take L2 lines from the operands.  Rows
             // are addressed from the lane's first row by 32-bit offsets; a
             // wave whose 16 * MI rows are all valid stores without row tests.
-            if (wave_has_rows) {
+            if (SMALL && sp.part != nullptr && wave_has_rows) {
+                // fp32 partial sums of the segment, at the rows' valid-row places
+                const int row0 = cur.m0 + wm * 16 * MI + (lane >> 4) * 4;
+                const int64_t v0 = (int64_t)s_vpre[cur.e] + (row0 - cur.e_lo);
+                float* const pb = sp.part + ((int64_t)cur.seg * sp.part_rows + v0) * n_out +
+                                  (cur.n0 + wn * 64 + 4 * fr);
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int dr = mi * 16 + v;
+                        if (row0 + dr < cur.row_end && v0 + dr < sp.part_rows)
+                            __builtin_nontemporal_store(v4f{acc[mi][0][v], acc[mi][1][v], acc[mi][2][v], acc[mi][3][v]},
+                                                        reinterpret_cast<v4f*>(pb + (int64_t)dr * n_out));
+                    }
+            } else if (wave_has_rows) {
                 const int row0 = cur.m0 + wm * 16 * MI + (lane >> 4) * 4;
                 uint16_t* const base = out + (int64_t)row0 * n_out + (cur.n0 + wn * 64 + 4 * fr);
                 auto store_row = [&](int mi, int v) __attribute__((always_inline)) {
@@ -730,9 +860,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(
 
 namespace {
 
-int64_t gemm_grid(int64_t cap_rows, int El, int n_out, int bm, int num_cus) {
+int64_t gemm_grid(int64_t cap_rows, int El, int n_out, int bm, int num_cus, int units_per_tile = 1) {
     const int64_t ntn = (n_out + BN - 1) / BN;
-    const int64_t bound = ((cap_rows + bm - 1) / bm + El) * ntn;
+    const int64_t bound = ((cap_rows + bm - 1) / bm + El) * ntn * units_per_tile;
     int64_t grid = num_cus;            // one 8-wave block per CU (up to 150 KB of LDS)
     if (bound < grid) grid = bound;
     grid = ((grid + 7) / 8) * 8;
@@ -757,12 +887,23 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_s, const uint8_t
     if (gemm_tile_rows(rows_hint, El) == 256) {
         const int64_t grid = gemm_grid(cap_rows, El, n_out, Shape<8>::BM, num_cus);
         k_grouped_gemm<false, 8><<<(unsigned)grid, kThreads, 0, s>>>(a, a_s, w, w_s, offsets, counts, El,
-                                                                      cap_rows, n_out, k_in, out, nullptr, nullptr, ReduceArgs{});
+                                                                      cap_rows, n_out, k_in, out, nullptr, nullptr, ReduceArgs{}, SplitArgs{});
     } else {
         const int64_t grid = gemm_grid(cap_rows, El, n_out, Shape<4>::BM, num_cus);
         k_grouped_gemm<false, 4><<<(unsigned)grid, kThreads, 0, s>>>(a, a_s, w, w_s, offsets, counts, El,
-                                                                      cap_rows, n_out, k_in, out, nullptr, nullptr, ReduceArgs{});
+                                                                      cap_rows, n_out, k_in, out, nullptr, nullptr, ReduceArgs{}, SplitArgs{});
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm_small(const uint8_t* a, const float* a_s, const uint8_t* w, const float* w_s,
+                                     const int32_t* offsets, const int32_t* counts, int El, int64_t cap_rows,
+                                     int n_out, int k_in, uint16_t* out, float* part, int64_t part_rows, int nsplit,
+                                     int32_t* info, int num_cus, hipStream_t s) {
+    const int64_t grid = gemm_grid(cap_rows, El, n_out, Shape<2>::BM, num_cus, part != nullptr ? nsplit : 1);
+    k_grouped_gemm<false, 2, false, true><<<(unsigned)grid, kThreads, 0, s>>>(
+        a, a_s, w, w_s, offsets, counts, El, cap_rows, n_out, k_in, part != nullptr ? nullptr : out, nullptr, nullptr,
+        ReduceArgs{}, SplitArgs{part, info, part_rows, nsplit});
     return hipGetLastError();
 }
 
@@ -777,12 +918,12 @@ hipError_t launch_grouped_gemm_reduce(const uint8_t* a, const float* a_s, const 
         const int64_t grid = gemm_grid(cap_rows, El, n_out, Shape<8>::BM, num_cus);
         k_grouped_gemm<false, 8, true><<<(unsigned)grid, kThreads, 0, s>>>(a, a_s, w, w_s, offsets, counts, El,
                                                                             cap_rows, n_out, k_in, y, nullptr,
-                                                                            nullptr, red);
+                                                                            nullptr, red, SplitArgs{});
     } else {
         const int64_t grid = gemm_grid(cap_rows, El, n_out, Shape<4>::BM, num_cus);
         k_grouped_gemm<false, 4, true><<<(unsigned)grid, kThreads, 0, s>>>(a, a_s, w, w_s, offsets, counts, El,
                                                                             cap_rows, n_out, k_in, y, nullptr,
-                                                                            nullptr, red);
+                                                                            nullptr, red, SplitArgs{});
     }
     return hipGetLastError();
 }
@@ -794,11 +935,11 @@ hipError_t launch_grouped_gemm_act(const uint8_t* a, const float* a_s, const uin
     if (gemm_tile_rows(rows_hint, El) == 256) {
         const int64_t grid = gemm_grid(cap_rows, El, 2 * N, Shape<8>::BM, num_cus);
         k_grouped_gemm<true, 8><<<(unsigned)grid, kThreads, 0, s>>>(a, a_s, w13, w13_s, offsets, counts, El,
-                                                                     cap_rows, 2 * N, k_in, nullptr, q, q_s, ReduceArgs{});
+                                                                     cap_rows, 2 * N, k_in, nullptr, q, q_s, ReduceArgs{}, SplitArgs{});
     } else {
         const int64_t grid = gemm_grid(cap_rows, El, 2 * N, Shape<4>::BM, num_cus);
         k_grouped_gemm<true, 4><<<(unsigned)grid, kThreads, 0, s>>>(a, a_s, w13, w13_s, offsets, counts, El,
-                                                                     cap_rows, 2 * N, k_in, nullptr, q, q_s, ReduceArgs{});
+                                                                     cap_rows, 2 * N, k_in, nullptr, q, q_s, ReduceArgs{}, SplitArgs{});
     }
     return hipGetLastError();
 }

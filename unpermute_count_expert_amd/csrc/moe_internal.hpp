@@ -53,6 +53,13 @@ hipError_t launch_act_quant(const uint16_t* in, int64_t rows, int n, int mode,
                             const int32_t* offsets, const int32_t* counts, int El, uint8_t* q,
                             float* q_s, int64_t rows_hint, hipStream_t s);
 
+// The SiLU-mul requant (masked) of the gate/up values that
+// launch_grouped_gemm_small left as partial sums part [S, part_rows, 2n]:
+// the same codes and scales as launch_act_quant of their bf16 sum.
+hipError_t launch_act_quant_part(const float* part, const int32_t* info, int64_t part_rows, int smax, int64_t rows,
+                                 int n, const int32_t* offsets, const int32_t* counts, int El, uint8_t* q, float* q_s,
+                                 int64_t rows_hint, hipStream_t s);
+
 // ---- grouped GEMM ------------------------------------------------------------
 // Output-tile rows of the plain GEMM for rows_hint routed rows over El
 // experts: 256 once the experts average 256 rows, else 128.
@@ -61,6 +68,32 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_s, const uint8_t
                                const float* w_s, const int32_t* offsets, const int32_t* counts,
                                int El, int64_t cap_rows, int n_out, int k_in, uint16_t* out,
                                int64_t rows_hint, int num_cus, hipStream_t s);
+
+// Output-tile rows of the GEMMs of a chunk of rows_hint routed rows over El
+// experts: 64 (launch_grouped_gemm_small) while the experts average at most
+// 64 rows.
+inline bool gemm_small_chunk(int64_t rows_hint, int El) { return El > 0 && rows_hint <= (int64_t)64 * El; }
+// The plain GEMM on 64-row tiles for such chunks (see gemm_fp8.hip).  part
+// null: bf16 out [cap_rows, n_out].  part set: when the tiles fill fewer than
+// four rounds of num_cus CUs, K is cut into nsplit segments (nsplit divides
+// k_in / 128, at most 8) and the fp32 partial sums go to part [nsplit,
+// part_rows, n_out], rows at their place among the valid rows (experts in
+// order); info[0] receives the segments used (1: one slab of whole-K sums,
+// whose bf16 rounding is the unsplit output).
+hipError_t launch_grouped_gemm_small(const uint8_t* a, const float* a_s, const uint8_t* w, const float* w_s,
+                                     const int32_t* offsets, const int32_t* counts, int El, int64_t cap_rows,
+                                     int n_out, int k_in, uint16_t* out, float* part, int64_t part_rows, int nsplit,
+                                     int32_t* info, int num_cus, hipStream_t s);
+// The K segments of a small-chunk GEMM: the largest S <= 8 dividing
+// k_in / 128 whose segments keep at least 8 groups (1024 of K); 1 below
+// 16 groups.  A shorter unit costs more in its pipeline refill (~1 us per
+// unit start, measured) than its finer spread over the grid saves.
+inline int gemm_split_segments(int k_in) {
+    const int kg = k_in / 128;
+    for (int S = 8; S > 1; --S)
+        if (kg % S == 0 && kg / S >= 8) return S;
+    return 1;
+}
 
 // The gate/up GEMM (w13 [El, 2N, k_in]) fused with SiLU-and-mul and the
 // per-128 requant: writes q [cap_rows, N] e4m3 and q_s [cap_rows, N/128].
@@ -88,6 +121,13 @@ hipError_t launch_reduce_prep(const int32_t* inv_perm, int64_t Mc, int topk, int
 hipError_t launch_unpermute(const uint16_t* y, int64_t y_rows, const int32_t* inv_perm,
                             const float* topk_w, int64_t Mc, int K, int topk, int apply_on_input, uint16_t* out,
                             hipStream_t s);
+
+// launch_unpermute of y given as launch_grouped_gemm_small's partial sums
+// part [S, part_rows, K] (y_rows: the rows of the expert slots).
+hipError_t launch_unpermute_part(const float* part, const int32_t* info, int64_t part_rows, int smax,
+                                 const int32_t* offsets, const int32_t* counts, int El, int64_t y_rows,
+                                 const int32_t* inv_perm, const float* topk_w, int64_t Mc, int K, int topk,
+                                 int apply_on_input, uint16_t* out, hipStream_t s);
 
 // ---- HBM streams (measured ceilings) -------------------------------------------
 // mode: MOE_STREAM_* of moe.h; sink receives nothing in practice (read mode
