@@ -37,7 +37,7 @@ import oracle
 import unpermute_count_expert_amd as moe
 from unpermute_count_expert_amd import generators as gen
 from unpermute_count_expert_amd.pipeline import StepBuffers, run_steps, step_ops
-from tests.gpu_helpers import (ATOL, RTOL, announce, bf16_f64, bf16_ulp, dev, filled, host, partial_rows, record,
+from tests.gpu_helpers import (ATOL, DEV, RTOL, announce, bf16_f64, bf16_ulp, dev, filled, host, partial_rows, record,
                                tight_excess, valid_rows)
 
 pytestmark = pytest.mark.gpu
@@ -426,6 +426,51 @@ def test_forward_workspace_guard_bands(name, cfg):
     ref, _ = _forward(layer, dict(x=dev(inp.x), ids=dev(inp.topk_ids), w=dev(inp.topk_weights)), cfg.M,
                       cfg.chunk_size, 0)
     np.testing.assert_array_equal(host(out, bf16=True), ref)
+
+
+@pytest.mark.parametrize("name,cfg", [
+    ("C4b_two_chunks", gen.CONFIGS["C4b"]),
+    ("zipf_300_in_64", gen.small_config(M=300, K=512, N=256, Eg=32, El=16, topk=4, chunk_size=64,
+                                        routing="zipf", seed=21, ep_rank_of_2=1)),
+    ("C2_one_chunk_split", gen.CONFIGS["C2"]),
+])
+def test_forward_graph_replay(name, cfg):
+    """The forward captured in a HIP graph (with two chunks or more, its two
+    library streams fork from and join the captured stream) and replayed
+    three times, with eager forwards on other inputs and synchronisations in
+    between: every replay writes the eager output bit for bit, and the eager
+    calls between replays are unaffected."""
+    announce("forward graph replay", name)
+    inp = _inputs(cfg)
+    layer = _layer(inp)
+    M, K = cfg.M, cfg.K
+    d = dict(x=dev(inp.x), ids=dev(inp.topk_ids), w=dev(inp.topk_weights))
+    other = dict(x=dev(inp.x[::-1].copy()), ids=dev(inp.topk_ids[::-1].copy()), w=dev(inp.topk_weights[::-1].copy()))
+    ref, _ = _forward(layer, d, M, cfg.chunk_size, 0)
+    ref_other, _ = _forward(layer, other, M, cfg.chunk_size, 0)
+    out = filled((M, K), "bf16", 0)
+    ws = torch.empty(moe.moe_forward_workspace_size(layer.problem(M, cfg.topk, cfg.chunk_size, 0)),
+                     dtype=torch.uint8, device=DEV)
+    p = layer.problem(M, cfg.topk, cfg.chunk_size, 0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        moe.moe_forward_chunked(p, d["x"], d["ids"], d["w"], layer.expert_map, layer.w13, layer.w13_s, layer.w2,
+                                layer.w2_s, out, ws)   # warm-up outside the capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            moe.moe_forward_chunked(p, d["x"], d["ids"], d["w"], layer.expert_map, layer.w13, layer.w13_s,
+                                    layer.w2, layer.w2_s, out, ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(0x5A5A)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(out, bf16=True), ref, err_msg=f"replay {rep}")
+        eager, _ = _forward(layer, other, M, cfg.chunk_size, 0)
+        np.testing.assert_array_equal(eager, ref_other, err_msg=f"eager call after replay {rep}")
 
 
 def test_forward_is_deterministic():
