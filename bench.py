@@ -206,6 +206,41 @@ def batched_masked(iters, stream):
             "TFLOP/s": round(2.0 * P * (2 * N * K + K * N) / (st["median"] * 1e-3) / 1e12, 1)}
 
 
+def small_chunk_ops(iters, stream, name="C2"):
+    """The 64-token profiling layer (one chunk, 64 of 128 experts local, top-4)
+    op by op through the same kernels the forward runs on it (the small-tile
+    GEMMs, the gate/up GEMM's K cut into partial slabs): each op timed in
+    place as in per_op_times, after ~0.2 s of warm passes.  At this size the
+    GEMMs stream every non-empty expert's weights once, so their roofline is
+    those bytes at the 8 TB/s HBM peak."""
+    c = gen.CONFIGS[name]
+    inp = gen.make_inputs(c)
+    layer = moe.MoeLayer(dev(inp.w13), dev(inp.w13_s), dev(inp.w2), dev(inp.w2_s), c.Eg,
+                         dev(inp.expert_map) if inp.expert_map is not None else None, c.align)
+    d = {"x": dev(inp.x), "ids": dev(inp.topk_ids), "w": dev(inp.topk_weights)}
+    t0 = time.time()
+    while time.time() - t0 < 0.2:
+        per_op_times(layer, d, 0, 5, stream)
+    res, counts, _ = per_op_times(layer, d, 0, iters, stream)
+    plan = moe.moe_forward_plan_info(layer.problem(c.M, c.topk, 0, 0))
+    ne = int((counts > 0).sum())
+    wb = {"gemm_w13": ne * 2 * c.N * c.K, "gemm_w2": ne * c.K * c.N}
+    ops = {}
+    for k, v in res.items():
+        if k == "count":
+            continue
+        m = float(np.median(v))
+        e = {"ms": round(m, 5)}
+        if k in wb:
+            e["weight_MB"] = round(wb[k] / 1e6, 1)
+            e["weight_GB/s"] = round(wb[k] / (m * 1e-3) / 1e9, 1)
+            e["hbm_frac"] = round(wb[k] / (m * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        ops[k] = e
+    return {"workload": f"{name}: M={c.M} K={c.K} N={c.N} E={c.El}/{c.Eg} topk={c.topk}, {int(counts.sum())} routed rows "
+                        f"over {ne} experts", "plan": plan, "ops": ops,
+            "note": "each op between HIP events, so every op's time includes its launch; the forward runs them back to back"}
+
+
 def algorithmic(cfg, counts: np.ndarray, R: int):
     M, K, N, T = cfg.M, cfg.K, cfg.N, cfg.topk
     P = int(counts.sum())
@@ -456,6 +491,7 @@ def main():
         "count_scaled_2^24_pairs": count_big,
         "ceilings": ceil,
         "batched_masked_experts": batched_masked(args.op_iters, stream),
+        "small_chunk_ops": small_chunk_ops(args.op_iters, stream),
         "wall_s_timed": round(wall, 3),
         "input_gen_s": round(t_gen, 1),
     }
