@@ -140,17 +140,30 @@ def per_op_times(layer, d, on_input, iters, stream, only=None, flush=None, fused
 def count_scaled(iters, stream):
     """moe_count on 2^24 (token, k) pairs (2^21 tokens x top-8 over 128
     experts, 64 MiB of ids): the layer's own count moves 0.5 MB, too little
-    for bandwidth to show."""
+    for bandwidth to show.  Timed as calls back to back (20 per event pair,
+    the figure GB/s is taken from) and one call per event pair (which adds
+    the events' own gaps to a call of a few tens of microseconds).  The
+    calls cycle over six copies of the ids (384 MiB, more than the 256 MB
+    MALL), so each call reads ids that four other calls' reads have passed
+    since its copy was last read."""
     g = torch.Generator(device="cpu").manual_seed(7)
     ids = torch.randint(0, 128, (1 << 21, 8), generator=g, dtype=torch.int32).to("cuda:0")
+    copies = [ids] + [ids.clone() for _ in range(5)]
     counts = torch.empty(128, dtype=torch.int32, device="cuda:0")
-    fn = lambda: moe._lib.moe_count(ids, None, 128, 128, counts)
+    nxt = [0]
+
+    def fn():
+        moe._lib.moe_count(copies[nxt[0]], None, 128, 128, counts)
+        nxt[0] = (nxt[0] + 1) % len(copies)
+
     fn()
     torch.cuda.synchronize()
-    ms = [timed(fn, 1, stream) for _ in range(iters)]
-    st = stats(ms)
+    st = stats([timed(fn, 20, stream) for _ in range(iters)])
     st["GB/s"] = round(4 * (1 << 24) / (st["median"] * 1e-3) / 1e9, 1)
     st["hbm_frac"] = round(st["GB/s"] / PEAK_HBM_GBS, 4)
+    st["one_call_per_event_pair_ms"] = round(float(np.median([timed(fn, 1, stream) for _ in range(iters)])), 5)
+    st["note"] = ("median of %d groups of 20 back-to-back calls over 6 copies of the ids (each call: a clear "
+                  "kernel and the count kernel)" % iters)
     return st
 
 
@@ -351,7 +364,8 @@ def main():
     ap.add_argument("--profile-op", default=None,
                     help="time only this op (count, quant_permute, input_quant, permute, gemm_w13, silu_mul_quant, "
                          "gemm_w2, unpermute, gemm_w13_act: the fused gate/up variant, or gemm_w2_reduce: the down GEMM with "
-                         "the weight-and-reduce) or 'copy'; for profiler runs")
+                         "the weight-and-reduce), 'count_scaled' (moe_count on 2^24 pairs) or 'copy'; for "
+                         "profiler runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -360,6 +374,10 @@ def main():
 
     if args.profile_op == "copy":
         copy_calibration(args.op_iters)
+        return
+    if args.profile_op == "count_scaled":
+        st = count_scaled(args.op_iters, torch.cuda.current_stream())
+        print(json.dumps({"mode": "profile_op", "op": "count_scaled", **st}), flush=True)
         return
     cfg = gen.CONFIGS[args.config]
     on_input = cfg.apply_router_weight_on_input

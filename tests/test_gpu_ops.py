@@ -168,16 +168,23 @@ def test_silu_mul_quant_every_bf16_gate(up, n):
     (1000, 6, 256, 256, False, 0.05, 0.02),
     (333, 2, 16, 1, True, 0.1, 0.05),
     (1 << 21, 8, 128, 128, False, 0.0, 0.0),     # 2^24 pairs (64 MiB of ids)
+    ((1 << 22) + 3, 8, 128, 128, False, 0.01, 0.01),   # several batch pairs per lane, ragged tail
+    (20000, 8, 1024, 1024, False, 0.01, 0.01),   # 16 slots per expert
+    (4096, 8, 4096, 1000, True, 0.02, 0.02),     # a map too long for LDS
+    (777, 3, 64, 63, True, 0.0, 0.0),            # odd El: the last expert alone
 ])
-def test_count_parity(M, T, Eg, El, mapped, p_neg, p_bad):
-    announce("count", M, T, Eg, El, mapped)
+@pytest.mark.parametrize("offset", [0, 1])       # 1: counts only 4-byte aligned
+def test_count_parity(M, T, Eg, El, mapped, p_neg, p_bad, offset):
+    if offset and M > 100000:
+        pytest.skip("the alignment case runs on the small shapes")
+    announce("count", M, T, Eg, El, mapped, offset)
     rng = np.random.default_rng(M + El)
     ids = gen.random_ids(rng, M, T, Eg, p_neg, p_bad)
     emap = None
     if mapped:
         emap = np.full(Eg, -1, np.int32)
         emap[rng.permutation(Eg)[:El]] = np.arange(El, dtype=np.int32)
-    counts = filled((El,), torch.int32, 12345)
+    counts = filled((El + offset,), torch.int32, 12345)[offset:]
     bad = filled((1,), torch.int32, 999)
     moe.moe_count(dev(ids), dev(emap) if mapped else None, Eg, El, counts, bad)
     cr, br = oracle.count(ids, emap, Eg, El)

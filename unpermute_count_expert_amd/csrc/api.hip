@@ -278,9 +278,10 @@ int moe_count(const int32_t* topk_ids, int64_t num_pairs, const int32_t* expert_
     REQUIRE(counts != nullptr && ((uintptr_t)counts & 3u) == 0, MOE_ERR_INVALID_ARG, "counts");
     REQUIRE(expert_map == nullptr || ((uintptr_t)expert_map & 3u) == 0, MOE_ERR_INVALID_ARG, "expert_map");
     REQUIRE(invalid_ids == nullptr || ((uintptr_t)invalid_ids & 3u) == 0, MOE_ERR_INVALID_ARG, "invalid_ids");
-    int st = check_device(nullptr);
+    int cus = 0;
+    int st = check_device(&cus);
     if (st) return st;
-    HIP_OK(moe::launch_count(topk_ids, num_pairs, expert_map, Eg, El, counts, invalid_ids,
+    HIP_OK(moe::launch_count(topk_ids, num_pairs, expert_map, Eg, El, counts, invalid_ids, cus,
                              static_cast<hipStream_t>(stream)));
     return MOE_OK;
 }

@@ -38,6 +38,12 @@ __global__ void k_fill_i32(int32_t* __restrict__ p, int64_t n, int32_t v) {
         p[i] = v;
 }
 
+// counts [El] and, when given, invalid [1] set to zero in one launch
+__global__ void k_count_clear(int32_t* __restrict__ counts, int El, int32_t* __restrict__ invalid) {
+    for (int e = threadIdx.x; e < El; e += blockDim.x) counts[e] = 0;
+    if (invalid && threadIdx.x == 0) invalid[0] = 0;
+}
+
 // The batched, masked layout: slot e holds rows [e * max_tokens,
 // (e + 1) * max_tokens), the first counts[e] of them valid.  offsets[e] =
 // e * max_tokens, cut[e] = counts[e] clamped to [0, max_tokens].
@@ -52,39 +58,91 @@ __global__ void k_slot_offsets(const int32_t* __restrict__ counts, int El, int64
     }
 }
 
-// Each wave of the block keeps its own LDS histogram (fewer conflicting
-// atomics), and each block adds its totals to counts with one global atomic
-// per expert.
-__global__ __launch_bounds__(256) void k_count(const int32_t* __restrict__ ids, int64_t num_pairs,
-                                               const int32_t* __restrict__ emap, int Eg, int El,
-                                               int32_t* __restrict__ counts,
-                                               int32_t* __restrict__ invalid) {
-    constexpr int kWaves = 256 / kWave;
-    __shared__ int h[kWaves][kMaxLocalExperts];
+// Tokens per local expert over a flat list of (token, k) expert ids.
+//
+// A block of kCountThreads keeps one LDS table of El x S counters, S slots
+// per expert (S a power of two, at most 64): lane l adds to slot l mod S of
+// its expert, so the adds of one wave spread over the banks whatever the ids
+// are (a plain El-word histogram makes lanes that draw nearby experts collide
+// on one bank).  The ids stream through 16-byte non-temporal loads, eight per
+// lane, the next eight in flight while the LDS adds count the last.  At the
+// end each block folds the slots and adds its totals to counts: two experts
+// per 64-bit atomic when the caller's counts are 8-byte aligned and no count
+// can pass 2^31 (then no carry crosses into the neighbour's word), else one
+// 32-bit atomic per expert.  Every block's adds meet on the same few cache
+// lines, where the memory side takes them one block at a time (about 15 ns
+// each, measured), so the launch uses at most one block per CU.
+constexpr int kCountThreads = 1024;
+constexpr int kCountLdsWords = 16384;   // the El x S table: 64 KiB
+
+__host__ __device__ inline int count_slots_log2(int El) {
+    int sl = 6;
+    while (sl > 0 && (El << sl) > kCountLdsWords) --sl;
+    return sl;
+}
+
+// MAP: kCountMapNone (local expert = id), kCountMapLds (the map staged in
+// LDS) or kCountMapGlobal (a map too long for LDS, read where it is).  The
+// first two keep global loads out of the counting, so the batch in flight is
+// never waited for early.
+enum { kCountMapNone = 0, kCountMapLds = 1, kCountMapGlobal = 2 };
+
+template <int MAP>
+__global__ __launch_bounds__(kCountThreads) void k_count(const int32_t* __restrict__ ids, int64_t num_pairs,
+                                                         const int32_t* __restrict__ emap, int Eg, int El,
+                                                         int slots_log2, int pack64,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ invalid) {
+    // h[e * S + slot]; the kWave words past the table take the adds of ids
+    // that are not local (one word per slot), so every id adds somewhere and
+    // the counting has no branches
+    __shared__ int h[kCountLdsWords + kWave];
+    __shared__ int s_map[MAP == kCountMapLds ? kMapLds + 1 : 1];   // [Eg] = -1
+    __shared__ int s_sum[kMaxLocalExperts];   // the block's total per expert
     __shared__ int bad;
-    for (int j = threadIdx.x; j < kWaves * El; j += blockDim.x) h[j / El][j % El] = 0;
-    if (threadIdx.x == 0) bad = 0;
+    const int S = 1 << slots_log2;
+    const int tid = threadIdx.x;
+    const int table = El << slots_log2;
+    for (int j = tid; j < table + S; j += kCountThreads) h[j] = 0;
+    if constexpr (MAP == kCountMapLds)
+        for (int j = tid; j <= Eg; j += kCountThreads) s_map[j] = j < Eg ? emap[j] : -1;
+    if (tid == 0) bad = 0;
     __syncthreads();
-    int* hw = h[threadIdx.x / kWave];
+    const int slot = tid & (S - 1);
     int my_bad = 0;
+    // The local expert as an unsigned value: anything at or past El (ids
+    // that are -1, not local or out of range) is clamped to El, the row of
+    // the table's spare words.  Invalid ids (below -1 or at least Eg) are
+    // counted apart.
     auto add = [&](int id) __attribute__((always_inline)) {
-        const int e = local_expert(id, emap, Eg, El);
-        if (e >= 0) atomicAdd(&hw[e], 1);
-        my_bad += (id < -1 || id >= Eg) ? 1 : 0;
+        my_bad += ((unsigned)id + 1u > (unsigned)Eg) ? 1 : 0;
+        unsigned e;
+        if constexpr (MAP == kCountMapNone)
+            e = (unsigned)id;   // El <= Eg without a map: ids in [El, Eg) are not local
+        else if constexpr (MAP == kCountMapLds)
+            e = (unsigned)s_map[min((unsigned)id, (unsigned)Eg)];
+        else
+            e = (unsigned)id < (unsigned)Eg ? (unsigned)emap[id] : 0xffffffffu;
+        atomicAdd(&h[(min(e, (unsigned)El) << slots_log2) | slot], 1);
     };
-    // 16-byte loads of four ids, four loads in flight per lane before the
-    // LDS atomics that consume them
-    constexpr int kLoads = 4;
-    const int4* ids4 = reinterpret_cast<const int4*>(ids);
+    // Full batches: kLoads vectors per lane, every one in bounds, so the
+    // loads are unconditional and the wait before counting a batch leaves
+    // the next batch in flight.  The rest (less than two batches of vectors,
+    // then the last num_pairs mod 4 ids) is read with bounds checks.
+    // (with a map read from global memory each count waits for its map
+    // loads, and with them for every load before: few vectors per batch)
+    constexpr int kLoads = MAP == kCountMapGlobal ? 2 : 8;
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    const v4i* ids4 = reinterpret_cast<const v4i*>(ids);
     const int64_t nvec = num_pairs / 4;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t v0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; v0 < nvec; v0 += kLoads * stride) {
-        int4 q[kLoads];
+    const int64_t stride = (int64_t)gridDim.x * kCountThreads;
+    const int64_t batch = kLoads * stride;
+    const int64_t lane_v = blockIdx.x * (int64_t)kCountThreads + tid;
+    auto load = [&](v4i (&q)[kLoads], int64_t v0) __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = 0; u < kLoads; ++u) {
-            const int64_t v = v0 + u * stride;
-            q[u] = v < nvec ? ids4[v] : int4{-1, -1, -1, -1};
-        }
+        for (int u = 0; u < kLoads; ++u) q[u] = __builtin_nontemporal_load(ids4 + v0 + u * stride);
+    };
+    auto count = [&](const v4i (&q)[kLoads]) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < kLoads; ++u) {
             add(q[u].x);
@@ -92,18 +150,73 @@ __global__ __launch_bounds__(256) void k_count(const int32_t* __restrict__ ids, 
             add(q[u].z);
             add(q[u].w);
         }
+    };
+    // batches go in pairs, A and B: B loads while A counts, then the next A
+    // while B counts; the scheduling barriers keep each batch's loads ahead
+    // of the counting they overlap
+    const int64_t npair = nvec / (2 * batch);
+    if (npair > 0) {
+        v4i qa[kLoads], qb[kLoads];
+        load(qa, lane_v);
+        for (int64_t p = 0; p + 1 < npair; ++p) {
+            load(qb, lane_v + (2 * p + 1) * batch);
+            __builtin_amdgcn_sched_barrier(0);
+            count(qa);
+            __builtin_amdgcn_sched_barrier(0);
+            load(qa, lane_v + (2 * p + 2) * batch);
+            __builtin_amdgcn_sched_barrier(0);
+            count(qb);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        load(qb, lane_v + (2 * npair - 1) * batch);
+        __builtin_amdgcn_sched_barrier(0);
+        count(qa);
+        count(qb);
     }
-    for (int64_t f = nvec * 4 + blockIdx.x * (int64_t)blockDim.x + threadIdx.x; f < num_pairs; f += stride)
-        add(ids[f]);
+    for (int64_t v = 2 * npair * batch + lane_v; v < nvec; v += stride) {
+        const v4i q = ids4[v];
+        add(q.x);
+        add(q.y);
+        add(q.z);
+        add(q.w);
+    }
+    for (int64_t f = nvec * 4 + lane_v; f < num_pairs; f += stride) add(ids[f]);
     if (my_bad) atomicAdd(&bad, my_bad);
     __syncthreads();
-    for (int e = threadIdx.x; e < El; e += blockDim.x) {
-        int c = 0;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) c += h[w][e];
-        if (c) atomicAdd(&counts[e], c);
+    // Fold: G consecutive lanes share expert e, each summing S / G of its
+    // slots (rotated by e, so that one wave's reads fall in distinct banks),
+    // then a shuffle reduction over the G lanes.
+    int g_log2 = 0;
+    while (g_log2 < slots_log2 && (El << (g_log2 + 1)) <= kCountThreads) ++g_log2;
+    const int G = 1 << g_log2;
+    const int e = tid >> g_log2;
+    const int part = tid & (G - 1);
+    const int per = S >> g_log2;
+    int c = 0;
+    if (e < El) {
+        const int* he = h + (e << slots_log2);
+        for (int j = 0; j < per; ++j) c += he[(part * per + j + e) & (S - 1)];
     }
-    if (threadIdx.x == 0 && invalid && bad) atomicAdd(invalid, bad);
+    for (int o = 1; o < G; o <<= 1) c += __shfl_xor(c, o);
+    if (e < El && part == 0) s_sum[e] = c;
+    __syncthreads();
+    // The block's totals leave from consecutive lanes over consecutive
+    // words (two experts per lane with 64-bit adds), so that each wave's
+    // atomics reach memory as few dense requests rather than many sparse
+    // ones: the adds of every block meet on these few hundred bytes.
+    if (pack64) {
+        const int pairs = El >> 1;
+        for (int q = tid; q < pairs; q += kCountThreads) {
+            const unsigned long long both = (unsigned long long)(unsigned)s_sum[2 * q] |
+                                            ((unsigned long long)(unsigned)s_sum[2 * q + 1] << 32);
+            if (both) atomicAdd(reinterpret_cast<unsigned long long*>(counts + 2 * q), both);
+        }
+        if ((El & 1) && tid == 0 && s_sum[El - 1]) atomicAdd(&counts[El - 1], s_sum[El - 1]);
+    } else {
+        for (int q = tid; q < El; q += kCountThreads)
+            if (s_sum[q]) atomicAdd(&counts[q], s_sum[q]);
+    }
+    if (tid == 0 && invalid && bad) atomicAdd(invalid, bad);
 }
 
 // Per-block histogram of local experts over the block's (token, k) pairs.
@@ -451,15 +564,27 @@ hipError_t launch_slot_offsets(const int32_t* counts, int El, int64_t max_tokens
 }
 
 hipError_t launch_count(const int32_t* ids, int64_t num_pairs, const int32_t* emap, int Eg, int El,
-                        int32_t* counts, int32_t* invalid, hipStream_t s) {
-    k_fill_i32<<<1, 256, 0, s>>>(counts, El, 0);
-    if (invalid) k_fill_i32<<<1, 64, 0, s>>>(invalid, 1, 0);
+                        int32_t* counts, int32_t* invalid, int num_cus, hipStream_t s) {
+    k_count_clear<<<1, 256, 0, s>>>(counts, El, invalid);
     if (num_pairs > 0) {
-        // few enough blocks that the per-block flush of the histogram (one
-        // global atomic per expert per block) stays small next to the reads
-        int64_t blocks = (num_pairs + 256 * 16 - 1) / (256 * 16);
-        if (blocks > 512) blocks = 512;
-        k_count<<<(unsigned)blocks, 256, 0, s>>>(ids, num_pairs, emap, Eg, El, counts, invalid);
+        // one 16-byte vector per lane until every CU has a block (small
+        // counts are latency-bound: the more lanes load at once the better),
+        // then at most one block per CU, each lane striding over the rest
+        const int64_t nvec = num_pairs / 4;
+        int64_t blocks = (nvec + kCountThreads - 1) / kCountThreads;
+        if (blocks < 1) blocks = 1;
+        if (blocks > num_cus) blocks = num_cus;
+        const int pack64 = ((uintptr_t)counts & 7u) == 0 && num_pairs <= INT32_MAX;
+        const int sl = count_slots_log2(El);
+        if (emap == nullptr)
+            k_count<kCountMapNone><<<(unsigned)blocks, kCountThreads, 0, s>>>(ids, num_pairs, emap, Eg, El, sl, pack64,
+                                                                         counts, invalid);
+        else if (Eg <= kMapLds)
+            k_count<kCountMapLds><<<(unsigned)blocks, kCountThreads, 0, s>>>(ids, num_pairs, emap, Eg, El, sl, pack64,
+                                                                        counts, invalid);
+        else
+            k_count<kCountMapGlobal><<<(unsigned)blocks, kCountThreads, 0, s>>>(ids, num_pairs, emap, Eg, El, sl, pack64,
+                                                                           counts, invalid);
     }
     return hipGetLastError();
 }

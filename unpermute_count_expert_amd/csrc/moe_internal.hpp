@@ -21,7 +21,7 @@ inline int64_t permute_num_blocks(int64_t Mc, int topk) {
 }
 
 hipError_t launch_count(const int32_t* ids, int64_t num_pairs, const int32_t* emap, int Eg, int El,
-                        int32_t* counts, int32_t* invalid, hipStream_t s);
+                        int32_t* counts, int32_t* invalid, int num_cus, hipStream_t s);
 
 // hist: [nblk, El] int32 scratch.  Writes counts, offsets, row_src padding,
 // and per-block row bases into hist.
