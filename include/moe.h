@@ -109,7 +109,9 @@ int moe_permute_workspace_size(int64_t Mc, int32_t topk, int32_t El, size_t* byt
  * topk_ids: [num_pairs] int32 global ids.  expert_map: [Eg] int32 or NULL
  * (identity, requires El <= Eg).  counts: [El] int32, overwritten.
  * invalid_ids: NULL or [1] int32, overwritten with the number of ids outside
- * [-1, Eg).  Exact integer counts. */
+ * [-1, Eg).  Exact integer counts.  topk_ids 16-byte aligned; counts and
+ * invalid_ids 4-byte aligned (counts 8-byte aligned lets the kernel add two
+ * experts' totals per atomic, which is faster on large inputs). */
 int moe_count(const int32_t* topk_ids, int64_t num_pairs, const int32_t* expert_map, int32_t Eg,
               int32_t El, int32_t* counts, int32_t* invalid_ids, void* stream);
 

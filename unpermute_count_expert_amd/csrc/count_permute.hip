@@ -32,12 +32,6 @@ constexpr int kMapLds = 2048;   // expert maps of up to this many global experts
 constexpr int kScanThreads = 1024;
 constexpr int kScanWaves = kScanThreads / kWave;
 
-__global__ void k_fill_i32(int32_t* __restrict__ p, int64_t n, int32_t v) {
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
-         i += (int64_t)gridDim.x * blockDim.x)
-        p[i] = v;
-}
-
 // counts [El] and, when given, invalid [1] set to zero in one launch
 __global__ void k_count_clear(int32_t* __restrict__ counts, int El, int32_t* __restrict__ invalid) {
     for (int e = threadIdx.x; e < El; e += blockDim.x) counts[e] = 0;
