@@ -152,12 +152,15 @@ int moe_quant_permute(const uint16_t* x, const int32_t* topk_ids, const float* t
                       float* a_perm_s, int32_t* counts, int32_t* expert_offsets, int32_t* inv_perm,
                       int32_t* row_src, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Output-tile rows (128 or 256) the grouped GEMM uses for rows_hint routed
- * rows over El local experts: 256 once the experts average at least 256 rows,
- * else 128.  moe_grouped_gemm_fp8 passes cap_rows as the hint and
- * moe_forward_chunked the chunk's token-expert pairs (Mc * topk).  The tile
- * changes only speed: outputs are identical either way.  Returns -1 when
- * El < 1. */
+/* Output-tile rows (128 or 256) the grouped GEMM entry points use for a
+ * row buffer of rows_hint rows over El local experts: 256 once it holds at
+ * least 256 rows per expert, else 128.  moe_grouped_gemm_fp8 (and the fused
+ * and reducing variants) pass cap_rows as the hint; for a buffer sized by
+ * moe_max_rows with 128-row alignment that is 256 tiles once the routed rows
+ * average about 129 per expert.  moe_forward_chunked knows its chunk's
+ * token-expert pairs (Mc * topk) and takes 256-row tiles once they average
+ * 104 per expert, the measured crossover.  The tile changes only speed:
+ * outputs are identical either way.  Returns -1 when El < 1. */
 int32_t moe_grouped_gemm_tile_rows(int64_t rows_hint, int32_t El);
 
 /* Block-scaled fp8 grouped GEMM (the DeepGEMM grouped GEMM of [P20903],

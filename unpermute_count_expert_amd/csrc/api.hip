@@ -399,7 +399,7 @@ int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const uint8_t* w, c
     int st = check_device(&cus);
     if (st) return st;
     HIP_OK(moe::launch_grouped_gemm(a, a_s, w, w_s, expert_offsets, counts, El, cap_rows, n_out, k_in, out,
-                                    cap_rows, cus, static_cast<hipStream_t>(stream)));
+                                    moe::gemm_tile_rows(cap_rows, El), cus, static_cast<hipStream_t>(stream)));
     return MOE_OK;
 }
 
@@ -444,7 +444,7 @@ int moe_grouped_gemm_fp8_weight_reduce(const uint8_t* a, const float* a_s, const
     if (cap_rows > 0)
         HIP_OK(moe::launch_grouped_gemm_reduce(a, a_s, w, w_s, expert_offsets, counts, El, cap_rows, n_out, k_in, y,
                                                row_src, inv_perm, topk_weights, apply_on_input, Mc, topk, counters,
-                                               out, cap_rows, cus, s));
+                                               out, moe::gemm_tile_rows(cap_rows, El), cus, s));
     return MOE_OK;
 }
 
@@ -471,7 +471,8 @@ int moe_grouped_gemm_fp8_act_quant(const uint8_t* a, const float* a_s, const uin
     int st = check_device(&cus);
     if (st) return st;
     HIP_OK(moe::launch_grouped_gemm_act(a, a_s, w13, w13_s, expert_offsets, counts, El, cap_rows, N, k_in, q,
-                                        q_s, cap_rows, cus, static_cast<hipStream_t>(stream)));
+                                        q_s, moe::gemm_tile_rows(cap_rows, El), cus,
+                                        static_cast<hipStream_t>(stream)));
     return MOE_OK;
 }
 
@@ -677,7 +678,8 @@ int forward_chunk(const moe_problem& P, const Plan& pl, int64_t c, const uint16_
                                               pl.smax13, info, cus, s));
     } else {
         HIP_OK(moe::launch_grouped_gemm(bufA, bufAs, w13, w13_s, offsets, counts, (int)El, pl.cap,
-                                        (int)(2 * N), (int)K, hy, Mc * T, cus, s));
+                                        (int)(2 * N), (int)K, hy, moe::gemm_tile_rows_routed(Mc * T, (int)El), cus,
+                                        s));
     }
     if (split13) {
         HIP_OK(moe::launch_act_quant_part(part, info, pl.part_rows, pl.smax13, pl.cap, (int)N, offsets, counts,
@@ -692,7 +694,7 @@ int forward_chunk(const moe_problem& P, const Plan& pl, int64_t c, const uint16_
                                               cus, s));
     } else {
         HIP_OK(moe::launch_grouped_gemm(bufA, bufAs, w2, w2_s, offsets, counts, (int)El, pl.cap, (int)K,
-                                        (int)N, hy, Mc * T, cus, s));
+                                        (int)N, hy, moe::gemm_tile_rows_routed(Mc * T, (int)El), cus, s));
     }
     if (split2) {
         HIP_OK(moe::launch_unpermute_part(part, info + 1, pl.part_rows, pl.smax2, offsets, counts, (int)El,
@@ -906,9 +908,10 @@ int moe_experts_batched_masked(const uint8_t* a_q, const float* a_s, const int32
     HIP_OK(moe::launch_slot_offsets(counts, El, max_tokens, offsets, cut, s));
     // gate/up GEMM with the SiLU-mul requant in its epilogue: h never
     // reaches memory
-    HIP_OK(moe::launch_grouped_gemm_act(a_q, a_s, w13, w13_s, offsets, cut, El, rows, N, K, act_q, act_s, rows,
-                                        cus, s));
-    HIP_OK(moe::launch_grouped_gemm(act_q, act_s, w2, w2_s, offsets, cut, El, rows, K, N, out, rows, cus, s));
+    HIP_OK(moe::launch_grouped_gemm_act(a_q, a_s, w13, w13_s, offsets, cut, El, rows, N, K, act_q, act_s,
+                                        moe::gemm_tile_rows(rows, El), cus, s));
+    HIP_OK(moe::launch_grouped_gemm(act_q, act_s, w2, w2_s, offsets, cut, El, rows, K, N, out,
+                                    moe::gemm_tile_rows(rows, El), cus, s));
     return MOE_OK;
 }
 

@@ -874,17 +874,24 @@ int64_t gemm_grid(int64_t cap_rows, int El, int n_out, int bm, int num_cus, int 
 
 // 256-row tiles move fewer bytes per flop, but every 16-row block of an
 // active wave is computed, so experts of a few rows are cheaper on 128-row
-// tiles (measured: 4 rows per expert, 0.042 vs 0.054 ms; 256 rows per
-// expert, 0.210 vs 0.218 ms; 1024, 0.53 vs 0.62 ms).
+// tiles.  Measured with hidden size 2048, intermediate size 768, 128 experts
+// and top-8 routing (ms, 128-row vs 256-row tiles, gate/up GEMM): 80 routed
+// rows per expert 0.081 vs 0.087, 96 rows 0.083 vs 0.090, 112 rows 0.103 vs
+// 0.094, 128 rows 0.117 vs 0.101, 192 rows 0.133 vs 0.114, 256 rows 0.182
+// vs 0.167, 384 rows 0.238 vs 0.199 (the down GEMM alike).
 int gemm_tile_rows(int64_t rows_hint, int El) {
     return (El > 0 && rows_hint >= (int64_t)256 * El) ? 256 : 128;
+}
+
+int gemm_tile_rows_routed(int64_t pairs, int El) {
+    return (El > 0 && pairs >= (int64_t)104 * El) ? 256 : 128;
 }
 
 hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_s, const uint8_t* w,
                                const float* w_s, const int32_t* offsets, const int32_t* counts,
                                int El, int64_t cap_rows, int n_out, int k_in, uint16_t* out,
-                               int64_t rows_hint, int num_cus, hipStream_t s) {
-    if (gemm_tile_rows(rows_hint, El) == 256) {
+                               int tile_rows, int num_cus, hipStream_t s) {
+    if (tile_rows == 256) {
         const int64_t grid = gemm_grid(cap_rows, El, n_out, Shape<8>::BM, num_cus);
         k_grouped_gemm<false, 8><<<(unsigned)grid, kThreads, 0, s>>>(a, a_s, w, w_s, offsets, counts, El,
                                                                       cap_rows, n_out, k_in, out, nullptr, nullptr, ReduceArgs{}, SplitArgs{});
@@ -911,10 +918,10 @@ hipError_t launch_grouped_gemm_reduce(const uint8_t* a, const float* a_s, const 
                                       const int32_t* offsets, const int32_t* counts, int El, int64_t cap_rows,
                                       int n_out, int k_in, uint16_t* y, const int32_t* row_src,
                                       const int32_t* inv_perm, const float* topk_w, int on_input, int64_t Mc,
-                                      int topk, int32_t* cnt, uint16_t* out, int64_t rows_hint, int num_cus,
+                                      int topk, int32_t* cnt, uint16_t* out, int tile_rows, int num_cus,
                                       hipStream_t s) {
     const ReduceArgs red{row_src, inv_perm, topk_w, on_input, topk, Mc, cnt, out};
-    if (gemm_tile_rows(rows_hint, El) == 256) {
+    if (tile_rows == 256) {
         const int64_t grid = gemm_grid(cap_rows, El, n_out, Shape<8>::BM, num_cus);
         k_grouped_gemm<false, 8, true><<<(unsigned)grid, kThreads, 0, s>>>(a, a_s, w, w_s, offsets, counts, El,
                                                                             cap_rows, n_out, k_in, y, nullptr,
@@ -931,8 +938,8 @@ hipError_t launch_grouped_gemm_reduce(const uint8_t* a, const float* a_s, const 
 hipError_t launch_grouped_gemm_act(const uint8_t* a, const float* a_s, const uint8_t* w13,
                                    const float* w13_s, const int32_t* offsets, const int32_t* counts,
                                    int El, int64_t cap_rows, int N, int k_in, uint8_t* q, float* q_s,
-                                   int64_t rows_hint, int num_cus, hipStream_t s) {
-    if (gemm_tile_rows(rows_hint, El) == 256) {
+                                   int tile_rows, int num_cus, hipStream_t s) {
+    if (tile_rows == 256) {
         const int64_t grid = gemm_grid(cap_rows, El, 2 * N, Shape<8>::BM, num_cus);
         k_grouped_gemm<true, 8><<<(unsigned)grid, kThreads, 0, s>>>(a, a_s, w13, w13_s, offsets, counts, El,
                                                                      cap_rows, 2 * N, k_in, nullptr, q, q_s, ReduceArgs{}, SplitArgs{});

@@ -61,13 +61,19 @@ hipError_t launch_act_quant_part(const float* part, const int32_t* info, int64_t
                                  int64_t rows_hint, hipStream_t s);
 
 // ---- grouped GEMM ------------------------------------------------------------
-// Output-tile rows of the plain GEMM for rows_hint routed rows over El
-// experts: 256 once the experts average 256 rows, else 128.
+// Output-tile rows (128 or 256) of the plain, fused and reducing GEMMs.
+// gemm_tile_rows: from a row-buffer bound (the GEMM entry points' cap_rows,
+// which for a buffer sized by moe_max_rows with 128-row alignment holds up to
+// 127 padding rows per expert): 256 once it reaches 256 rows per expert.
+// gemm_tile_rows_routed: from the routed pairs themselves (the forward's
+// Mc * topk): 256 once they average 104 rows per expert, the measured
+// crossover.
 int gemm_tile_rows(int64_t rows_hint, int El);
+int gemm_tile_rows_routed(int64_t pairs, int El);
 hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_s, const uint8_t* w,
                                const float* w_s, const int32_t* offsets, const int32_t* counts,
                                int El, int64_t cap_rows, int n_out, int k_in, uint16_t* out,
-                               int64_t rows_hint, int num_cus, hipStream_t s);
+                               int tile_rows, int num_cus, hipStream_t s);
 
 // Output-tile rows of the GEMMs of a chunk of rows_hint routed rows over El
 // experts: 64 (launch_grouped_gemm_small) while the experts average at most
@@ -100,7 +106,7 @@ inline int gemm_split_segments(int k_in) {
 hipError_t launch_grouped_gemm_act(const uint8_t* a, const float* a_s, const uint8_t* w13,
                                    const float* w13_s, const int32_t* offsets, const int32_t* counts,
                                    int El, int64_t cap_rows, int N, int k_in, uint8_t* q, float* q_s,
-                                   int64_t rows_hint, int num_cus, hipStream_t s);
+                                   int tile_rows, int num_cus, hipStream_t s);
 
 // The down GEMM with the unpermute's weight-and-reduce in its epilogue: y
 // [cap_rows, n_out] as launch_grouped_gemm, and out [Mc, n_out] as
@@ -110,7 +116,7 @@ hipError_t launch_grouped_gemm_reduce(const uint8_t* a, const float* a_s, const 
                                       const int32_t* offsets, const int32_t* counts, int El, int64_t cap_rows,
                                       int n_out, int k_in, uint16_t* y, const int32_t* row_src,
                                       const int32_t* inv_perm, const float* topk_w, int on_input, int64_t Mc,
-                                      int topk, int32_t* cnt, uint16_t* out, int64_t rows_hint, int num_cus,
+                                      int topk, int32_t* cnt, uint16_t* out, int tile_rows, int num_cus,
                                       hipStream_t s);
 // Zeroes cnt [Mc, ceil(K / 256)] and writes +0 output rows for the tokens
 // without a valid row.
