@@ -290,8 +290,21 @@ def test_forward_workspace_slices_leave_guard_bands():
     (dict(M=8192, K=2048, N=768, topk=8, Eg=128, El=64, chunk_size=64),
      dict(small_tiles=True, nsplit_w13=2, nsplit_w2=1, part_rows=512, lanes=2)),
     # a down projection of 16 groups is cut too
-    (dict(M=64, K=2048, N=2048, topk=8, Eg=64, El=64), dict(small_tiles=True, nsplit_w13=2, nsplit_w2=2,
-                                                          part_rows=512, lanes=1)),
+    (dict(M=64, K=2048, N=2048, topk=2, Eg=64, El=16), dict(small_tiles=True, nsplit_w13=2, nsplit_w2=2,
+                                                          part_rows=128, lanes=1)),
+    # the same layer with 64 experts all local: 64 touched experts x 16 gate/up
+    # n-tiles fill the chip, so the larger tiles, K whole
+    (dict(M=64, K=2048, N=2048, topk=8, Eg=64, El=64), dict(small_tiles=False, nsplit_w13=1, nsplit_w2=1,
+                                                          part_rows=0, lanes=1)),
+    # 64 tokens, topk 8, all 128 experts local: ~126 touched experts x 6 tiles
+    (dict(M=64, K=2048, N=768, topk=8, Eg=128, El=128), dict(small_tiles=False, nsplit_w13=1, nsplit_w2=1,
+                                                           part_rows=0, lanes=1)),
+    # 384 tokens over 64 of 128 experts (48 pairs per local expert): small tiles
+    (dict(M=384, K=2048, N=768, topk=8, Eg=128, El=64), dict(small_tiles=True, nsplit_w13=2, nsplit_w2=1,
+                                                           part_rows=3072, lanes=1)),
+    # 512 tokens: past 48 pairs per local expert
+    (dict(M=512, K=2048, N=768, topk=8, Eg=128, El=64), dict(small_tiles=False, nsplit_w13=1, nsplit_w2=1,
+                                                           part_rows=0, lanes=1)),
     # 4096 tokens, topk 8, 128 experts (256 rows each): the 128/256-row GEMMs, K whole
     (dict(M=4096, K=2048, N=768, topk=8, Eg=128, El=128), dict(small_tiles=False, nsplit_w13=1, nsplit_w2=1,
                                                              part_rows=0, lanes=1)),

@@ -143,7 +143,7 @@ Plan make_plan(const moe_problem& p, bool allow_lanes = true) {
     // the split: the segments of gemm_split_segments, fewer (still dividing
     // K / 128) where the budget holds fewer partials
     const int64_t pairs = pl.cs * p.topk;
-    pl.small = moe::gemm_small_chunk(pairs, (int)El);
+    pl.small = moe::gemm_small_chunk(pairs, (int)El, p.num_global_experts, (int)(2 * N));
     auto segments = [&](int k_in, int64_t n) {
         if (!pl.small) return 1;
         const int64_t fit = (int64_t)(kPartBudget / ((size_t)pairs * (size_t)n * 4));
