@@ -11,16 +11,21 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libmoe_ref.so")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, sanitize: bool = False) -> str:
+    """sanitize: AddressSanitizer + UndefinedBehaviorSanitizer instrumentation
+    (-O1 -g; the process that loads it needs the sanitizer runtimes
+    preloaded), for the sanitizer test; out names that build's file."""
     src = os.path.join(HERE, "moe_ref.c")
-    cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+    opt = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=undefined"] if sanitize else ["-O2"]
+    cmd = ["gcc", "-std=c11", *opt, "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
            "-fPIC", "-shared", "-Wall", "-Wextra", "-Wno-unused-parameter",
-           src, "-o", LIB + ".tmp", "-lm"]
+           src, "-o", out + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.check_call(cmd)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":

@@ -12,7 +12,9 @@ from typing import Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libmoe_ref.so")
+# MOE_REF_LIB: another build of the same source (the sanitizer test loads one
+# built with AddressSanitizer and UndefinedBehaviorSanitizer)
+_LIB_PATH = os.environ.get("MOE_REF_LIB") or os.path.join(_HERE, "libmoe_ref.so")
 _lib = None
 
 GROUP = 128
