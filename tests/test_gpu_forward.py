@@ -356,6 +356,18 @@ CASES = [
     # the most local experts the library takes (1024), ~16 rows each
     ("max_experts_1024", gen.small_config(M=2048, K=256, N=128, Eg=1024, El=1024, topk=8, chunk_size=0,
                                           routing="softmax", seed=23), 0),
+    # 128 pairs per expert: the forward takes 256-row tiles (from 104 pairs
+    # per expert on) where the op-by-op chain, sized by its row buffer, takes
+    # 128-row ones; the two must agree bit for bit
+    ("mid_2048_tokens", gen.small_config(M=2048, K=2048, N=768, Eg=128, El=128, topk=8, chunk_size=0,
+                                         routing="softmax", seed=26), 0),
+    # 64 tokens over 128 local experts: the 128-row GEMMs (~126 touched
+    # experts fill the chip), not the small-chunk tiles
+    ("all_local_64_tokens", gen.small_config(M=64, K=2048, N=768, Eg=128, El=128, topk=8, chunk_size=0,
+                                             routing="softmax", seed=27), 0),
+    # 384 tokens over 64 of 128 local experts: still the small-chunk tiles
+    ("ep_half_384_tokens", gen.small_config(M=384, K=2048, N=768, Eg=128, El=64, topk=8, chunk_size=0,
+                                            routing="softmax", seed=28, ep_rank_of_2=1), 0),
 ]
 
 
