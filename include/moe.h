@@ -91,8 +91,9 @@ int moe_forward_workspace_size(const moe_problem* p, size_t* bytes);
  * their scales, h then y, counts, offsets, inv_perm, row_src, the permute's
  * per-block histogram, the fp32 partial sums of the GEMMs with K split for
  * small chunks (empty when the plan splits neither GEMM) and the two
- * GEMMs' segment counts), times the lanes (two with two chunks or more:
- * the second lane's ten slices follow the first's, in the same order); the
+ * GEMMs' segment counts), times the lanes (min(chunks, 3) with two chunks
+ * or more: each lane's ten slices follow the previous lane's, in the same
+ * order); the
  * first min(max_slices, *num_slices) byte offsets
  * and lengths are written to offsets[] and bytes[].  Between the end of a
  * slice and the next slice's offset (and up to the workspace size after the
@@ -287,11 +288,14 @@ int moe_unpermute_partials(const float* part, const int32_t* info, int64_t part_
                            int32_t apply_on_input, uint16_t* out, void* stream);
 
 /* How moe_forward_chunked runs problem p: *small_tiles = 1 when its chunks
- * take moe_grouped_gemm_fp8_small (at most 64 routed rows per local expert
- * on average); *nsplit_w13 / *nsplit_w2 the K segments those GEMMs are
- * given (1: K whole, bf16 h / y), *part_rows the rows of the partial
- * slabs (0 without a cut), *lanes the chunk lanes (2 with two chunks or
- * more).  Any output pointer may be NULL. */
+ * take moe_grouped_gemm_fp8_small (a chunk's token-expert pairs average at
+ * most 48 per local expert, and the gate/up GEMM would have fewer than 512
+ * tiles of 128 or 256 rows: the local experts that uniform routing over the
+ * Eg experts would touch, times its 256-column tiles); *nsplit_w13 /
+ * *nsplit_w2 the K segments those GEMMs are given (1: K whole, bf16 h / y),
+ * *part_rows the rows of the partial slabs (0 without a cut), *lanes the
+ * chunk lanes (min(chunks, 3) with two chunks or more).  Any output pointer
+ * may be NULL. */
 int moe_forward_plan_info(const moe_problem* p, int32_t* small_tiles, int32_t* nsplit_w13, int32_t* nsplit_w2,
                           int64_t* part_rows, int32_t* lanes);
 
@@ -305,13 +309,13 @@ int moe_forward_plan_info(const moe_problem* p, int32_t* small_tiles, int32_t* n
  * e4m3, w2_s [El,K/128,N/128] f32, out [M,K] bf16, workspace >=
  * moe_forward_workspace_size(p).  per_chunk_counts: NULL or device
  * [num_chunks, El] int32 receiving each chunk's counts.
- * Chunks of at most 64 routed rows per expert take the small-tile GEMMs
- * (moe_forward_plan_info).  With two chunks or more, consecutive chunks
- * alternate between two copies of the workspace slices and two library
- * streams (created on the first such call on a device and kept), which wait
- * for the work enqueued on `stream` before the call, and on which `stream`
- * waits after it: every chunk computes what it computes alone, and work
- * enqueued on `stream` afterwards sees the whole output. */
+ * Small chunks take the small-tile GEMMs (moe_forward_plan_info).  With
+ * two chunks or more, consecutive chunks go round-robin to min(chunks, 3)
+ * copies of the workspace slices and as many library streams (created on
+ * the first such call on a device and kept), which wait for the work
+ * enqueued on `stream` before the call, and on which `stream` waits after
+ * it: every chunk computes what it computes alone, and work enqueued on
+ * `stream` afterwards sees the whole output. */
 int moe_forward_chunked(const moe_problem* p, const uint16_t* x, const int32_t* topk_ids,
                         const float* topk_weights, const int32_t* expert_map, const uint8_t* w13,
                         const float* w13_s, const uint8_t* w2, const float* w2_s, uint16_t* out,

@@ -286,9 +286,12 @@ def test_forward_workspace_slices_leave_guard_bands():
     # 64 tokens, topk 4, 64 local experts: small tiles, w13 K (16 groups) in two, w2 K (6 groups) whole
     (dict(M=64, K=2048, N=768, topk=4, Eg=128, El=64), dict(small_tiles=True, nsplit_w13=2, nsplit_w2=1,
                                                           part_rows=256, lanes=1)),
-    # 8192 tokens in chunks of 64: the same per chunk, and two lanes
+    # 8192 tokens in chunks of 64: the same per chunk, and three lanes
     (dict(M=8192, K=2048, N=768, topk=8, Eg=128, El=64, chunk_size=64),
-     dict(small_tiles=True, nsplit_w13=2, nsplit_w2=1, part_rows=512, lanes=2)),
+     dict(small_tiles=True, nsplit_w13=2, nsplit_w2=1, part_rows=512, lanes=3)),
+    # two chunks: two lanes
+    (dict(M=130, K=2048, N=768, topk=8, Eg=128, El=64, chunk_size=128),
+     dict(small_tiles=True, nsplit_w13=2, nsplit_w2=1, part_rows=1024, lanes=2)),
     # a down projection of 16 groups is cut too
     (dict(M=64, K=2048, N=2048, topk=2, Eg=64, El=16), dict(small_tiles=True, nsplit_w13=2, nsplit_w2=2,
                                                           part_rows=128, lanes=1)),
@@ -322,9 +325,9 @@ def test_noalloc_plan_stays_in_one_lane():
     # chunked problems need two lanes' slices from moe_forward_chunked but one
     # from the scratch of the no-alloc entry: its size check uses one lane
     p = moe.problem(8192, 2048, 768, 8, 128, 64, chunk_size=64)
-    assert moe.moe_forward_plan_info(p)["lanes"] == 2
+    assert moe.moe_forward_plan_info(p)["lanes"] == 3
     sl = moe.moe_forward_workspace_slices(p)
-    assert moe.moe_forward_workspace_size(p) == 2 * sl[10][0]
+    assert moe.moe_forward_workspace_size(p) == 3 * sl[10][0]
 
 
 def test_noalloc_forward_rejects_a_problem_beyond_the_scratch():

@@ -119,10 +119,19 @@ size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr size_t kGuard = 256;
 constexpr int kSlices = 10;
 constexpr size_t kPartBudget = size_t(64) << 20;
+// Chunk lanes: consecutive chunks go round-robin to this many library streams,
+// each with its own copy of the workspace slices, so that one chunk's
+// latency-bound kernels overlap the next chunks' work.  Three: HIP gives a
+// process four hardware queues by default, one of them the caller's stream;
+// with a fourth lane two streams share a queue and serialise.  Measured
+// (ms; 2, 3, 4 lanes): 8192 tokens in chunks of 64, 6.06 / 4.82 / 6.07;
+// 16384 tokens in chunks of 512, 4.23 / 3.94 / 4.17, of 2048, 1.670 / 1.657 /
+// 1.684 (one lane: 4.85 and 1.85).
+constexpr int kLanes = 3;
 
 struct Plan {
     int64_t cs, cap, nblk;
-    int lanes;               // 1, or 2 with two chunks or more
+    int lanes;               // 1, or min(chunks, kLanes) with two chunks or more
     size_t one;              // bytes of one lane's slices
     size_t bufA, bufAs, bufB, counts, offsets, inv, rsrc, hist, part, info, total;
     bool small;              // the GEMMs on 64-row tiles
@@ -184,7 +193,8 @@ Plan make_plan(const moe_problem& p, bool allow_lanes = true) {
     pl.part = pl.off[8];
     pl.info = pl.off[9];
     pl.one = off;
-    pl.lanes = (allow_lanes && p.M > pl.cs) ? 2 : 1;
+    const int64_t nchunks = (p.M + pl.cs - 1) / pl.cs;
+    pl.lanes = (allow_lanes && nchunks > 1) ? (int)(nchunks < kLanes ? nchunks : kLanes) : 1;
     pl.total = off * pl.lanes;
     return pl;
 }
@@ -623,15 +633,15 @@ int moe_forward_plan_info(const moe_problem* p, int32_t* small_tiles, int32_t* n
 
 namespace {
 
-// The two library streams of a device and the events that fork them from and
-// join them to the caller's stream; created on first use and kept.  The
-// mutex covers one call's enqueue: a wait on an event takes the event as last
-// recorded before the wait, so the next call may record it again.
+// The library's chunk-lane streams of a device and the events that fork them
+// from and join them to the caller's stream; created on first use and kept.
+// The mutex covers one call's enqueue: a wait on an event takes the event as
+// last recorded before the wait, so the next call may record it again.
 struct LaneStreams {
     std::mutex mu;
     bool ready = false;
-    hipStream_t s[2] = {nullptr, nullptr};
-    hipEvent_t fork = nullptr, join[2] = {nullptr, nullptr};
+    hipStream_t s[kLanes] = {};
+    hipEvent_t fork = nullptr, join[kLanes] = {};
 };
 LaneStreams g_lanes[kMaxDevices];
 
@@ -725,28 +735,28 @@ int forward_impl(const moe_problem& P, const Plan& pl, const uint16_t* x, const 
     if (st) return st;
     std::lock_guard<std::mutex> lock(L->mu);
     if (!L->ready) {
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < kLanes; ++i) {
             HIP_OK(hipStreamCreateWithFlags(&L->s[i], hipStreamNonBlocking));
             HIP_OK(hipEventCreateWithFlags(&L->join[i], hipEventDisableTiming));
         }
         HIP_OK(hipEventCreateWithFlags(&L->fork, hipEventDisableTiming));
         L->ready = true;
     }
+    const int nl = pl.lanes;   // <= kLanes and <= nchunks
     HIP_OK(hipEventRecord(L->fork, s));
-    HIP_OK(hipStreamWaitEvent(L->s[0], L->fork, 0));
-    HIP_OK(hipStreamWaitEvent(L->s[1], L->fork, 0));
+    for (int i = 0; i < nl; ++i) HIP_OK(hipStreamWaitEvent(L->s[i], L->fork, 0));
     // the lanes run free: holding chunk c + 1 until chunk c's gate/up GEMM is
     // done was measured slower (8192 tokens in chunks of 64: 6.7 against
     // 6.1 ms)
     for (int64_t c = 0; c < nchunks; ++c) {
-        const int lane = (int)(c & 1);
+        const int lane = (int)(c % nl);
         st = forward_chunk(P, pl, c, x, topk_ids, topk_weights, expert_map, w13, w13_s, w2, w2_s, out,
                            ws + lane * pl.one, per_chunk_counts, cus, L->s[lane]);
         if (st) break;
     }
     // joined even after a failed launch, so the caller's stream never runs
     // ahead of work already enqueued on the lanes
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < nl; ++i) {
         HIP_OK(hipEventRecord(L->join[i], L->s[i]));
         HIP_OK(hipStreamWaitEvent(s, L->join[i], 0));
     }
