@@ -4,8 +4,8 @@
 // the two grouped GEMMs.
 //
 // Sixteen lanes own one group (8 bf16 = 16 bytes each, fully coalesced); the
-// group amax is a 4-step xor-shuffle inside the 16 lanes; codes leave as one
-// 8-byte store per lane.  Compiled without FMA contraction so each operation
+// group amax is a DPP maximum over the 16 lanes; codes leave as one 8-byte
+// store per lane.  Compiled without FMA contraction so each operation
 // below is the IEEE operation written.
 //
 // SiLU of a bf16 gate value is a function of 16 bits, so each block first

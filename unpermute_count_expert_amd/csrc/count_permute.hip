@@ -271,53 +271,89 @@ __global__ __launch_bounds__(kScanThreads) void k_permute_colscan(int32_t* __res
     }
 }
 
+// What the scatter's loads of items past the end read (never written; not
+// const, so that they sit in the global address space with the kernel's
+// pointers and a choice between the two is still a global load).
+__device__ int32_t g_fill_neg1[1] = {-1};
+__device__ int32_t g_fill_zero[1] = {0};
+__device__ float g_fill_one[1] = {1.0f};
+__device__ __attribute__((aligned(16))) uint32_t g_fill_zero16[4] = {0u, 0u, 0u, 0u};
+
 // Stable rank of every local pair, inverse indices, then the row copies.
 // QUANT: the rows come from bf16 x [Mc, K] and are quantised here (per
 // 1x128 group, exactly as the identity act quant), so a_q / a_s are never
-// written or read; otherwise they are copied from a_q / a_s.
-template <bool QUANT>
+// written or read; otherwise they are copied from a_q / a_s.  GMAP: the
+// expert map has too many entries for LDS and is read from global memory.
+// SELF: few pairs, so every block counts all of the chunk's pairs itself
+// (no histogram launches); otherwise the counts and this block's row bases
+// come from the column scan.  Every global read is issued first (the block's ids and router weights, the
+// chunk's ids or the block's counts and row bases, the expert map, the first
+// batch of rows), and that batch is quantised as soon as it arrives, before
+// the first store: a wait for a load issued after a store waits for the
+// store as well, so the count, scan and rank that follow use LDS alone and
+// every store leaves after them.
+template <bool QUANT, bool GMAP, bool SELF>
 __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
     const uint8_t* __restrict__ a_q, const float* __restrict__ a_s, const uint16_t* __restrict__ x,
     const int32_t* __restrict__ ids,
     const float* __restrict__ topk_w, int apply_on_input, int64_t Mc, int K, int topk, int tpb,
     const int32_t* __restrict__ emap, int Eg, int El, int nbits, const int32_t* __restrict__ base,
-    int32_t* __restrict__ counts, int32_t* __restrict__ counts_copy, int self_count, int align,
+    int32_t* __restrict__ counts, int32_t* __restrict__ counts_copy, int align,
     int64_t cap_rows, int32_t* __restrict__ offsets,
     uint8_t* __restrict__ a_perm, float* __restrict__ a_perm_s, int32_t* __restrict__ inv_perm,
     int32_t* __restrict__ row_src) {
     constexpr int kWaves = kPermThreads / kWave;
     constexpr int kBatch = 8;
-    constexpr int kSelfLoads = 16;   // self_count: at most 16 * 256 pairs
+    constexpr int kSelfLoads = 16;                                  // SELF: at most 16 * 256 pairs
+    constexpr int kExPerThread = kMaxLocalExperts / kPermThreads;   // experts 4 * tid + j
+    constexpr int kMapPerThread = GMAP ? 1 : kMapLds / kPermThreads;
     __shared__ int wcnt[kWaves][kMaxLocalExperts];
     __shared__ int rowmap[kPermThreads];
+    __shared__ float s_tw[kPermThreads];       // the block's router weights (apply_on_input)
     __shared__ int s_off[kMaxLocalExperts + 1];
     __shared__ int s_wsum[kWaves];
-    __shared__ int s_cnt[kMaxLocalExperts];    // self_count: the counts
-    __shared__ int s_base[kMaxLocalExperts];   // self_count: pairs of each expert before this block
-    __shared__ int s_map[kMapLds];             // expert_map, when it fits
+    __shared__ int s_cnt[kMaxLocalExperts];    // the counts
+    __shared__ int s_base[kMaxLocalExperts];   // pairs of each expert before this block
+    __shared__ int s_map[GMAP ? 1 : kMapLds + 1];   // expert_map, when there is one; [kMapLds] = -1
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
 
-    // ---- everything read from global memory up front, so that the
-    // latencies overlap: this block's ids, the expert map, the pair ids of the
-    // whole chunk (self_count) and the first batch of token rows
+    // ---- every global read, issued before the first wait and none of them
+    // conditional (an item past the end reads one of the fill constants
+    // instead), so that the compiler knows how many loads follow each one
+    // and a wait covers only the loads it needs: the rows, loaded last, are
+    // still in flight while the count, scan and rank run
     const int64_t t0 = (int64_t)blockIdx.x * tpb;
     const int ntok = (int)((Mc - t0) < tpb ? (Mc - t0) : tpb);
     const int npairs = ntok * topk;
     const int i = threadIdx.x;
     const bool active = i < npairs;
     const int64_t f = t0 * topk + i;
-    const int own_id = active ? ids[f] : -1;
-    const bool map_lds = emap != nullptr && Eg <= kMapLds;
-    if (map_lds)
-        for (int j = threadIdx.x; j < Eg; j += blockDim.x) s_map[j] = emap[j];
+    const int own_id = *(active ? ids + f : g_fill_neg1);
+    const float own_w = *(active && apply_on_input ? topk_w + f : g_fill_one);
     const int64_t np = Mc * topk;
-    int sid[kSelfLoads];
-    if (self_count) {
+    int sid[SELF ? kSelfLoads : 1];
+    int cb[2][SELF ? 1 : kExPerThread];   // not SELF: counts and this block's row bases
+    if constexpr (SELF) {
 #pragma unroll
         for (int u = 0; u < kSelfLoads; ++u) {
             const int64_t f2 = threadIdx.x + (int64_t)u * kPermThreads;
-            sid[u] = f2 < np ? ids[f2] : -1;
+            sid[u] = *(f2 < np ? ids + f2 : g_fill_neg1);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kExPerThread; ++j) {
+            const int ex = threadIdx.x * kExPerThread + j;
+            cb[0][j] = *(ex < El ? counts + ex : g_fill_zero);
+            cb[1][j] = *(ex < El ? base + (int64_t)blockIdx.x * El + ex : g_fill_zero);
+        }
+    }
+    int mv[kMapPerThread];
+    if constexpr (!GMAP) {
+#pragma unroll
+        for (int m = 0; m < kMapPerThread; ++m) {
+            const int j = threadIdx.x + m * kPermThreads;
+            mv[m] = *(emap != nullptr && j < Eg ? emap + j : g_fill_neg1);
         }
     }
     // this block's slice of the K groups: [g_lo, g_lo + ng)
@@ -348,58 +384,93 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
         for (int u = 0; u < kBatch; ++u) {
             int tl, gc;
             const int q = item(q0, u, tl, gc);
-            v[u] = uint4{0, 0, 0, 0};
-            if (q < items) {
-                if constexpr (QUANT)
-                    v[u] = load_once16(x + (t0 + tl) * K + (int64_t)gc * kGroup + sub * 8);
-                else
-                    v[u] = load_once16(a_q + (t0 + tl) * K + (int64_t)gc * 16);
+            const void* src = g_fill_zero16;
+            if constexpr (QUANT) {
+                if (q < items) src = x + (t0 + tl) * K + (int64_t)gc * kGroup + sub * 8;
+            } else {
+                if (q < items) src = a_q + (t0 + tl) * K + (int64_t)gc * 16;
             }
+            v[u] = load_once16(src);
+        }
+    };
+    // QUANT: codes and scales of a batch (every lane quantises, zeros past
+    // the end, so the group max always runs on whole 16-lane groups)
+    uint2 codes[kBatch];
+    float scale[kBatch];
+    auto quant_batch = [&](int q0, const uint4 (&v)[kBatch]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (q0 + 4 * u >= items) break;   // no item of this wave left (wave-uniform)
+            float fv[8];
+            bf16x8_to_f32(v[u], fv);
+            scale[u] = quant_group16(fv, codes[u]);
         }
     };
     uint4 v[kBatch];
     load_batch(0, v);
 
-    auto loc = [&](int id) __attribute__((always_inline)) {
-        if (id < 0 || id >= Eg) return -1;
-        const int ex = map_lds ? s_map[id] : (emap ? emap[id] : id);
-        return (ex >= 0 && ex < El) ? ex : -1;
-    };
-    for (int j = threadIdx.x; j < kWaves * El; j += blockDim.x) wcnt[j / El][j % El] = 0;
-    if (self_count)
-        for (int ex = threadIdx.x; ex < El; ex += blockDim.x) {
-            s_cnt[ex] = 0;
-            s_base[ex] = 0;
+    // ---- LDS set-up from what was read
+    if constexpr (!GMAP) {
+        if (emap != nullptr) {
+#pragma unroll
+            for (int m = 0; m < kMapPerThread; ++m) {
+                const int j = threadIdx.x + m * kPermThreads;
+                if (j < Eg) s_map[j] = mv[m];
+            }
         }
-    __syncthreads();   // s_map, wcnt, s_cnt, s_base ready
-    if (self_count) {
-        // few pairs: every block counts them all (no histogram launches)
+        if (threadIdx.x == 0) s_map[kMapLds] = -1;
+    }
+    for (int j = threadIdx.x; j < kWaves * El; j += blockDim.x) wcnt[j / El][j % El] = 0;
+#pragma unroll
+    for (int j = 0; j < kExPerThread; ++j) {
+        const int ex = threadIdx.x * kExPerThread + j;
+        if (ex < El) {
+            s_cnt[ex] = SELF ? 0 : cb[0][SELF ? 0 : j];
+            s_base[ex] = SELF ? 0 : cb[1][SELF ? 0 : j];
+        }
+    }
+    s_tw[i] = own_w;
+    // local expert of a global id, -1 when out of range or not local; with
+    // the map in LDS the read is unconditional (out-of-range ids read the
+    // -1 past its end), so lookups do not wait on one another
+    const bool has_map = emap != nullptr;
+    auto loc = [&](int id) __attribute__((always_inline)) {
+        const bool in = (unsigned)id < (unsigned)Eg;
+        int ex;
+        if constexpr (GMAP) {
+            ex = in ? emap[id] : -1;
+        } else {
+            const int m = s_map[in && has_map ? id : kMapLds];
+            ex = has_map ? m : (in ? id : -1);
+        }
+        return (unsigned)ex < (unsigned)El ? ex : -1;
+    };
+    __syncthreads();   // s_map, wcnt, s_cnt, s_base, s_tw ready
+    if constexpr (SELF) {
+        // few pairs: every block counts them all
         const int64_t mine = (int64_t)blockIdx.x * tpb * topk;   // this block's first pair
+        int exu[kSelfLoads];   // every map lookup before the first add
+#pragma unroll
+        for (int u = 0; u < kSelfLoads; ++u) exu[u] = loc(sid[u]);
 #pragma unroll
         for (int u = 0; u < kSelfLoads; ++u) {
             const int64_t f2 = threadIdx.x + (int64_t)u * kPermThreads;
-            const int ex = loc(sid[u]);
-            if (ex >= 0) {
-                atomicAdd(&s_cnt[ex], 1);
-                if (f2 < mine) atomicAdd(&s_base[ex], 1);
+            if (exu[u] >= 0) {
+                atomicAdd(&s_cnt[exu[u]], 1);
+                if (f2 < mine) atomicAdd(&s_base[exu[u]], 1);
             }
         }
         __syncthreads();
-        if (blockIdx.x == 0 && blockIdx.y == 0)
-            for (int ex = threadIdx.x; ex < El; ex += blockDim.x) {
-                counts[ex] = s_cnt[ex];
-                if (counts_copy) counts_copy[ex] = s_cnt[ex];
-            }
     }
 
     // aligned segment offsets: exclusive scan of align * ceil(counts / align)
     // over the experts, four experts per thread
     {
-        int seg[4], tsum = 0;
+        int seg[kExPerThread], tsum = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int ex = threadIdx.x * 4 + j;
-            const int c = ex < El ? (self_count ? s_cnt[ex] : counts[ex]) : 0;
+        for (int j = 0; j < kExPerThread; ++j) {
+            const int ex = threadIdx.x * kExPerThread + j;
+            const int c = ex < El ? s_cnt[ex] : 0;
             seg[j] = ((c + align - 1) / align) * align;
             tsum += seg[j];
         }
@@ -409,32 +480,15 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
         int run = incl - tsum;
         for (int w = 0; w < wave; ++w) run += s_wsum[w];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int ex = threadIdx.x * 4 + j;
+        for (int j = 0; j < kExPerThread; ++j) {
+            const int ex = threadIdx.x * kExPerThread + j;
             if (ex < El) s_off[ex] = run;
             run += seg[j];
         }
         if (threadIdx.x == kPermThreads - 1) s_off[El] = run;
-        __syncthreads();
     }
-    {   // block (0, 0) publishes the offsets; all blocks share the padding
-        // marks (one wave per expert, its lanes on consecutive padding rows)
-        // and the rows past the last segment
-        const int nblocks = (int)(gridDim.x * gridDim.y);
-        const int bid = (int)(blockIdx.y * gridDim.x + blockIdx.x);
-        if (bid == 0)
-            for (int ex = threadIdx.x; ex <= El; ex += blockDim.x) offsets[ex] = s_off[ex];
-        for (int ex = bid * kWaves + wave; ex < El; ex += nblocks * kWaves) {
-            const int pad_lo = s_off[ex] + (self_count ? s_cnt[ex] : counts[ex]);
-            for (int r = pad_lo + lane; r < s_off[ex + 1]; r += kWave) row_src[r] = -1;
-        }
-        for (int64_t r = s_off[El] + (int64_t)bid * blockDim.x + threadIdx.x; r < cap_rows;
-             r += (int64_t)nblocks * blockDim.x)
-            row_src[r] = -1;
-    }
-
-    const int e = active ? loc(own_id) : -1;
     // lanes of this wave with the same expert (multisplit over the id bits)
+    const int e = active ? loc(own_id) : -1;
     uint64_t peers = ballot(e >= 0);
     for (int bit = 0; bit < nbits; ++bit) {
         const bool b = (e >> bit) & 1;
@@ -443,46 +497,65 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
     }
     const int rank_w = __popcll(peers & lanemask_lt());
     if (e >= 0 && rank_w == 0) wcnt[wave][e] = __popcll(peers);
-    __syncthreads();
+    __syncthreads();   // s_off, wcnt ready
     int row = -1;
     if (e >= 0) {
         int pre = 0;
         for (int w = 0; w < wave; ++w) pre += wcnt[w][e];
-        row = s_off[e] + (self_count ? s_base[e] : base[(int64_t)blockIdx.x * El + e]) + pre + rank_w;
+        row = s_off[e] + s_base[e] + pre + rank_w;
     }
-    if (active) {
-        rowmap[i] = row;
-        if (blockIdx.y == 0) {
+    if (active) rowmap[i] = row;
+    if constexpr (QUANT) quant_batch(0, v);   // its loads flew during the count, scan and rank
+    __syncthreads();   // rowmap ready
+
+    // ---- the stores
+    {   // block (0, 0) publishes the counts and offsets; all blocks share the
+        // padding marks (one wave per expert, its lanes on consecutive
+        // padding rows) and the rows past the last segment
+        const int nblocks = (int)(gridDim.x * gridDim.y);
+        const int bid = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+        if (bid == 0) {
+            for (int ex = threadIdx.x; ex <= El; ex += blockDim.x) offsets[ex] = s_off[ex];
+            if (SELF)
+                for (int ex = threadIdx.x; ex < El; ex += blockDim.x) {
+                    counts[ex] = s_cnt[ex];
+                    if (counts_copy) counts_copy[ex] = s_cnt[ex];
+                }
+        }
+        if (active && blockIdx.y == 0) {
             inv_perm[f] = row;
             if (row >= 0) row_src[row] = (int32_t)(t0 + i / topk);
         }
+        for (int ex = bid * kWaves + wave; ex < El; ex += nblocks * kWaves) {
+            const int pad_lo = s_off[ex] + s_cnt[ex];
+            for (int r = pad_lo + lane; r < s_off[ex + 1]; r += kWave) row_src[r] = -1;
+        }
+        for (int64_t r = s_off[El] + (int64_t)bid * blockDim.x + threadIdx.x; r < cap_rows;
+             r += (int64_t)nblocks * blockDim.x)
+            row_src[r] = -1;
     }
-    __syncthreads();
-
-    // ---- the row copies, batch 0 already loaded
+    // the row copies, batch 0 already loaded (and quantised)
     for (int q0 = 0; q0 < items; q0 += istep) {
-        if (q0 > 0) load_batch(q0, v);
+        if (q0 > 0) {
+            load_batch(q0, v);
+            if constexpr (QUANT) quant_batch(q0, v);
+        }
         if constexpr (QUANT) {
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
                 if (q0 + 4 * u >= items) break;   // no item of this wave left (wave-uniform)
                 int tl, g;
                 const int q = item(q0, u, tl, g);
-                // every lane quantises (zeros past the end), so the group
-                // max shuffle always runs on whole 16-lane groups
-                float fv[8];
-                bf16x8_to_f32(v[u], fv);
-                uint2 codes;
-                const float scale = quant_group16(fv, codes);
                 if (q < items) {
-                    const int64_t t = t0 + tl;
                     const int* rm = rowmap + tl * topk;
                     for (int k = 0; k < topk; ++k) {
                         const int r = rm[k];
                         if (r >= 0) {
-                            *reinterpret_cast<uint2*>(a_perm + (int64_t)r * K + (int64_t)g * kGroup + sub * 8) = codes;
+                            *reinterpret_cast<uint2*>(a_perm + (int64_t)r * K + (int64_t)g * kGroup + sub * 8) =
+                                codes[u];
                             if (sub == 0)
-                                a_perm_s[(int64_t)r * kg + g] = apply_on_input ? scale * topk_w[t * topk + k] : scale;
+                                a_perm_s[(int64_t)r * kg + g] =
+                                    apply_on_input ? scale[u] * s_tw[tl * topk + k] : scale[u];
                         }
                     }
                 }
@@ -511,7 +584,7 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
                 const float s = a_s[t * kg + g];
                 for (int k = 0; k < topk; ++k) {
                     const int r = rm[k];
-                    if (r >= 0) a_perm_s[(int64_t)r * kg + g] = apply_on_input ? s * topk_w[t * topk + k] : s;
+                    if (r >= 0) a_perm_s[(int64_t)r * kg + g] = apply_on_input ? s * s_tw[tl * topk + k] : s;
                 }
             }
         }
@@ -547,6 +620,12 @@ int bits_for(int El) {
     int b = 0;
     while ((1 << b) < El) ++b;
     return b;
+}
+
+template <bool QUANT>
+auto scatter_kernel(bool gmap, int self) {
+    if (gmap) return self ? k_permute_scatter<QUANT, true, true> : k_permute_scatter<QUANT, true, false>;
+    return self ? k_permute_scatter<QUANT, false, true> : k_permute_scatter<QUANT, false, false>;
 }
 
 }  // namespace
@@ -596,9 +675,10 @@ hipError_t launch_permute(const uint8_t* a_q, const float* a_s, const int32_t* i
         k_permute_hist<<<(unsigned)nblk, kPermThreads, 0, s>>>(ids, Mc, topk, tpb, emap, Eg, El, hist);
         k_permute_colscan<<<(unsigned)El, kScanThreads, 0, s>>>(hist, (int)nblk, El, counts, counts_copy);
     }
-    k_permute_scatter<false><<<scatter_grid(nblk, K), kPermThreads, 0, s>>>(
+    auto* kern = scatter_kernel<false>(emap != nullptr && Eg > kMapLds, self);
+    kern<<<scatter_grid(nblk, K), kPermThreads, 0, s>>>(
         a_q, a_s, nullptr, ids, topk_w, apply_on_input, Mc, K, topk, tpb, emap, Eg, El, bits_for(El), hist,
-        counts, counts_copy, self, align, cap_rows, offsets, a_perm, a_perm_s, inv_perm, row_src);
+        counts, counts_copy, align, cap_rows, offsets, a_perm, a_perm_s, inv_perm, row_src);
     return hipGetLastError();
 }
 
@@ -614,9 +694,10 @@ hipError_t launch_quant_permute(const uint16_t* x, const int32_t* ids, const flo
         k_permute_hist<<<(unsigned)nblk, kPermThreads, 0, s>>>(ids, Mc, topk, tpb, emap, Eg, El, hist);
         k_permute_colscan<<<(unsigned)El, kScanThreads, 0, s>>>(hist, (int)nblk, El, counts, counts_copy);
     }
-    k_permute_scatter<true><<<scatter_grid(nblk, K), kPermThreads, 0, s>>>(
+    auto* kern = scatter_kernel<true>(emap != nullptr && Eg > kMapLds, self);
+    kern<<<scatter_grid(nblk, K), kPermThreads, 0, s>>>(
         nullptr, nullptr, x, ids, topk_w, apply_on_input, Mc, K, topk, tpb, emap, Eg, El, bits_for(El), hist,
-        counts, counts_copy, self, align, cap_rows, offsets, a_perm, a_perm_s, inv_perm, row_src);
+        counts, counts_copy, align, cap_rows, offsets, a_perm, a_perm_s, inv_perm, row_src);
     return hipGetLastError();
 }
 

@@ -72,12 +72,36 @@ __device__ __forceinline__ uint32_t f32x4_to_e4m3_bounded(float a, float b, floa
     return r;
 }
 
+// Largest value among the 16 lanes of this lane's DPP row, returned to all
+// 16, for values that are never NaN (so the hardware maximum is the plain
+// larger value, as compare-select would give): lane pairs xor 1, xor 2
+// (quad permutes), then the two quads of each half and the two halves (the
+// half-row and row mirrors), one v_max_f32 with a DPP operand each.  The
+// s_nop before each step covers the wait a DPP read of a VGPR written by the
+// previous VALU instruction needs.
+__device__ __forceinline__ float row16_max_nonnan(float m) {
+    float r;
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_max_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf"
+        : "=&v"(r)
+        : "v"(m));
+    return r;
+}
+
 // One 1x128 quantisation group held by 16 consecutive lanes, 8 values each
 // (lane l owns group elements 8*(l mod 16) .. +7): amax over the group (the
 // largest non-NaN magnitude, by compare-select, so quiet and signalling NaNs
 // are both skipped), d = max(amax, 1e-10), scale = d / 448, inv = 448 / d,
-// codes = e4m3(x * inv).  Every lane of the wave must call it (the group max
-// is an xor-shuffle inside each 16-lane group); returns the scale.
+// codes = e4m3(x * inv).  All 16 lanes of a group must call it together
+// (the group max is a DPP maximum over the 16-lane row, no LDS involved);
+// returns the scale.
 __device__ __forceinline__ float quant_group16(const float (&x)[8], uint2& codes) {
     float amax = 0.0f;
 #pragma unroll
@@ -85,11 +109,7 @@ __device__ __forceinline__ float quant_group16(const float (&x)[8], uint2& codes
         const float a = __builtin_fabsf(x[i]);
         amax = a > amax ? a : amax;
     }
-#pragma unroll
-    for (int d = 8; d >= 1; d >>= 1) {
-        const float o = __shfl_xor(amax, d, kWave);
-        amax = o > amax ? o : amax;
-    }
+    amax = row16_max_nonnan(amax);   // the lane maxima are never NaN
     const float dd = __builtin_fmaxf(amax, 1e-10f);
     const float scale = dd / 448.0f;
     const float inv = 448.0f / dd;
@@ -149,29 +169,6 @@ __device__ __forceinline__ float exp_pinned(float x) {
     p = __builtin_fmaf(p, r, 1.0f);
     p = __builtin_fmaf(p, r, 1.0f);
     return __builtin_amdgcn_ldexpf(p, static_cast<int>(n));
-}
-
-// Largest value among the 16 lanes of this lane's DPP row, returned to all
-// 16, for values that are never NaN (so the hardware maximum is the plain
-// larger value, as compare-select would give): lane pairs xor 1, xor 2
-// (quad permutes), then the two quads of each half and the two halves (the
-// half-row and row mirrors), one v_max_f32 with a DPP operand each.  The
-// s_nop before each step covers the wait a DPP read of a VGPR written by the
-// previous VALU instruction needs.
-__device__ __forceinline__ float row16_max_nonnan(float m) {
-    float r;
-    asm volatile(
-        "s_nop 1\n\t"
-        "v_max_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-        "s_nop 1\n\t"
-        "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
-        "s_nop 1\n\t"
-        "v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
-        "s_nop 1\n\t"
-        "v_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf"
-        : "=&v"(r)
-        : "v"(m));
-    return r;
 }
 
 // SiLU as the SiLU-mul requant defines it: g / (1 + exp(-g)) with the
