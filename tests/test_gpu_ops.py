@@ -239,6 +239,8 @@ def _check_permute(g, r):
     (512, 256, 8, 64, 40, True, 32, 0, "random"),          # 16 pair blocks: counted in the scatter
     (513, 256, 8, 64, 40, True, 32, 1, "random"),          # 17: histogram and column scan
     (100, 256, 4, 5000, 64, True, 16, 0, "random"),        # expert map too large for LDS
+    (1100, 256, 4, 3000, 48, True, 32, 1, "random"),       # the same, 18 pair blocks: histogram path
+    (0, 256, 4, 32, 12, True, 16, 0, "random"),            # an empty chunk: counts and offsets only
 ])
 def test_permute_parity(M, K, T, Eg, El, mapped, align, on_input, routing):
     announce("permute", M, K, T, Eg, El, mapped, align, on_input, routing)
@@ -290,6 +292,9 @@ def _gpu_quant_permute(x, ids, w, on_input, emap, Eg, El, align):
     (130, 2048, 8, 128, 64, True, 128, 0, "uniform", True),  # 5 pair blocks x 16 K slices
     (512, 384, 8, 64, 40, True, 64, 1, "random", False),     # 16 pair blocks: counted in the scatter
     (513, 384, 8, 64, 40, True, 64, 0, "random", False),     # 17: histogram and column scan
+    (100, 256, 4, 5000, 64, True, 16, 1, "random", False),   # expert map too large for LDS
+    (1100, 384, 4, 3000, 48, True, 32, 0, "random", False),  # the same, 18 pair blocks: histogram path
+    (0, 256, 4, 32, 12, True, 16, 0, "random", False),       # an empty chunk: counts and offsets only
 ])
 def test_quant_permute_parity(M, K, T, Eg, El, mapped, align, on_input, routing, special):
     """The input quant fused into the permute: bit-exact with the oracle's
