@@ -567,13 +567,17 @@ def test_small_gemm_and_partials(El, hi, n_out, k_in, nsplit):
     assert np.all(p[:want, len(rows):] == -3.0), "a slab row past the valid rows was written"
 
 
-@pytest.mark.parametrize("El,hi,n,nsplit", [(64, 4, 768, 2), (16, 90, 256, 4), (8, 3, 128, 8), (30, 10, 384, 1)])
-def test_act_quant_and_unpermute_from_partials(El, hi, n, nsplit):
+@pytest.mark.parametrize("El,hi,n,nsplit,short", [(64, 4, 768, 2, False), (16, 90, 256, 4, False),
+                                                  (8, 3, 128, 8, False), (30, 10, 384, 1, False),
+                                                  (16, 90, 256, 4, True)])
+def test_act_quant_and_unpermute_from_partials(El, hi, n, nsplit, short):
     """The SiLU-mul requant and the unpermute that read the small GEMM's
     partial slabs give the bits of moe_act_quant / the unpermute run on the
     slabs' bf16 sum (formed on the host in slab order), on every valid row
-    and token, and leave rows that are not valid alone."""
-    announce("partials consumers", El, hi, n, nsplit)
+    and token, and leave rows that are not valid alone.  short: the requant
+    is given slabs of only half the valid rows (its grid is sized by them),
+    and the rows past them read as zero."""
+    announce("partials consumers", El, hi, n, nsplit, short)
     rng = np.random.default_rng(El + hi + n + nsplit)
     k_in = 1024
     # the gate/up GEMM: 2n outputs as partial slabs
@@ -584,10 +588,16 @@ def test_act_quant_and_unpermute_from_partials(El, hi, n, nsplit):
     info = filled((1,), torch.int32, -1)
     moe.moe_grouped_gemm_fp8_small(A, As, W, Ws, O, Cn, part=part, nsplit=nsplit, info=info)
     h = partial_rows(part, info, offs, cnt, cap)
+    part_q, h_q = part, h
+    if short:
+        pr = max(1, len(rows) // 2)
+        part_q = part[:, :pr].contiguous()
+        h_q = h.copy()
+        h_q[rows[pr:]] = 0
     q1, s1 = filled((cap, n), torch.uint8, 0xA5), filled((cap, n // 128), torch.float32, -7.0)
-    moe.moe_act_quant_partials(part, info, n, cap, O, Cn, q1, s1)
+    moe.moe_act_quant_partials(part_q, info, n, cap, O, Cn, q1, s1)
     q2, s2 = filled((cap, n), torch.uint8, 0), filled((cap, n // 128), torch.float32, 0.0)
-    moe.moe_act_quant(dev(h), n, moe.MOE_ACT_SILU_MUL, q2, s2, O, Cn, El)
+    moe.moe_act_quant(dev(h_q), n, moe.MOE_ACT_SILU_MUL, q2, s2, O, Cn, El)
     q1, s1, q2, s2 = host(q1), host(s1), host(q2), host(s2)
     np.testing.assert_array_equal(q1[rows], q2[rows])
     np.testing.assert_array_equal(s1[rows], s2[rows])

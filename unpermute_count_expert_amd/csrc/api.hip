@@ -582,8 +582,10 @@ int moe_act_quant_partials(const float* part, const int32_t* info, int64_t part_
     REQUIRE_PTR(q_s);
     int st = check_device(nullptr);
     if (st) return st;
+    // the grid is sized for the slabs' rows (the kernel's blocks take more
+    // groups each when there are more valid rows than that)
     HIP_OK(moe::launch_act_quant_part(part, info, part_rows, nsplit, rows, n, expert_offsets, counts, El, q, q_s,
-                                      rows, static_cast<hipStream_t>(stream)));
+                                      part_rows < rows ? part_rows : rows, static_cast<hipStream_t>(stream)));
     return MOE_OK;
 }
 
