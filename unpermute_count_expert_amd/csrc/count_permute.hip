@@ -317,6 +317,23 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
     __shared__ int s_map[GMAP ? 1 : kMapLds + 1];   // expert_map, when there is one; [kMapLds] = -1
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
+    // every argument and grid size in SGPRs here, all loaded together: the
+    // compiler would otherwise load each just before its first use, and at a
+    // kernel's start each such load waits for a scalar-cache miss
+    const unsigned grid_x = gridDim.x, grid_y = gridDim.y;
+    asm volatile("" ::"s"(a_q), "s"(a_s), "s"(x), "s"(ids), "s"(topk_w), "s"(apply_on_input), "s"(Mc), "s"(K),
+                 "s"(topk), "s"(tpb), "s"(emap), "s"(Eg), "s"(El), "s"(nbits), "s"(base));
+    asm volatile("" ::"s"(counts), "s"(counts_copy), "s"(align), "s"(cap_rows), "s"(offsets), "s"(a_perm),
+                 "s"(a_perm_s), "s"(inv_perm), "s"(row_src), "s"(grid_x), "s"(grid_y));
+    // the fill constants at a per-lane offset the compiler cannot see is
+    // zero: read with vector loads, which it counts with the others, rather
+    // than as scalar loads of a uniform address
+    int vzero = 0;
+    asm volatile("" : "+v"(vzero));
+    const int32_t* f_neg1 = g_fill_neg1 + vzero;
+    const int32_t* f_zero = g_fill_zero + vzero;
+    const float* f_one = g_fill_one + vzero;
+    const void* f_zero16 = g_fill_zero16 + vzero;
 
     // ---- every global read, issued before the first wait and none of them
     // conditional (an item past the end reads one of the fill constants
@@ -329,8 +346,8 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
     const int i = threadIdx.x;
     const bool active = i < npairs;
     const int64_t f = t0 * topk + i;
-    const int own_id = *(active ? ids + f : g_fill_neg1);
-    const float own_w = *(active && apply_on_input ? topk_w + f : g_fill_one);
+    const int own_id = *(active ? ids + f : f_neg1);
+    const float own_w = *(active && apply_on_input ? topk_w + f : f_one);
     const int64_t np = Mc * topk;
     int sid[SELF ? kSelfLoads : 1];
     int cb[2][SELF ? 1 : kExPerThread];   // not SELF: counts and this block's row bases
@@ -338,14 +355,14 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
 #pragma unroll
         for (int u = 0; u < kSelfLoads; ++u) {
             const int64_t f2 = threadIdx.x + (int64_t)u * kPermThreads;
-            sid[u] = *(f2 < np ? ids + f2 : g_fill_neg1);
+            sid[u] = *(f2 < np ? ids + f2 : f_neg1);
         }
     } else {
 #pragma unroll
         for (int j = 0; j < kExPerThread; ++j) {
             const int ex = threadIdx.x * kExPerThread + j;
-            cb[0][j] = *(ex < El ? counts + ex : g_fill_zero);
-            cb[1][j] = *(ex < El ? base + (int64_t)blockIdx.x * El + ex : g_fill_zero);
+            cb[0][j] = *(ex < El ? counts + ex : f_zero);
+            cb[1][j] = *(ex < El ? base + (int64_t)blockIdx.x * El + ex : f_zero);
         }
     }
     int mv[kMapPerThread];
@@ -353,12 +370,12 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
 #pragma unroll
         for (int m = 0; m < kMapPerThread; ++m) {
             const int j = threadIdx.x + m * kPermThreads;
-            mv[m] = *(emap != nullptr && j < Eg ? emap + j : g_fill_neg1);
+            mv[m] = *(emap != nullptr && j < Eg ? emap + j : f_neg1);
         }
     }
     // this block's slice of the K groups: [g_lo, g_lo + ng)
     const int kg = K / kGroup;
-    const int gps = (kg + (int)gridDim.y - 1) / (int)gridDim.y;
+    const int gps = (kg + (int)grid_y - 1) / (int)grid_y;
     const int g_lo = min(kg, (int)blockIdx.y * gps);
     const int ng = min(kg, g_lo + gps) - g_lo;
     const int my_tokens = ntok > wave ? (ntok - wave + kWaves - 1) / kWaves : 0;
@@ -384,7 +401,7 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
         for (int u = 0; u < kBatch; ++u) {
             int tl, gc;
             const int q = item(q0, u, tl, gc);
-            const void* src = g_fill_zero16;
+            const void* src = f_zero16;
             if constexpr (QUANT) {
                 if (q < items) src = x + (t0 + tl) * K + (int64_t)gc * kGroup + sub * 8;
             } else {
@@ -420,7 +437,7 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
         }
         if (threadIdx.x == 0) s_map[kMapLds] = -1;
     }
-    for (int j = threadIdx.x; j < kWaves * El; j += blockDim.x) wcnt[j / El][j % El] = 0;
+    for (int j = threadIdx.x; j < kWaves * El; j += kPermThreads) wcnt[j / El][j % El] = 0;
 #pragma unroll
     for (int j = 0; j < kExPerThread; ++j) {
         const int ex = threadIdx.x * kExPerThread + j;
@@ -512,12 +529,12 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
     {   // block (0, 0) publishes the counts and offsets; all blocks share the
         // padding marks (one wave per expert, its lanes on consecutive
         // padding rows) and the rows past the last segment
-        const int nblocks = (int)(gridDim.x * gridDim.y);
-        const int bid = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+        const int nblocks = (int)(grid_x * grid_y);
+        const int bid = (int)(blockIdx.y * grid_x + blockIdx.x);
         if (bid == 0) {
-            for (int ex = threadIdx.x; ex <= El; ex += blockDim.x) offsets[ex] = s_off[ex];
+            for (int ex = threadIdx.x; ex <= El; ex += kPermThreads) offsets[ex] = s_off[ex];
             if (SELF)
-                for (int ex = threadIdx.x; ex < El; ex += blockDim.x) {
+                for (int ex = threadIdx.x; ex < El; ex += kPermThreads) {
                     counts[ex] = s_cnt[ex];
                     if (counts_copy) counts_copy[ex] = s_cnt[ex];
                 }
@@ -530,8 +547,8 @@ __global__ __launch_bounds__(kPermThreads) void k_permute_scatter(
             const int pad_lo = s_off[ex] + s_cnt[ex];
             for (int r = pad_lo + lane; r < s_off[ex + 1]; r += kWave) row_src[r] = -1;
         }
-        for (int64_t r = s_off[El] + (int64_t)bid * blockDim.x + threadIdx.x; r < cap_rows;
-             r += (int64_t)nblocks * blockDim.x)
+        for (int64_t r = s_off[El] + (int64_t)bid * kPermThreads + threadIdx.x; r < cap_rows;
+             r += (int64_t)nblocks * kPermThreads)
             row_src[r] = -1;
     }
     // the row copies, batch 0 already loaded (and quantised)
