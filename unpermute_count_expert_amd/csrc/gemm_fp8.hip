@@ -81,15 +81,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ int wave_incl_scan(int v) {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        int u = __shfl_up(v, d, kWave);
-        if (lane >= d) v += u;
-    }
-    return v;
-}
+__device__ __forceinline__ int wave_incl_scan(int v) { return wave_inclusive_scan(v); }
 
 // position (0..7) of 16-byte chunk c in LDS tile row r, and its inverse
 __device__ __forceinline__ int swz_pos(int c, int r) { return c ^ (r & 7) ^ ((r >> 3) & 1); }

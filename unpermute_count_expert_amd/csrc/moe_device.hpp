@@ -222,6 +222,21 @@ __device__ __forceinline__ T wave_inclusive_scan(T v) {
     return v;
 }
 
+// The same for 32-bit values, without LDS: a Hillis-Steele scan inside each
+// 16-lane DPP row (row shifts by 1, 2, 4 and 8; a lane whose source falls
+// outside its row adds 0), then every row adds the totals of the rows before
+// it (lane 15's value broadcast into rows 1 and 3, then lane 31's into rows 2
+// and 3).  Every lane of the wave must call it.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31
+    return v;
+}
+
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
