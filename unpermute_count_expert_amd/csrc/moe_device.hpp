@@ -237,6 +237,26 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
     return v;
 }
 
+// And for 64-bit values: each step moves both 32-bit halves with the same DPP
+// pattern and adds them as one 64-bit value.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int64_t dpp_add64(int64_t v) {
+    const uint64_t u = (uint64_t)v;
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)u, CTRL, ROW_MASK, 0xf, false);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(u >> 32), CTRL, ROW_MASK, 0xf, false);
+    return (int64_t)(u + (((uint64_t)hi << 32) | lo));
+}
+
+__device__ __forceinline__ int64_t wave_inclusive_scan(int64_t v) {
+    v = dpp_add64<0x111, 0xf>(v);   // row_shr:1
+    v = dpp_add64<0x112, 0xf>(v);   // row_shr:2
+    v = dpp_add64<0x114, 0xf>(v);   // row_shr:4
+    v = dpp_add64<0x118, 0xf>(v);   // row_shr:8
+    v = dpp_add64<0x142, 0xa>(v);   // row_bcast:15
+    v = dpp_add64<0x143, 0xc>(v);   // row_bcast:31
+    return v;
+}
+
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
