@@ -241,6 +241,8 @@ def _check_permute(g, r):
     (100, 256, 4, 5000, 64, True, 16, 0, "random"),        # expert map too large for LDS
     (1100, 256, 4, 3000, 48, True, 32, 1, "random"),       # the same, 18 pair blocks: histogram path
     (0, 256, 4, 32, 12, True, 16, 0, "random"),            # an empty chunk: counts and offsets only
+    (300, 256, 8, 1024, 1024, False, 16, 1, "random"),     # 1024 experts, counted in the scatter
+    (2000, 256, 8, 1024, 1024, False, 16, 0, "random"),    # 1024 experts, histogram path
 ])
 def test_permute_parity(M, K, T, Eg, El, mapped, align, on_input, routing):
     announce("permute", M, K, T, Eg, El, mapped, align, on_input, routing)
@@ -295,6 +297,7 @@ def _gpu_quant_permute(x, ids, w, on_input, emap, Eg, El, align):
     (100, 256, 4, 5000, 64, True, 16, 1, "random", False),   # expert map too large for LDS
     (1100, 384, 4, 3000, 48, True, 32, 0, "random", False),  # the same, 18 pair blocks: histogram path
     (0, 256, 4, 32, 12, True, 16, 0, "random", False),       # an empty chunk: counts and offsets only
+    (400, 256, 8, 1024, 1000, True, 16, 0, "random", False),  # 1000 local experts, counted in the scatter
 ])
 def test_quant_permute_parity(M, K, T, Eg, El, mapped, align, on_input, routing, special):
     """The input quant fused into the permute: bit-exact with the oracle's
@@ -470,6 +473,7 @@ def test_gemm_random_parity(El, n_out, k_in, counts, align, tile):
     (48, 700, 2048, 512, 256, "codes"),    # ~620 256-row tiles (2 LDS stages)
     (64, 300, 2048, 512, 128, "layer"),
     (48, 700, 2048, 512, 256, "layer"),
+    (1024, 20, 256, 256, 128, "codes"),     # 1024 experts: the prologue's scans at full width
 ])
 def test_gemm_full_grid_every_row(El, hi, n_out, k_in, tile, data):
     """Several times more tiles than the persistent grid has blocks, over
@@ -531,6 +535,7 @@ def _num_cus():
     (8, 3, 256, 2048, 1),       # one slab: whole-K sums
     (40, 20, 768, 768, 3),      # down-projection K (6 groups) cut in three
     (300, 30, 2048, 512, 2),    # tiles enough for four rounds: K kept whole
+    (1024, 2, 256, 256, 2),     # 1024 experts: the prologue's scans at full width
 ])
 def test_small_gemm_and_partials(El, hi, n_out, k_in, nsplit):
     """moe_grouped_gemm_fp8_small on layer-like data: without part, the bits
